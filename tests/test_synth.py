@@ -1,0 +1,55 @@
+"""The seeded input generator: reproducible, per-head streams, distributions as stated."""
+import numpy as np
+
+from video_diffusion_transformers_amd import synth
+
+
+def test_named_config_shapes():
+    c = synth.CONFIGS
+    assert (c["tiny"].N, c["tiny"].D, c["tiny"].split) == (32, 64, (24, 20, 20))
+    assert c["small"].N == 1024 and c["480p"].N == 32760 and c["720p"].N == 75600
+    assert c["mixed"].steps == 4 and c["mixed"].N == 75600
+    for cfg in c.values():
+        assert sum(cfg.split) == cfg.D and all(d % 2 == 0 for d in cfg.split)
+
+
+def test_reproducible_and_per_head_independent():
+    cfg = synth.CONFIGS["small"]
+    a = synth.head_qkv(cfg, 0, 0, 3)
+    b = synth.head_qkv(cfg, 0, 0, 3)
+    c = synth.head_qkv(cfg, 0, 0, 4)
+    d = synth.head_qkv(cfg, 1, 0, 3)
+    for x, y in zip(a, b):
+        assert x.dtype == np.float16 and x.shape == (1024, 128) and np.array_equal(x, y)
+    assert not np.array_equal(a[0], c[0]) and not np.array_equal(a[0], d[0])
+
+
+def test_video_outliers_sit_in_the_temporal_partition():
+    cfg = synth.CONFIGS["small"]
+    q, k, v = synth.head_qkv(cfg, 0, 0, 0)
+    for x in (q, k):
+        rms = np.sqrt(np.mean(x.astype(np.float64) ** 2, axis=0))
+        top4 = np.argsort(rms)[-4:]
+        assert np.all(top4 < cfg.split[0])
+    row_rms = np.sqrt(np.mean(v.astype(np.float64) ** 2, axis=1))
+    n_out = max(1, round(0.002 * cfg.N))
+    assert np.sum(row_rms > 6) == n_out
+
+
+def test_tiny_outliers_two_per_partition():
+    cfg = synth.CONFIGS["tiny"]
+    q, _, _ = synth.head_qkv(cfg, 0, 0, 0)
+    rms = np.sqrt(np.mean(q.astype(np.float64) ** 2, axis=0))
+    heavy = np.nonzero(rms > 8)[0]
+    offs = synth.partition_offsets(cfg.split)
+    counts = [np.sum((heavy >= o) & (heavy < o + w)) for o, w in zip(offs, cfg.split)]
+    assert counts == [2, 2, 2]
+
+
+def test_masks_and_rows():
+    assert list(synth.fallback_mask(synth.CONFIGS["tiny"])) == [0, 1]
+    m = synth.fallback_mask(synth.CONFIGS["mixed"])
+    assert m.sum() == 10 and m.size == 40
+    r = synth.sampled_rows(synth.CONFIGS["720p"], 5)
+    assert r.size == 256 and np.all(np.diff(r) > 0) and r.max() < 75600
+    assert np.array_equal(synth.sampled_rows(synth.CONFIGS["small"], 0), np.arange(1024))
