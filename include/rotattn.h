@@ -1,0 +1,232 @@
+/*
+ * rotattn.h -- C ABI of librotattn.so: RotateAttention's mixed-precision INT4
+ * FlashAttention forward for DiT video models with 3D RoPE, on AMD MI355X
+ * (gfx950).
+ *
+ * Source: "RotateAttention: RoPE-Aware Rotation and Range Rectification for
+ * INT4 Quantized Attention in Video Generation", Abstract.  The abstract
+ * states the problem as attention inside DiT video generators that use 3D
+ * RoPE, computed by a quantized FlashAttention whose Q and K are rotated by
+ * RoPE-aware orthogonal matrices, whose probabilities P = exp(S - max S) are
+ * quantized to the full unsigned INT4 range with a fixed scale and zero point,
+ * and with a selective FP16 fallback for accuracy-sensitive heads.  The entry
+ * points below are the steps of that forward pass:
+ *
+ *   rotattn_prepare_qkv  3D RoPE + partition-wise rotation + per-block INT4
+ *                        quantize and pack (RoPE'd fp16 Q/K for fallback heads)
+ *   rotattn_int4_fwd     integer QK^T, online softmax, u4 P, integer P.V
+ *   rotattn_fp16_fwd     FP16 FlashAttention for the fallback heads
+ *   rotattn_mixed_fwd    all of the above on one stream, routed by a head mask
+ *
+ * Conventions (every entry point):
+ *  - Tensors are device pointers owned by the caller.  The library never
+ *    allocates device memory, never synchronizes, and enqueues work only on
+ *    the stream it is given.  fp16 tensors are IEEE binary16 bit patterns
+ *    (uint16_t).  Device pointers must be 16-byte aligned.
+ *  - Shapes: Q, K, V, O are [B][H][N][D] contiguous.  Token n sits at
+ *    t = n / (Hg*Wg), h = (n / Wg) % Hg, w = n % Wg of the latent grid
+ *    (T, Hg, Wg) = (grid_t, grid_h, grid_w), so N = T*Hg*Wg.  The head
+ *    dimension D is split into RoPE partitions [d_t | d_h | d_w] in that
+ *    order; inside a partition channels (2j, 2j+1) form one rotary pair.
+ *  - Supported: D in {64, 128}, (d_t, d_h, d_w) = (24, 20, 20) for D = 64 and
+ *    (44, 42, 42) for D = 128, B*H <= ROTATTN_MAX_HEADS.
+ *  - Host-side arrays (masks) are read during the call and not kept.
+ *  - Return value: ROTATTN_OK (0) or a negative rotattn_status.  Argument
+ *    errors are reported before anything is enqueued; a launch error maps to
+ *    ROTATTN_E_HIP.  Nothing throws across the ABI and there is no mutable
+ *    global state, so calls are re-entrant.
+ *  - Non-finite inputs are undefined behaviour (not checked).
+ */
+#ifndef ROTATTN_H
+#define ROTATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ROTATTN_BLOCK 128        /* quantization block == key tile, in tokens */
+#define ROTATTN_MAX_HEADS 4096   /* B*H limit (head masks travel as kernel arguments) */
+#define ROTATTN_P_LEVELS 15      /* u4 P: scale 1/15, zero point 0 */
+
+typedef enum rotattn_status {
+  ROTATTN_OK = 0,
+  ROTATTN_E_NULL = -1,          /* a required pointer is NULL */
+  ROTATTN_E_SHAPE = -2,         /* inconsistent shape (N != T*Hg*Wg, d_t+d_h+d_w != D, odd d_a, <= 0) */
+  ROTATTN_E_UNSUPPORTED = -3,   /* D or RoPE split outside the supported set, too many heads */
+  ROTATTN_E_WORKSPACE = -4,     /* workspace smaller than rotattn_workspace_bytes() */
+  ROTATTN_E_ALIGN = -5,         /* a device pointer is not 16-byte aligned */
+  ROTATTN_E_HIP = -6,           /* a HIP launch or runtime call failed */
+  ROTATTN_E_ARG = -7            /* another argument is out of range (debug q-block, sweep range) */
+} rotattn_status;
+
+/* Problem shape. */
+typedef struct rotattn_shape {
+  int32_t B, H, N, D;
+  int32_t grid_t, grid_h, grid_w;
+  int32_t d_t, d_h, d_w;
+} rotattn_shape;
+
+/*
+ * RoPE tables and rotation matrices (device, fp32, caller-owned).
+ * cos_a/sin_a: [extent_a][d_a/2] with entry [p][j] = cos/sin(p * theta_{a,j}),
+ * theta_{a,j} = base^(-2j/d_a); rotattn_rope_tables_host() fills them.
+ * rot_a: [d_a][d_a] row-major orthogonal matrix, row = output channel; the
+ * same matrices apply to Q and K of every head (RoPE-aware rotation inside
+ * each RoPE partition, applied after RoPE).
+ */
+typedef struct rotattn_rope_rot {
+  const float *cos_t, *sin_t, *cos_h, *sin_h, *cos_w, *sin_w;
+  const float *rot_t, *rot_h, *rot_w;
+} rotattn_rope_rot;
+
+/*
+ * Output of rotattn_prepare_qkv (device, caller-allocated; carve it from one
+ * buffer with rotattn_prepared_carve).  NB = ceil(N/128), N_pad = 128*NB.
+ *  q4, k4: [B*H][N_pad][D/2] bytes: INT4 codes in [-7, 7], two's complement
+ *          nibbles.  Each group of 8 consecutive channels 8g..8g+7 occupies 4
+ *          bytes; byte i holds channel 8g+i in its low nibble and 8g+4+i in
+ *          its high nibble.  Rows N..N_pad-1 are zero.
+ *  v4:     [B*H][NB][D][64] bytes: V codes per 128-token block, transposed
+ *          (channel-major): row d holds the 128 keys of the block packed the
+ *          same way along keys (byte i of group g = keys 8g+i, 8g+4+i).
+ *  q_scale_l2, k_scale, v_scale: [B*H][NB] fp32 block scales (amax/7).
+ *          q_scale_l2 = fl(q_scale * kappa), kappa = fl32(log2(e)/sqrt(D)), so
+ *          that 2^(I * q_scale_l2 * k_scale) = exp(QK^T / sqrt(D)).
+ *  q_rope, k_rope: [B*H][N][D] fp16 RoPE'd (not rotated, not quantized) Q/K,
+ *          written for fallback heads only; may be NULL when no head falls
+ *          back.
+ *  rot64:  library scratch, 3*64*64 doubles (the rotation in fp64).
+ */
+typedef struct rotattn_prepared {
+  uint8_t *q4, *k4, *v4;
+  float *q_scale_l2, *k_scale, *v_scale;
+  uint16_t *q_rope, *k_rope;
+  double *rot64;
+} rotattn_prepared;
+
+/*
+ * Integer dumps of one (b, h, q_block) for parity checks (device,
+ * caller-allocated); pass NULL in production.  Rows are the 128 queries of
+ * the block (rows past N are written but meaningless).
+ *  s_int:  [128][N_pad] int32 I = q-codes . k-codes (exact)
+ *  p_code: [128][N_pad] uint8 P codes in [0, 15] (0 for keys >= N)
+ *  pv_int: [NB][128][D] int32 per-key-tile sum_j code_ij * v-code_jd (exact)
+ *  m_final, l_final: [128] fp32 final running max (log2 units) and normalizer
+ */
+typedef struct rotattn_debug {
+  int32_t b, h, q_block;
+  int32_t *s_int;
+  uint8_t *p_code;
+  int32_t *pv_int;
+  float *m_final, *l_final;
+} rotattn_debug;
+
+/* Host-only shape check; needs no GPU.  Returns a rotattn_status. */
+int rotattn_validate(const rotattn_shape* s);
+
+/* Human-readable name of a status code (static string). */
+const char* rotattn_strerror(int status);
+
+/*
+ * Host: fill RoPE tables (host arrays of the sizes in rotattn_rope_rot) with
+ * the exact cos/sin of p * base^(-2j/d_a), rounded once to fp32 (computed in
+ * long double).
+ */
+int rotattn_rope_tables_host(const rotattn_shape* s, double base,
+                             float* cos_t, float* sin_t, float* cos_h,
+                             float* sin_h, float* cos_w, float* sin_w);
+
+/*
+ * Host: the 15 P-code thresholds tau_k (smallest fp32 with 15*2^tau_k >=
+ * k - 1/2), so code(x) = #{k : x >= tau_k} = rne(15 * 2^x) for x <= 0.
+ */
+int rotattn_pcode_thresholds_host(float tau[15]);
+
+/* Host: kappa = fl32(log2(e)/sqrt(D)). */
+float rotattn_kappa_host(int32_t D);
+
+/* Bytes for a rotattn_prepared (with_rope != 0 adds the fp16 Q'/K' arrays). */
+size_t rotattn_prepared_bytes(const rotattn_shape* s, int with_rope);
+
+/* Lay a rotattn_prepared out in [base, base+bytes) (256-byte aligned parts). */
+int rotattn_prepared_carve(const rotattn_shape* s, void* base, size_t bytes,
+                           int with_rope, rotattn_prepared* out);
+
+/*
+ * Prologue.  For every head with fallback_mask_host[b*H+h] == 0 (or all heads
+ * when the mask is NULL): 3D RoPE on Q and K in fp32, the partition-wise
+ * rotation (fp64 accumulation, one rounding to fp32), per-block symmetric
+ * INT4 quantization of Q, K, V and packing into `out`.  For a fallback head:
+ * RoPE'd fp16 Q'/K' into out->q_rope / out->k_rope only.
+ */
+int rotattn_prepare_qkv(const rotattn_shape* s, const uint16_t* q,
+                        const uint16_t* k, const uint16_t* v,
+                        const rotattn_rope_rot* rr,
+                        const uint8_t* fallback_mask_host,
+                        const rotattn_prepared* out, hipStream_t stream);
+
+/*
+ * INT4 attention over the heads with fallback_mask_host[...] == 0 (all heads
+ * when NULL): I = q4.k4^T on i8 MFMA, one-pass online softmax over 128-key
+ * tiles in the log2 domain, P codes rne(15*2^(s-m)) against the running max,
+ * PV = codes.v4 on i8 MFMA, O = acc / l written as fp16 into o [B][H][N][D].
+ * dbg != NULL additionally runs one instrumented work-group for (dbg->b,
+ * dbg->h, dbg->q_block) that fills the integer dumps.
+ */
+int rotattn_int4_fwd(const rotattn_shape* s, const rotattn_prepared* p,
+                     const uint8_t* fallback_mask_host, uint16_t* o,
+                     const rotattn_debug* dbg, hipStream_t stream);
+
+/*
+ * FP16 FlashAttention: O = softmax(Q'K'^T / sqrt(D)) V on fp16 MFMA with fp32
+ * softmax and accumulation, for the heads with head_select_host[...] != 0
+ * (all heads when NULL).  q_rope, k_rope, v, o: [B][H][N][D] fp16.
+ */
+int rotattn_fp16_fwd(const rotattn_shape* s, const uint16_t* q_rope,
+                     const uint16_t* k_rope, const uint16_t* v,
+                     const uint8_t* head_select_host, uint16_t* o,
+                     hipStream_t stream);
+
+/* Workspace bytes for rotattn_mixed_fwd (a rotattn_prepared with fp16 Q'/K'). */
+size_t rotattn_workspace_bytes(const rotattn_shape* s);
+
+/*
+ * Whole forward: prepare, INT4 attention for mask == 0 heads, FP16
+ * attention for mask != 0 heads, all on `stream`, writing every head of o.
+ */
+int rotattn_mixed_fwd(const rotattn_shape* s, const uint16_t* q,
+                      const uint16_t* k, const uint16_t* v,
+                      const rotattn_rope_rot* rr,
+                      const uint8_t* fallback_mask_host, void* workspace,
+                      size_t workspace_bytes, uint16_t* o, hipStream_t stream);
+
+/*
+ * Self-test of the P-code device function (the exact code the attention
+ * kernel uses).  Evaluates code(x) for x = -magnitude over the magnitude bit
+ * patterns [mag_lo, mag_lo + count) with c = 1, m = 0, and records every
+ * position where the code changes: transitions[3*i] = magnitude bits,
+ * [3*i+1] = code before, [3*i+2] = code after, for i < max_transitions.
+ * *n_transitions (device) receives the total count (zero it first).
+ */
+int rotattn_pcode_sweep(uint32_t mag_lo, uint32_t count, uint32_t* transitions,
+                        uint32_t max_transitions, uint32_t* n_transitions,
+                        hipStream_t stream);
+
+/*
+ * Self-test: P codes of raw integer scores through the attention kernel's
+ * code path.  I: [n] int32 exact QK^T values, c: fl(q_scale_l2*k_scale),
+ * m: running max (log2 units, >= fl(I*c) for every element).  codes: [n]
+ * uint8.  n must be a multiple of 4096.
+ */
+int rotattn_pcode_eval(const int32_t* I, uint32_t n, float c, float m,
+                       uint8_t* codes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ROTATTN_H */

@@ -1,0 +1,456 @@
+// K2: RotateAttention's INT4 FlashAttention forward on gfx950.
+//
+// RotateAttention page ("RotateAttention: RoPE-Aware Rotation and Range
+// Rectification for INT4 Quantized Attention in Video Generation", Abstract):
+// quantized FlashAttention over INT4 Q/K/V, where P = exp(S - max S) is
+// non-negative and is quantized to the full unsigned 4-bit range with a fixed
+// scale (1/15) and zero point (0) -- "range-optimized P quantization".
+//
+// What one work-group computes (4 waves x 32 queries = one 128-query block of
+// one head; the block shares one Q scale):
+//   for each 128-key tile t (ascending):
+//     S^T  = K_t Q^T on v_mfma_i32_32x32x32_i8: operands are INT4 codes held
+//            as 16*code in int8 lanes, so the int32 result is 256*I exactly
+//     m'   = max(m, fl(max_j I * c_t)),  c_t = fl(q_scale_l2 * k_scale_t)
+//     code = rne(15 * 2^(fl(fl(I*c_t) - m')))            (u4, exact, see below)
+//     l    = 2^(m-m') l + sum_j 15 * 2^(...)             (fp32, unquantized)
+//     O^T  = 2^(m-m') O^T + (v_scale_t/16) * (V_t^T P^T) (v_mfma_i32_32x32x32_i8)
+//   O = O / l  -> fp16.
+// Computing S^T (keys as MFMA rows) leaves every lane holding one query's
+// scores in exactly the operand layout the P.V MFMA needs for P^T, so the
+// requantized codes never leave registers; the running max, sum and O rows of
+// a query live in the same lane pair (lane, lane^32).
+//
+// P codes, exactly.  The fast path computes y = v_exp_f32(fma(256I, c_t/256,
+// log2(15) - m')) ~ 15*2^x and rounds it with v_cvt_pk_u8_f32 (round to
+// nearest even, checked on the device).  |y - 15*2^x| is bounded by the
+// rounding of the fused argument (at most ~ulp(|m'| + 8) + 2^-21 in x) and the
+// exp error (< 1 ulp); whenever some y of a 32-key subtile lies within delta
+// of a half-integer, that register is recomputed exactly as
+// #{k : fl(fl(I*c_t) - m') >= tau_k}.  The self-test entry points run this same
+// function over every float32 score and over random integer scores.
+#include <math.h>
+
+#include "rotattn_internal.h"
+
+namespace rotattn {
+
+constexpr int kThreads = 256;
+constexpr int kVStride = 144;   // V^T tile row: 128 keys + 16 bytes of padding
+
+struct CodeCtx {
+  float cq;      // c_t / 256 (scores arrive as 256*I)
+  float m15n;    // fl(log2(15)) - m'
+  float ct;      // c_t
+  float mnew;    // m'
+  float delta;   // half-width of the band around each half-integer that takes the exact path
+};
+
+__device__ __forceinline__ float ulp_pos(float v) {   // ulp of a positive normal float
+  return __uint_as_float(__float_as_uint(v) & 0x7F800000u) * 0x1p-23f;
+}
+
+__device__ __forceinline__ CodeCtx make_ctx(float ct, float mnew, float log2_15) {
+  CodeCtx c;
+  c.ct = ct;
+  c.mnew = mnew;
+  c.cq = ct * 0x1p-8f;
+  c.m15n = log2_15 - mnew;
+  // error of the fused argument against x + log2(15) for scores that can
+  // round to a code in 1..15 (|x| < 8), in log2 units:
+  const float e = 0x1p-21f + ulp_pos(fabsf(mnew) + 8.0f);
+  // 15.5 * ln 2 < 10.75; v_exp_f32 error < 1 ulp; 12x and +4e-6 are margin.
+  c.delta = 12.0f * e + 4e-6f;
+  // c_t so small that c_t/256 is subnormal: never trust the fast path.
+  if (ct != 0.0f && ct < 0x1p-100f) c.delta = 1.0f;
+  return c;
+}
+
+__device__ __forceinline__ uint32_t wave_any(bool p) { return __ballot(p) != 0; }
+
+// Exact P code of one score (float f = 256*I exactly).
+__device__ __forceinline__ int exact_code(float f, const CodeCtx& cx, const float* tau) {
+  const float I = f * 0x1p-8f;     // exact
+  const float s = I * cx.ct;       // fl(I * c_t)
+  const float x = s - cx.mnew;     // fl(s - m')
+  int code = 0;
+#pragma unroll
+  for (int k = 0; k < 15; ++k) code += (x >= tau[k]) ? 1 : 0;
+  return code;
+}
+
+// 16 scores of one lane (one 32-key subtile) -> 16 u4 codes packed in byte
+// lanes (byte r = code of score r), and their unquantized 15*2^x added to lsum.
+template <bool TAIL>
+__device__ __forceinline__ v4i pcode16(const float (&f)[16], const CodeCtx& cx, const float* tau,
+                                       float& lsum, uint32_t valid) {
+  float y[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float t = fmaf(f[r], cx.cq, cx.m15n);
+    if (TAIL) t = ((valid >> r) & 1u) ? t : -INFINITY;
+    y[r] = __builtin_amdgcn_exp2f(t);
+    lsum += y[r];
+  }
+  float g = 1.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) g = fminf(g, fabsf(__builtin_amdgcn_fractf(y[r]) - 0.5f));
+  uint32_t pk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t v = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * i], 0, 0u);
+    v = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * i + 1], 1, v);
+    v = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * i + 2], 2, v);
+    pk[i] = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * i + 3], 3, v);
+  }
+  if (wave_any(g < cx.delta)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bool near = fabsf(__builtin_amdgcn_fractf(y[r]) - 0.5f) < cx.delta;
+      if (wave_any(near)) {
+        int code = exact_code(f[r], cx, tau);
+        if (TAIL && !((valid >> r) & 1u)) code = 0;
+        const int sh = 8 * (r & 3);
+        pk[r >> 2] = (pk[r >> 2] & ~(0xFFu << sh)) | ((uint32_t)code << sh);
+      }
+    }
+  }
+  return v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+}
+
+template <int D, bool DBG>
+struct Int4Kernel {
+  static constexpr int KS = D / 32;        // k-steps of 32 channels for QK^T
+  static constexpr int DB = D / 32;        // 32-channel blocks of O^T
+  static constexpr int KStride = D + 16;   // K tile row in LDS (bytes)
+  static constexpr int KB = D / 4;         // bytes of packed K (and of V^T) per thread per tile
+  static constexpr int TPR = 256 / D;      // threads per packed V^T row
+
+  // One key tile, part 1: S^T, running max, P codes.  TAIL: keys >= N exist
+  // in this tile.
+  template <bool TAIL>
+  __device__ __forceinline__ static void scores(const Int4Args& a, const Int4Debug& dbg, int bh,
+                                                int t, const uint8_t* sk, const v4i (&qf)[KS],
+                                                float qs, float& m, float& l, v16f (&O)[DB],
+                                                v4i (&P)[4]) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int col = lane & 31, hh = lane >> 5;
+    const size_t sidx = (size_t)bh * a.NB + t;
+
+    v16i S[4];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      S[sub] = v16i{0};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const v4i kf = *(const v4i*)(sk + (32 * sub + col) * KStride + 32 * ks + 16 * hh);
+        S[sub] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[ks], S[sub], 0, 0, 0);
+      }
+    }
+
+    uint32_t valid[4] = {0xffffu, 0xffffu, 0xffffu, 0xffffu};
+    if (TAIL) {
+      const int nv = a.N - t * kBlock;
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        uint32_t vm = 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * sub + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key < nv) vm |= 1u << r;
+          else S[sub][r] = INT32_MIN;
+        }
+        valid[sub] = vm;
+      }
+    }
+
+    int mx = INT32_MIN;
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = max(mx, S[sub][r]);
+    mx = max(mx, __shfl_xor(mx, 32, 64));
+
+    const float ct = qs * a.k_scale[sidx];
+    const float smax = (float)(mx >> 8) * ct;
+    const float mnew = fmaxf(m, smax);
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    if (wave_any(alpha != 1.0f)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
+    }
+    m = mnew;
+    const CodeCtx cx = make_ctx(ct, mnew, a.log2_15);
+
+    // the tile's terms are summed on their own first: adding ~10^4 terms per
+    // lane straight into the running l would drop the ones below half an ulp
+    float ls = 0.0f;
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      float f[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) f[r] = (float)S[sub][r];
+      P[sub] = pcode16<TAIL>(f, cx, a.tau, ls, valid[sub]);
+    }
+    l = fmaf(l, alpha, ls);
+
+    if (DBG) {
+      const int q = 32 * w + col;
+      const size_t npad = (size_t)a.NB * kBlock;
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const size_t key = (size_t)t * kBlock + 32 * sub + 8 * (r >> 2) + 4 * hh + (r & 3);
+          dbg.s_int[q * npad + key] = S[sub][r] >> 8;
+          dbg.p_code[q * npad + key] = (uint8_t)((uint32_t)P[sub][r >> 2] >> (8 * (r & 3)));
+        }
+    }
+
+  }
+
+  // One key tile, part 2: O^T = alpha O^T + (v_scale/16) V^T P^T.
+  __device__ __forceinline__ static void pv(const Int4Args& a, const Int4Debug& dbg, int bh, int t,
+                                            const uint8_t* sv, const v4i (&P)[4], v16f (&O)[DB]) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int col = lane & 31, hh = lane >> 5;
+    const float sv16 = a.v_scale[(size_t)bh * a.NB + t] * 0.0625f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      v16i pv = v16i{0};
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        const v4i vf = *(const v4i*)(sv + (32 * db + col) * kVStride + 32 * sub + 16 * hh);
+        pv = __builtin_amdgcn_mfma_i32_32x32x32_i8(vf, P[sub], pv, 0, 0, 0);
+      }
+      if (DBG) {
+        const int q = 32 * w + col;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int d = 32 * db + 8 * (r >> 2) + 4 * hh + (r & 3);
+          dbg.pv_int[((size_t)t * kBlock + q) * D + d] = pv[r] >> 4;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) O[db][r] = fmaf((float)pv[r], sv16, O[db][r]);
+    }
+  }
+
+  __device__ static void run(const Int4Args& a, const Int4Debug& dbg) {
+    __shared__ __align__(16) uint8_t sk[2][kBlock * KStride];
+    __shared__ __align__(16) uint8_t sv[2][D * kVStride];
+    const int qb = DBG ? dbg.q_block : blockIdx.x;
+    const int bh = DBG ? dbg.bh : blockIdx.y;
+    if (!DBG && !a.run.test(bh)) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int col = lane & 31, hh = lane >> 5;
+    const int NB = a.NB;
+    const size_t rows0 = (size_t)bh * NB * kBlock;   // first packed row of this head
+
+    v4i qf[KS];
+    {
+      const uint8_t* qrow = a.q4 + (rows0 + (size_t)qb * kBlock + 32 * w + col) * (D / 2);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint2 p = *(const uint2*)(qrow + 16 * ks + 8 * hh);
+        qf[ks] = v4i{(int)unpack_lo(p.x), (int)unpack_hi(p.x), (int)unpack_lo(p.y),
+                     (int)unpack_hi(p.y)};
+      }
+    }
+    const float qs = a.q_scale_l2[(size_t)bh * NB + qb];
+
+    uint4 kreg[KB / 16], vreg[KB / 16];
+    auto gload = [&](int t) {
+      const uint8_t* ks = a.k4 + (rows0 + (size_t)t * kBlock + (tid >> 1)) * (D / 2) + (tid & 1) * KB;
+      const uint8_t* vs = a.v4 + (((size_t)bh * NB + t) * D + tid / TPR) * 64 + (tid % TPR) * KB;
+#pragma unroll
+      for (int i = 0; i < KB / 16; ++i) {
+        kreg[i] = *(const uint4*)(ks + 16 * i);
+        vreg[i] = *(const uint4*)(vs + 16 * i);
+      }
+    };
+    auto lstore = [&](int buf) {
+      uint8_t* kd = sk[buf] + (tid >> 1) * KStride + (tid & 1) * (D / 2);
+      uint8_t* vd = sv[buf] + (tid / TPR) * kVStride + (tid % TPR) * (D / 2);
+#pragma unroll
+      for (int i = 0; i < KB / 16; ++i) {
+        const uint4 p = kreg[i];
+        *(uint4*)(kd + 32 * i) = uint4{unpack_lo(p.x), unpack_hi(p.x), unpack_lo(p.y), unpack_hi(p.y)};
+        *(uint4*)(kd + 32 * i + 16) = uint4{unpack_lo(p.z), unpack_hi(p.z), unpack_lo(p.w), unpack_hi(p.w)};
+        // V^T: a packed 16-byte chunk is one 32-key subtile (groups g = 0..3 of 8
+        // keys).  Dword slot s of the subtile row receives keys
+        // 8(s%4) + 4(s/4) .. +3, which is the key order of the P^T operand
+        // taken straight from the S^T accumulator layout.
+        const uint4 q = vreg[i];
+        *(uint4*)(vd + 32 * i) = uint4{unpack_lo(q.x), unpack_lo(q.y), unpack_lo(q.z), unpack_lo(q.w)};
+        *(uint4*)(vd + 32 * i + 16) = uint4{unpack_hi(q.x), unpack_hi(q.y), unpack_hi(q.z), unpack_hi(q.w)};
+      }
+    };
+
+    float m = -INFINITY, l = 0.0f;
+    v16f O[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) O[db] = v16f{0.0f};
+
+    const int NT = NB;
+    const bool ragged = (a.N % kBlock) != 0;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+#pragma unroll 1
+    for (int t = 0; t < NT; ++t) {
+      const int buf = t & 1;
+      v4i P[4];
+      if (ragged && t == NT - 1)
+        scores<true>(a, dbg, bh, t, sk[buf], qf, qs, m, l, O, P);
+      else
+        scores<false>(a, dbg, bh, t, sk[buf], qf, qs, m, l, O, P);
+      // the next tile's global loads overlap the P.V products; issuing them
+      // here keeps their registers off the score phase's peak
+      if (t + 1 < NT) gload(t + 1);
+      pv(a, dbg, bh, t, sv[buf], P, O);
+      if (t + 1 < NT) lstore(buf ^ 1);
+      __syncthreads();
+    }
+
+    l += __shfl_xor(l, 32, 64);
+    const int query = qb * kBlock + 32 * w + col;
+    if (DBG && hh == 0) {
+      dbg.m_final[32 * w + col] = m;
+      dbg.l_final[32 * w + col] = l * (1.0f / 15.0f);
+    }
+    if (query < a.N) {
+      const float il = 1.0f / l;
+      uint16_t* orow = a.o + ((size_t)bh * a.N + query) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * db + 8 * g + 4 * hh;
+          uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[db][4 * g] * il)) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[db][4 * g + 1] * il)) << 16);
+          uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[db][4 * g + 2] * il)) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[db][4 * g + 3] * il)) << 16);
+          *(uint2*)(orow + d0) = uint2{w0, w1};
+        }
+    }
+  }
+};
+
+template <int D, bool DBG>
+__global__ __launch_bounds__(kThreads, 2) void k_int4_attn(Int4Args a, Int4Debug dbg) {
+  Int4Kernel<D, DBG>::run(a, dbg);
+}
+
+hipError_t launch_int4(int D, int BH, const Int4Args& a, const Int4Debug* dbg, hipStream_t st) {
+  Int4Debug none{};
+  if (dbg == nullptr) {
+    dim3 grid(a.NB, BH);
+    if (D == 128)
+      hipLaunchKernelGGL((k_int4_attn<128, false>), grid, dim3(kThreads), 0, st, a, none);
+    else
+      hipLaunchKernelGGL((k_int4_attn<64, false>), grid, dim3(kThreads), 0, st, a, none);
+  } else {
+    if (D == 128)
+      hipLaunchKernelGGL((k_int4_attn<128, true>), dim3(1), dim3(kThreads), 0, st, a, *dbg);
+    else
+      hipLaunchKernelGGL((k_int4_attn<64, true>), dim3(1), dim3(kThreads), 0, st, a, *dbg);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- self-tests
+
+struct SweepArgs {
+  float tau[15];
+  float log2_15;
+  uint32_t mag_lo, count, max_trans;
+  uint32_t *trans, *n_trans;
+};
+
+// Each lane evaluates 16 consecutive magnitudes (x = -magnitude, c = 1, m = 0)
+// and the 16 magnitudes one below, then reports every change of code.
+__global__ __launch_bounds__(256) void k_pcode_sweep(SweepArgs a) {
+  const uint32_t idx = blockIdx.x * 256u + threadIdx.x;
+  const uint32_t b0 = a.mag_lo + 16u * idx;
+  const CodeCtx cx = make_ctx(1.0f, 0.0f, a.log2_15);
+  float f[16], fp[16];
+  uint32_t live = 0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const uint32_t b = b0 + r;
+    const bool in = (16u * idx + r) < a.count;
+    live |= (in ? 1u : 0u) << r;
+    const uint32_t bp = b == 0 ? 0u : b - 1u;
+    f[r] = -__uint_as_float(in ? b : 0u) * 256.0f;
+    fp[r] = -__uint_as_float(in ? bp : 0u) * 256.0f;
+  }
+  float ls = 0.0f;
+  const v4i c = pcode16<false>(f, cx, a.tau, ls, 0xffffu);
+  const v4i cp = pcode16<false>(fp, cx, a.tau, ls, 0xffffu);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const uint32_t cc = ((uint32_t)c[r >> 2] >> (8 * (r & 3))) & 0xffu;
+    const uint32_t pc = ((uint32_t)cp[r >> 2] >> (8 * (r & 3))) & 0xffu;
+    if (((live >> r) & 1u) && cc != pc) {
+      const uint32_t i = atomicAdd(a.n_trans, 1u);
+      if (i < a.max_trans) {
+        a.trans[3 * i] = b0 + r;
+        a.trans[3 * i + 1] = pc;
+        a.trans[3 * i + 2] = cc;
+      }
+    }
+  }
+}
+
+hipError_t launch_pcode_sweep(uint32_t mag_lo, uint32_t count, const float tau[15], float log2_15,
+                              uint32_t* transitions, uint32_t max_transitions, uint32_t* n_trans,
+                              hipStream_t st) {
+  SweepArgs a;
+  for (int k = 0; k < 15; ++k) a.tau[k] = tau[k];
+  a.log2_15 = log2_15;
+  a.mag_lo = mag_lo;
+  a.count = count;
+  a.max_trans = max_transitions;
+  a.trans = transitions;
+  a.n_trans = n_trans;
+  const uint32_t lanes = (count + 15u) / 16u;
+  const uint32_t blocks = (lanes + 255u) / 256u;
+  hipLaunchKernelGGL(k_pcode_sweep, dim3(blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+struct EvalArgs {
+  float tau[15];
+  float log2_15, c, m;
+  const int32_t* I;
+  uint8_t* codes;
+};
+
+__global__ __launch_bounds__(256) void k_pcode_eval(EvalArgs a) {
+  const size_t base = ((size_t)blockIdx.x * 256u + threadIdx.x) * 16u;
+  const CodeCtx cx = make_ctx(a.c, a.m, a.log2_15);
+  float f[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) f[r] = (float)(a.I[base + r] * 256);
+  float ls = 0.0f;
+  const v4i c = pcode16<false>(f, cx, a.tau, ls, 0xffffu);
+  *(v4i*)(a.codes + base) = c;
+}
+
+hipError_t launch_pcode_eval(const int32_t* I, uint32_t n, float c, float m, const float tau[15],
+                             float log2_15, uint8_t* codes, hipStream_t st) {
+  EvalArgs a;
+  for (int k = 0; k < 15; ++k) a.tau[k] = tau[k];
+  a.log2_15 = log2_15;
+  a.c = c;
+  a.m = m;
+  a.I = I;
+  a.codes = codes;
+  hipLaunchKernelGGL(k_pcode_eval, dim3(n / 4096u), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace rotattn

@@ -1,0 +1,230 @@
+// K4: gfx950 roofline denominators measured on the box -- HBM copy bandwidth,
+// i8 and f16 MFMA rates, VALU issue rates of the instructions the softmax and
+// P-code path use, and MFMA/VALU co-issue.  Also the plain copy kernel of known
+// size against which rocprofv3's FETCH_SIZE / WRITE_SIZE counters are scaled.
+//
+//   rotattn_microbench [--copy-only] [--copy-mib N]
+//
+// Prints one JSON object.  Each rate kernel runs a few milliseconds with
+// enough independent chains per lane and waves per SIMD to be throughput-bound.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define CK(x)                                                                        \
+  do {                                                                               \
+    hipError_t e_ = (x);                                                             \
+    if (e_ != hipSuccess) {                                                          \
+      fprintf(stderr, "HIP error %s at %s:%d\n", hipGetErrorString(e_), __FILE__, __LINE__); \
+      exit(1);                                                                       \
+    }                                                                                \
+  } while (0)
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+__global__ __launch_bounds__(256) void k_copy(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                               size_t n) {
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (; i < n; i += stride) dst[i] = src[i];
+}
+
+constexpr int kChains = 8;
+
+#define RATE_KERNEL(NAME, BODY)                                          \
+  __global__ __launch_bounds__(256) void NAME(float* out, int iters) {   \
+    float a[kChains];                                                    \
+    for (int j = 0; j < kChains; ++j) a[j] = 1e-3f * (threadIdx.x + j);  \
+    for (int i = 0; i < iters; ++i) {                                    \
+      _Pragma("unroll") for (int j = 0; j < kChains; ++j) { BODY; }      \
+    }                                                                    \
+    float s = 0;                                                         \
+    for (int j = 0; j < kChains; ++j) s += a[j];                         \
+    if (s == 12345.678f) out[threadIdx.x] = s;                           \
+  }
+
+// one instruction per chain step
+RATE_KERNEL(k_fma, a[j] = __builtin_fmaf(a[j], 0.999f, -1e-4f))
+RATE_KERNEL(k_exp, a[j] = __builtin_amdgcn_exp2f(a[j]))
+RATE_KERNEL(k_fract, a[j] = __builtin_amdgcn_fractf(a[j] + 0.37f))
+RATE_KERNEL(k_cvt, a[j] = (float)(int)a[j] + 0.5f)
+
+__global__ __launch_bounds__(256) void k_cvtpk(float* out, int iters) {
+  float a[kChains];
+  uint32_t acc = 0;
+  for (int j = 0; j < kChains; ++j) a[j] = 1e-3f * (threadIdx.x + j);
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < kChains; ++j) acc = __builtin_amdgcn_cvt_pk_u8_f32(a[j], j & 3, acc);
+  }
+  if (acc == 0x12345678u) out[threadIdx.x] = (float)acc;
+}
+
+__global__ __launch_bounds__(256) void k_mfma_i8(float* out, int iters) {
+  v4i a = {(int)threadIdx.x, 1, 2, 3}, b = {3, 2, 1, (int)threadIdx.x};
+  v16i c[4] = {};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c[j], 0, 0, 0);
+  }
+  int s = 0;
+  for (int j = 0; j < 4; ++j) for (int r = 0; r < 16; ++r) s += c[j][r];
+  if (s == 12345) out[threadIdx.x] = (float)s;
+}
+
+__global__ __launch_bounds__(256) void k_mfma_f16(float* out, int iters) {
+  v8h a, b;
+  for (int j = 0; j < 8; ++j) { a[j] = (_Float16)(1e-3f * threadIdx.x); b[j] = (_Float16)0.5f; }
+  v16f c[4] = {};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c[j], 0, 0, 0);
+  }
+  float s = 0;
+  for (int j = 0; j < 4; ++j) for (int r = 0; r < 16; ++r) s += c[j][r];
+  if (s == 12345.f) out[threadIdx.x] = s;
+}
+
+// co-issue: even waves run the i8 MFMA loop, odd waves an FMA loop
+__global__ __launch_bounds__(256) void k_mix(float* out, int iters, int valu_per_mfma) {
+  const int wave = threadIdx.x >> 6;
+  if (wave & 1) {
+    float a[kChains];
+    for (int j = 0; j < kChains; ++j) a[j] = 1e-3f * (threadIdx.x + j);
+    const int n = iters * valu_per_mfma * 4 / kChains;
+    for (int i = 0; i < n; ++i) {
+#pragma unroll
+      for (int j = 0; j < kChains; ++j) a[j] = __builtin_fmaf(a[j], 0.999f, -1e-4f);
+    }
+    float s = 0;
+    for (int j = 0; j < kChains; ++j) s += a[j];
+    if (s == 12345.678f) out[threadIdx.x] = s;
+  } else {
+    v4i a = {(int)threadIdx.x, 1, 2, 3}, b = {3, 2, 1, (int)threadIdx.x};
+    v16i c[4] = {};
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c[j], 0, 0, 0);
+    }
+    int s = 0;
+    for (int j = 0; j < 4; ++j) for (int r = 0; r < 16; ++r) s += c[j][r];
+    if (s == 12345) out[threadIdx.x] = (float)s;
+  }
+}
+
+static float time_ms(void (*launch)(void*), void* ctx, int reps) {
+  hipEvent_t e0, e1;
+  CK(hipEventCreate(&e0));
+  CK(hipEventCreate(&e1));
+  launch(ctx);
+  CK(hipDeviceSynchronize());
+  CK(hipEventRecord(e0));
+  for (int r = 0; r < reps; ++r) launch(ctx);
+  CK(hipEventRecord(e1));
+  CK(hipEventSynchronize(e1));
+  float ms;
+  CK(hipEventElapsedTime(&ms, e0, e1));
+  CK(hipEventDestroy(e0));
+  CK(hipEventDestroy(e1));
+  return ms / reps;
+}
+
+struct RateCtx {
+  void (*kern)(float*, int);
+  float* out;
+  int iters, blocks;
+};
+static void launch_rate(void* p) {
+  RateCtx* c = (RateCtx*)p;
+  hipLaunchKernelGGL(c->kern, dim3(c->blocks), dim3(256), 0, 0, c->out, c->iters);
+}
+struct MixCtx {
+  float* out;
+  int iters, blocks, vpm;
+};
+static void launch_mix(void* p) {
+  MixCtx* c = (MixCtx*)p;
+  hipLaunchKernelGGL(k_mix, dim3(c->blocks), dim3(256), 0, 0, c->out, c->iters, c->vpm);
+}
+struct CopyCtx {
+  const uint4* src;
+  uint4* dst;
+  size_t n;
+};
+static void launch_copy(void* p) {
+  CopyCtx* c = (CopyCtx*)p;
+  hipLaunchKernelGGL(k_copy, dim3(256 * 32), dim3(256), 0, 0, c->src, c->dst, c->n);
+}
+
+int main(int argc, char** argv) {
+  bool copy_only = false;
+  size_t copy_mib = 4096;
+  for (int i = 1; i < argc; ++i) {
+    if (!strcmp(argv[i], "--copy-only")) copy_only = true;
+    else if (!strcmp(argv[i], "--copy-mib") && i + 1 < argc) copy_mib = (size_t)atol(argv[++i]);
+  }
+  hipDeviceProp_t prop;
+  CK(hipGetDeviceProperties(&prop, 0));
+  const int cus = prop.multiProcessorCount;
+  printf("{\"device\": \"%s\", \"cus\": %d", prop.gcnArchName, cus);
+
+  const size_t bytes = copy_mib << 20;
+  uint4 *src, *dst;
+  CK(hipMalloc(&src, bytes));
+  CK(hipMalloc(&dst, bytes));
+  CK(hipMemset(src, 1, bytes));
+  CopyCtx cc{src, dst, bytes / 16};
+  const float cms = time_ms(launch_copy, &cc, copy_only ? 3 : 10);
+  printf(", \"copy_bytes_each_way\": %zu, \"copy_ms\": %.4f, \"copy_GBps\": %.1f", bytes, cms,
+         2.0 * bytes / (cms * 1e-3) / 1e9);
+  CK(hipFree(src));
+  CK(hipFree(dst));
+  if (copy_only) {
+    printf("}\n");
+    return 0;
+  }
+
+  float* out;
+  CK(hipMalloc(&out, 1024 * sizeof(float)));
+  const int blocks = cus * 8;   // 8 waves per SIMD
+  struct {
+    const char* name;
+    void (*k)(float*, int);
+    double per_iter;   // lane-ops per lane per iteration
+  } vk[] = {{"fma", k_fma, kChains}, {"exp", k_exp, kChains},
+            {"add_fract_steps", k_fract, kChains},        // v_add + v_fract per step
+            {"cvt_cvt_add_steps", k_cvt, kChains},        // f32->i32, i32->f32, v_add per step
+            {"cvt_pk_u8", k_cvtpk, kChains}};
+  for (auto& v : vk) {
+    RateCtx c{v.k, out, 4000, blocks};
+    const float ms = time_ms(launch_rate, &c, 3);
+    const double lane_ops = (double)blocks * 256 * c.iters * v.per_iter;
+    printf(", \"%s_G_per_s\": %.1f", v.name, lane_ops / (ms * 1e-3) / 1e9);
+  }
+  {
+    RateCtx c{k_mfma_i8, out, 2000, blocks};
+    const float ms = time_ms(launch_rate, &c, 3);
+    const double ops = (double)blocks * 4 * c.iters * 4 * 65536.0;
+    printf(", \"mfma_i8_32x32x32_TOPS\": %.1f", ops / (ms * 1e-3) / 1e12);
+  }
+  {
+    RateCtx c{k_mfma_f16, out, 2000, blocks};
+    const float ms = time_ms(launch_rate, &c, 3);
+    const double ops = (double)blocks * 4 * c.iters * 4 * 32768.0;
+    printf(", \"mfma_f16_32x32x16_TFLOPS\": %.1f", ops / (ms * 1e-3) / 1e12);
+  }
+  for (int vpm : {4, 8, 16}) {
+    MixCtx c{out, 2000, blocks, vpm};
+    const float ms = time_ms(launch_mix, &c, 3);
+    const double ops = (double)blocks * 2 * c.iters * 4 * 65536.0;   // two MFMA waves per block
+    printf(", \"mix_i8_with_%d_fma_per_mfma_TOPS\": %.1f", vpm, ops / (ms * 1e-3) / 1e12);
+  }
+  printf("}\n");
+  CK(hipFree(out));
+  return 0;
+}

@@ -1,0 +1,89 @@
+// Internal declarations shared by the HIP translation units of librotattn.so.
+// gfx950 (CDNA4) only: wave64, MFMA, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/rotattn.h"
+
+namespace rotattn {
+
+constexpr int kBlock = ROTATTN_BLOCK;          // tokens per quantization block / key tile
+constexpr int kHeadWords = ROTATTN_MAX_HEADS / 32;
+
+// Head-selection bitmask passed by value as a kernel argument.
+struct HeadBits {
+  uint32_t w[kHeadWords];
+  __host__ __device__ bool test(int bh) const { return (w[bh >> 5] >> (bh & 31)) & 1u; }
+};
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// Nibble layout of a packed INT4 dword: 8 elements e0..e7, byte i holds e_i in
+// its low nibble and e_{i+4} in its high nibble.  The two unpack steps below
+// give e0..e3 and e4..e7 as int8 lanes holding 16*e (exact: |16*e| <= 112),
+// so an i8 MFMA over unpacked operands accumulates 256*I (two unpacked
+// operands) or 16*I (one unpacked operand against unscaled int8).
+__device__ __forceinline__ uint32_t unpack_lo(uint32_t p) { return (p << 4) & 0xF0F0F0F0u; }
+__device__ __forceinline__ uint32_t unpack_hi(uint32_t p) { return p & 0xF0F0F0F0u; }
+
+// Pack 8 int8 codes (two dwords, e0..e3 and e4..e7) into one nibble dword.
+__device__ __forceinline__ uint32_t pack_nibbles(uint32_t lo4, uint32_t hi4) {
+  return (lo4 & 0x0F0F0F0Fu) | ((hi4 & 0x0F0F0F0Fu) << 4);
+}
+
+struct PrologueArgs {
+  const uint16_t *q, *k, *v;
+  const float *cos_t, *sin_t, *cos_h, *sin_h, *cos_w, *sin_w;
+  const double* rot64;          // [3][64*64], partition a at a*4096, [d_a][d_a] row-major
+  uint8_t *q4, *k4, *v4;
+  float *q_scale_l2, *k_scale, *v_scale;
+  uint16_t *q_rope, *k_rope;
+  int N, NB, grid_h, grid_w;
+  float kappa;
+  HeadBits fallback;            // bit set: RoPE'd fp16 only
+};
+
+struct Int4Args {
+  const uint8_t *q4, *k4, *v4;
+  const float *q_scale_l2, *k_scale, *v_scale;
+  uint16_t* o;
+  int N, NB;
+  float log2_15;                // fl32(log2(15))
+  float tau[15];                // P-code thresholds
+  HeadBits run;                 // bit set: run this head
+};
+
+struct Int4Debug {
+  int32_t* s_int;
+  uint8_t* p_code;
+  int32_t* pv_int;
+  float *m_final, *l_final;
+  int bh, q_block;
+};
+
+struct Fp16Args {
+  const uint16_t *q, *k, *v;
+  uint16_t* o;
+  int N;
+  float kappa;
+  HeadBits run;
+};
+
+// Launchers (each defined next to its kernel).  Return a hipError_t.
+hipError_t launch_rot_to_f64(const float* rt, const float* rh, const float* rw, int dt, int dh,
+                             int dw, double* out, hipStream_t st);
+hipError_t launch_prologue(int D, int dt, int BH, const PrologueArgs& a, hipStream_t st);
+hipError_t launch_int4(int D, int BH, const Int4Args& a, const Int4Debug* dbg, hipStream_t st);
+hipError_t launch_fp16(int D, int BH, const Fp16Args& a, hipStream_t st);
+hipError_t launch_pcode_sweep(uint32_t mag_lo, uint32_t count, const float tau[15], float log2_15,
+                              uint32_t* transitions, uint32_t max_transitions, uint32_t* n_trans,
+                              hipStream_t st);
+hipError_t launch_pcode_eval(const int32_t* I, uint32_t n, float c, float m, const float tau[15],
+                             float log2_15, uint8_t* codes, hipStream_t st);
+
+}  // namespace rotattn
