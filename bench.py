@@ -33,7 +33,7 @@ METRIC = "effective attention TOPS at 1 MI355X + % of i8 MFMA peak, N=75600 D=12
 PEAK_I8_TOPS = 5000.0        # MI355X dense int8 MFMA (5.0 POPS)
 PEAK_F16_TFLOPS = 2500.0     # MI355X dense fp16 MFMA (2.5 PFLOPS)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E (8 TB/s)
-PMC_FILE = os.path.join(ROOT, "profiles", "int4_attn_720p_pmc.txt")
+PMC_FILE = os.path.join(ROOT, "profiles", "int4_attn_f8_720p_pmc.txt")
 KERNEL_SRC = os.path.join(ROOT, "video_diffusion_transformers_amd", "csrc", "int4_attn.hip")
 
 
@@ -146,7 +146,7 @@ def main():
     traffic = traffic_from_profile(k2_ms)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_I8_TOPS,
                 "unit": "TOPS", "frac": round(achieved / PEAK_I8_TOPS, 4), "traffic": traffic,
-                "kernel": "k_int4_attn<128>", "algorithmic_ops_per_launch": int4_ops}
+                "kernel": "k_int4_attn_f8<128>", "algorithmic_ops_per_launch": int4_ops}
     # prologue: algorithmic HBM bytes per token per head (read Q,K,V fp16; write
     # packed INT4 Q,K,V; block scales are negligible)
     k1_bytes = BH * N * (3 * 2 * D + 3 * D / 2)
@@ -160,9 +160,21 @@ def main():
         "event_step_ms": round(float(tot.mean()), 4),
     }
 
+    # the same INT4 attention on the nibble-packed layout (i8 MFMA kernel)
+    prep_p = R.PreparedDevice(shape, with_rope=False, layout=R.LAYOUT_PACKED)
+    R.prepare_qkv(shape, qd, kd, vd, rr, prep_p, mask)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    R.int4_fwd(shape, prep_p, o, mask=mask)
+    e0.record()
+    for _ in range(3):
+        R.int4_fwd(shape, prep_p, o, mask=mask)
+    e1.record()
+    torch.cuda.synchronize()
+    kernels["int4_attn_packed_i8_ms"] = round(e0.elapsed_time(e1) / 3, 4)
+    del prep_p
+
     # mixed_fwd (one C call) on the same inputs, as a cross-check of the sequence
     ws = torch.empty(R.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     R.mixed_fwd(shape, qd, kd, vd, rr, mask, ws, o)
     e0.record()
     for _ in range(3):

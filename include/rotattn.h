@@ -85,28 +85,47 @@ typedef struct rotattn_rope_rot {
 } rotattn_rope_rot;
 
 /*
+ * Layout of the INT4 codes in a rotattn_prepared.
+ *  ROTATTN_LAYOUT_PACKED: two codes per byte (4-bit two's complement); the
+ *      attention kernel multiplies them on i8 MFMA.
+ *  ROTATTN_LAYOUT_FP8: one code per byte, encoded as the FP8 E4M3 value of
+ *      the integer (every integer in [-15, 15] is exact in E4M3); the attention
+ *      kernel multiplies them on the f8f6f4 MFMA with fp32 accumulation.  The
+ *      integer products and sums are the same exact integers as on i8 MFMA.
+ */
+typedef enum rotattn_layout {
+  ROTATTN_LAYOUT_PACKED = 0,
+  ROTATTN_LAYOUT_FP8 = 1
+} rotattn_layout;
+
+/*
  * Output of rotattn_prepare_qkv (device, caller-allocated; carve it from one
  * buffer with rotattn_prepared_carve).  NB = ceil(N/128), N_pad = 128*NB.
- *  q4, k4: [B*H][N_pad][D/2] bytes: INT4 codes in [-7, 7], two's complement
- *          nibbles.  Each group of 8 consecutive channels 8g..8g+7 occupies 4
- *          bytes; byte i holds channel 8g+i in its low nibble and 8g+4+i in
- *          its high nibble.  Rows N..N_pad-1 are zero.
- *  v4:     [B*H][NB][D][64] bytes: V codes per 128-token block, transposed
- *          (channel-major): row d holds the 128 keys of the block packed the
- *          same way along keys (byte i of group g = keys 8g+i, 8g+4+i).
+ *  layout: a rotattn_layout.
+ *  q4, k4: INT4 codes in [-7, 7] of Q and K, rows N..N_pad-1 zero.
+ *          PACKED: [B*H][N_pad][D/2] bytes.  Each group of 8 consecutive
+ *          channels 8g..8g+7 occupies 4 bytes; byte i holds channel 8g+i in
+ *          its low nibble and 8g+4+i in its high nibble.
+ *          FP8: [B*H][N_pad][D] bytes, E4M3 of the code, channel order.
+ *  v4:     V codes per 128-token block, transposed (channel-major).
+ *          PACKED: [B*H][NB][D][64]: row d holds the 128 keys of the block
+ *          packed along keys as above (byte i of group g = keys 8g+i, 8g+4+i).
+ *          FP8: [B*H][NB][D][128]: row d holds the block's 128 keys as E4M3
+ *          codes, each 64-key half in the operand order of the P.V product:
+ *          byte 32h+j (h in {0,1}, j < 32) is key 8(j%16/4) + 4h + j%4, plus
+ *          32 when j >= 16.
  *  q_scale_l2, k_scale, v_scale: [B*H][NB] fp32 block scales (amax/7).
  *          q_scale_l2 = fl(q_scale * kappa), kappa = fl32(log2(e)/sqrt(D)), so
  *          that 2^(I * q_scale_l2 * k_scale) = exp(QK^T / sqrt(D)).
  *  q_rope, k_rope: [B*H][N][D] fp16 RoPE'd (not rotated, not quantized) Q/K,
  *          written for fallback heads only; may be NULL when no head falls
  *          back.
- *  rot64:  library scratch, 3*64*64 doubles (the rotation in fp64).
  */
 typedef struct rotattn_prepared {
+  int32_t layout;
   uint8_t *q4, *k4, *v4;
   float *q_scale_l2, *k_scale, *v_scale;
   uint16_t *q_rope, *k_rope;
-  double *rot64;
 } rotattn_prepared;
 
 /*
@@ -150,18 +169,19 @@ int rotattn_pcode_thresholds_host(float tau[15]);
 /* Host: kappa = fl32(log2(e)/sqrt(D)). */
 float rotattn_kappa_host(int32_t D);
 
-/* Bytes for a rotattn_prepared (with_rope != 0 adds the fp16 Q'/K' arrays). */
-size_t rotattn_prepared_bytes(const rotattn_shape* s, int with_rope);
+/* Bytes for a rotattn_prepared of the given rotattn_layout (with_rope != 0
+ * adds the fp16 Q'/K' arrays); 0 for an invalid shape or layout. */
+size_t rotattn_prepared_bytes(const rotattn_shape* s, int with_rope, int layout);
 
 /* Lay a rotattn_prepared out in [base, base+bytes) (256-byte aligned parts). */
 int rotattn_prepared_carve(const rotattn_shape* s, void* base, size_t bytes,
-                           int with_rope, rotattn_prepared* out);
+                           int with_rope, int layout, rotattn_prepared* out);
 
 /*
  * Prologue.  For every head with fallback_mask_host[b*H+h] == 0 (or all heads
  * when the mask is NULL): 3D RoPE on Q and K in fp32, the partition-wise
  * rotation (fp64 accumulation, one rounding to fp32), per-block symmetric
- * INT4 quantization of Q, K, V and packing into `out`.  For a fallback head:
+ * INT4 quantization of Q, K, V, stored in out->layout.  For a fallback head:
  * RoPE'd fp16 Q'/K' into out->q_rope / out->k_rope only.
  */
 int rotattn_prepare_qkv(const rotattn_shape* s, const uint16_t* q,
@@ -172,9 +192,10 @@ int rotattn_prepare_qkv(const rotattn_shape* s, const uint16_t* q,
 
 /*
  * INT4 attention over the heads with fallback_mask_host[...] == 0 (all heads
- * when NULL): I = q4.k4^T on i8 MFMA, one-pass online softmax over 128-key
- * tiles in the log2 domain, P codes rne(15*2^(s-m)) against the running max,
- * PV = codes.v4 on i8 MFMA, O = acc / l written as fp16 into o [B][H][N][D].
+ * when NULL): I = q4.k4^T (i8 MFMA for the PACKED layout, f8f6f4 MFMA for
+ * FP8), one-pass online softmax over 128-key tiles in the log2 domain, P codes
+ * rne(15*2^(s-m)) against the running max, PV = codes.v4 on the same MFMA
+ * kind, O = acc / l written as fp16 into o [B][H][N][D].
  * dbg != NULL additionally runs one instrumented work-group for (dbg->b,
  * dbg->h, dbg->q_block) that fills the integer dumps.
  */
@@ -192,12 +213,13 @@ int rotattn_fp16_fwd(const rotattn_shape* s, const uint16_t* q_rope,
                      const uint8_t* head_select_host, uint16_t* o,
                      hipStream_t stream);
 
-/* Workspace bytes for rotattn_mixed_fwd (a rotattn_prepared with fp16 Q'/K'). */
+/* Workspace bytes for rotattn_mixed_fwd (a FP8-layout rotattn_prepared with
+ * fp16 Q'/K'). */
 size_t rotattn_workspace_bytes(const rotattn_shape* s);
 
 /*
- * Whole forward: prepare, INT4 attention for mask == 0 heads, FP16
- * attention for mask != 0 heads, all on `stream`, writing every head of o.
+ * Whole forward: prepare (FP8 layout), INT4 attention for mask == 0 heads,
+ * FP16 attention for mask != 0 heads, all on `stream`, writing every head of o.
  */
 int rotattn_mixed_fwd(const rotattn_shape* s, const uint16_t* q,
                       const uint16_t* k, const uint16_t* v,
@@ -207,24 +229,25 @@ int rotattn_mixed_fwd(const rotattn_shape* s, const uint16_t* q,
 
 /*
  * Self-test of the P-code device function (the exact code the attention
- * kernel uses).  Evaluates code(x) for x = -magnitude over the magnitude bit
- * patterns [mag_lo, mag_lo + count) with c = 1, m = 0, and records every
- * position where the code changes: transitions[3*i] = magnitude bits,
- * [3*i+1] = code before, [3*i+2] = code after, for i < max_transitions.
- * *n_transitions (device) receives the total count (zero it first).
+ * kernel of `layout` uses).  Evaluates code(x) for x = -magnitude over the
+ * magnitude bit patterns [mag_lo, mag_lo + count) with c = 1, m = 0, and
+ * records every position where the code changes: transitions[3*i] =
+ * magnitude bits, [3*i+1] = code before, [3*i+2] = code after, for
+ * i < max_transitions.  *n_transitions (device) receives the total count
+ * (zero it first).
  */
-int rotattn_pcode_sweep(uint32_t mag_lo, uint32_t count, uint32_t* transitions,
-                        uint32_t max_transitions, uint32_t* n_transitions,
-                        hipStream_t stream);
+int rotattn_pcode_sweep(int layout, uint32_t mag_lo, uint32_t count,
+                        uint32_t* transitions, uint32_t max_transitions,
+                        uint32_t* n_transitions, hipStream_t stream);
 
 /*
- * Self-test: P codes of raw integer scores through the attention kernel's
- * code path.  I: [n] int32 exact QK^T values, c: fl(q_scale_l2*k_scale),
+ * Self-test: P codes of raw integer scores through the code path of the
+ * attention kernel of `layout`.  I: [n] int32 exact QK^T values, c: fl(q_scale_l2*k_scale),
  * m: running max (log2 units, >= fl(I*c) for every element).  codes: [n]
  * uint8.  n must be a multiple of 4096.
  */
-int rotattn_pcode_eval(const int32_t* I, uint32_t n, float c, float m,
-                       uint8_t* codes, hipStream_t stream);
+int rotattn_pcode_eval(int layout, const int32_t* I, uint32_t n, float c,
+                       float m, uint8_t* codes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -28,6 +28,36 @@ def pack_rows(codes: np.ndarray) -> np.ndarray:
     return (c[:, :, :4] | (c[:, :, 4:] << 4)).reshape(n, D // 2)
 
 
+E4M3 = {0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44, 4: 0x48, 5: 0x4A, 6: 0x4C, 7: 0x4E}
+
+
+def fp8_bytes(codes: np.ndarray) -> np.ndarray:
+    """INT4 codes -> FP8 E4M3 bytes of the integers (the FP8 layout)."""
+    mag = np.abs(codes.astype(np.int16))
+    lut = np.array([E4M3[i] for i in range(8)], np.uint8)
+    return lut[mag] | np.where(codes < 0, 0x80, 0).astype(np.uint8)
+
+
+def fp8_vt_blocks(codes: np.ndarray, N_pad: int) -> np.ndarray:
+    """V codes [N, D] -> [NB, D, 128] FP8 bytes: per 128-token block, transposed,
+    each 64-key half in the P.V operand order (byte 32h + j holds key
+    32(j/16) + 8((j%16)/4) + 4h + j%4)."""
+    N, D = codes.shape
+    full = np.zeros((N_pad, D), np.int8)
+    full[:N] = codes
+    perm = np.empty(128, np.int64)
+    for c in range(2):
+        for h in range(2):
+            for j in range(32):
+                perm[64 * c + 32 * h + j] = 64 * c + 32 * (j // 16) + 8 * ((j % 16) // 4) + 4 * h + j % 4
+    assert sorted(perm) == list(range(128))
+    out = []
+    for b in range(N_pad // 128):
+        blk = full[b * 128:(b + 1) * 128]          # [128 keys, D]
+        out.append(fp8_bytes(blk[perm].T))          # [D, 128]
+    return np.stack(out)
+
+
 def pack_vt_blocks(codes: np.ndarray, N_pad: int) -> np.ndarray:
     """V codes [N, D] -> [NB, D, 64]: per 128-token block, transposed, packed along keys."""
     N, D = codes.shape
@@ -42,7 +72,7 @@ def pack_vt_blocks(codes: np.ndarray, N_pad: int) -> np.ndarray:
 class Run:
     """One config on the device: inputs, RoPE/rotation, prepared buffers."""
 
-    def __init__(self, cfg: synth.Config, step: int = 0):
+    def __init__(self, cfg: synth.Config, step: int = 0, layout: int = 1):
         torch = torch_cuda()
         from video_diffusion_transformers_amd import rotattn as R
         self.R = R
@@ -57,7 +87,8 @@ class Run:
         self.r64, self.r32 = synth.rotation_matrices(cfg.split)
         self.rr = R.RopeRotDevice(self.shape, self.r32)
         self.mask = synth.fallback_mask(cfg)
-        self.prep = R.PreparedDevice(self.shape, with_rope=True)
+        self.layout = layout
+        self.prep = R.PreparedDevice(self.shape, with_rope=True, layout=layout)
 
     def prepare(self, mask="cfg"):
         m = self.mask if isinstance(mask, str) else mask
@@ -69,10 +100,12 @@ class Run:
         torch.cuda.synchronize()
         BH, D, NB, N = self.cfg.BH, self.cfg.D, self.NB, self.cfg.N
         p = self.prep
+        w = D if self.layout == self.R.LAYOUT_FP8 else D // 2      # bytes per code row
+        vw = 128 if self.layout == self.R.LAYOUT_FP8 else 64
         out = {
-            "q4": p.view("q4", torch.uint8, BH * self.N_pad * D // 2).cpu().numpy().reshape(BH, self.N_pad, D // 2),
-            "k4": p.view("k4", torch.uint8, BH * self.N_pad * D // 2).cpu().numpy().reshape(BH, self.N_pad, D // 2),
-            "v4": p.view("v4", torch.uint8, BH * NB * D * 64).cpu().numpy().reshape(BH, NB, D, 64),
+            "q4": p.view("q4", torch.uint8, BH * self.N_pad * w).cpu().numpy().reshape(BH, self.N_pad, w),
+            "k4": p.view("k4", torch.uint8, BH * self.N_pad * w).cpu().numpy().reshape(BH, self.N_pad, w),
+            "v4": p.view("v4", torch.uint8, BH * NB * D * vw).cpu().numpy().reshape(BH, NB, D, vw),
         }
         for f in ("q_scale_l2", "k_scale", "v_scale"):
             out[f] = p.view(f, torch.float32, BH * NB).cpu().numpy().reshape(BH, NB)

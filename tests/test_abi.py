@@ -59,31 +59,38 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert L.rotattn_mixed_fwd(C.byref(s), nul, nul, nul, None, nul, nul, 0, nul, nul) == -1
     bad = R.make_shape(1, 2, (2, 4, 4), 64, (24, 20, 22))
     assert L.rotattn_mixed_fwd(C.byref(bad), nul, nul, nul, None, nul, nul, 0, nul, nul) == -2
-    assert L.rotattn_pcode_sweep(0, 0, nul, 0, nul, nul) == -1
+    assert L.rotattn_pcode_sweep(1, 0, 0, nul, 0, nul, nul) == -1
     t = (C.c_uint32 * 4)()
-    assert L.rotattn_pcode_sweep(0x7B000000, 0x01000000, t, 1, t, nul) == -7
-    assert L.rotattn_pcode_eval(t, 1000, C.c_float(1.0), C.c_float(0.0), t, nul) == -7
-    # an unaligned workspace is refused by the carve
+    assert L.rotattn_pcode_sweep(1, 0x7B000000, 0x01000000, t, 1, t, nul) == -7
+    assert L.rotattn_pcode_sweep(2, 0, 16, t, 1, t, nul) == -7          # unknown layout
+    assert L.rotattn_pcode_eval(1, t, 1000, C.c_float(1.0), C.c_float(0.0), t, nul) == -7
+    # an unaligned workspace is refused by the carve, and so is an unknown layout
     p = R.Prepared()
-    assert L.rotattn_prepared_carve(C.byref(s), C.c_void_p(8), 1 << 30, 1, C.byref(p)) == -5
-    assert L.rotattn_prepared_carve(C.byref(s), C.c_void_p(256), 16, 1, C.byref(p)) == -4
+    assert L.rotattn_prepared_carve(C.byref(s), C.c_void_p(8), 1 << 30, 1, 1, C.byref(p)) == -5
+    assert L.rotattn_prepared_carve(C.byref(s), C.c_void_p(256), 16, 1, 1, C.byref(p)) == -4
+    assert L.rotattn_prepared_carve(C.byref(s), C.c_void_p(256), 1 << 30, 1, 5, C.byref(p)) == -7
+    assert L.rotattn_prepared_bytes(C.byref(s), 1, 5) == 0
 
 
-def test_prepared_layout_sizes():
+@pytest.mark.parametrize("layout,code_bytes", [(R.LAYOUT_PACKED, 64), (R.LAYOUT_FP8, 128)])
+def test_prepared_layout_sizes(layout, code_bytes):
     s = R.shape_of(synth.CONFIGS["720p"])
     NB = R.n_blocks(s)
     assert NB == 591
-    n0 = R.lib().rotattn_prepared_bytes(C.byref(s), 0)
-    n1 = R.lib().rotattn_prepared_bytes(C.byref(s), 1)
-    packed = 40 * NB * 128 * 64
-    assert n0 >= 3 * packed + 3 * 40 * NB * 4 + 3 * 4096 * 8
+    n0 = R.lib().rotattn_prepared_bytes(C.byref(s), 0, layout)
+    n1 = R.lib().rotattn_prepared_bytes(C.byref(s), 1, layout)
+    codes = 40 * NB * 128 * code_bytes
+    assert n0 >= 3 * codes + 3 * 40 * NB * 4
     assert n1 - n0 >= 2 * 40 * 75600 * 128 * 2
-    assert R.workspace_bytes(s) == n1
+    if layout == R.LAYOUT_FP8:
+        assert R.workspace_bytes(s) == n1
     p = R.Prepared()
-    assert R.lib().rotattn_prepared_carve(C.byref(s), C.c_void_p(1 << 20), n1, 1, C.byref(p)) == 0
-    addrs = [p.q4, p.k4, p.v4, p.q_scale_l2, p.k_scale, p.v_scale, p.rot64, p.q_rope, p.k_rope]
+    assert R.lib().rotattn_prepared_carve(C.byref(s), C.c_void_p(1 << 20), n1, 1, layout,
+                                          C.byref(p)) == 0
+    assert p.layout == layout
+    addrs = [p.q4, p.k4, p.v4, p.q_scale_l2, p.k_scale, p.v_scale, p.q_rope, p.k_rope]
     assert all(a % 256 == 0 for a in addrs) and addrs == sorted(addrs)
-    assert p.k4 - p.q4 >= packed and max(addrs) < (1 << 20) + n1
+    assert p.k4 - p.q4 >= codes and max(addrs) < (1 << 20) + n1
 
 
 @pytest.mark.parametrize("name", ["tiny", "small", "480p", "720p"])

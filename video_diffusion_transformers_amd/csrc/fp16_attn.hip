@@ -173,20 +173,24 @@ struct Fp16Kernel {
 #pragma unroll
     for (int db = 0; db < DB; ++db) O[db] = v16f{0.0f};
     const int NT = (N + kKT - 1) / kKT;
-    const bool ragged = (N % kKT) != 0;
     gload(0);
     lstore(0);
     __syncthreads();
+    // full tiles in the loop, the last (possibly ragged) tile peeled off
 #pragma unroll 1
-    for (int t = 0; t < NT; ++t) {
+    for (int t = 0; t < NT - 1; ++t) {
       const int buf = t & 1;
-      if (t + 1 < NT) gload(t + 1);
-      if (ragged && t == NT - 1)
+      gload(t + 1);
+      tile<false>(a, t, sk[buf], sv[buf], qf, m, l, O);
+      lstore(buf ^ 1);
+      __syncthreads();
+    }
+    {
+      const int t = NT - 1, buf = t & 1;
+      if ((N % kKT) != 0)
         tile<true>(a, t, sk[buf], sv[buf], qf, m, l, O);
       else
         tile<false>(a, t, sk[buf], sv[buf], qf, m, l, O);
-      if (t + 1 < NT) lstore(buf ^ 1);
-      __syncthreads();
     }
     l += __shfl_xor(l, 32, 64);
     const int query = qb * kBlock + 32 * w + col;

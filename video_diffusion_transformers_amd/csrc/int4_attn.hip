@@ -39,7 +39,8 @@ constexpr int kThreads = 256;
 constexpr int kVStride = 144;   // V^T tile row: 128 keys + 16 bytes of padding
 
 struct CodeCtx {
-  float cq;      // c_t / 256 (scores arrive as 256*I)
+  float iscale;  // exact factor from the incoming score to I (2^-8 on i8 MFMA, 1 on fp8)
+  float cq;      // c_t * iscale
   float m15n;    // fl(log2(15)) - m'
   float ct;      // c_t
   float mnew;    // m'
@@ -50,27 +51,29 @@ __device__ __forceinline__ float ulp_pos(float v) {   // ulp of a positive norma
   return __uint_as_float(__float_as_uint(v) & 0x7F800000u) * 0x1p-23f;
 }
 
-__device__ __forceinline__ CodeCtx make_ctx(float ct, float mnew, float log2_15) {
+__device__ __forceinline__ CodeCtx make_ctx(float ct, float mnew, float log2_15,
+                                            float iscale = 0x1p-8f) {
   CodeCtx c;
+  c.iscale = iscale;
   c.ct = ct;
   c.mnew = mnew;
-  c.cq = ct * 0x1p-8f;
+  c.cq = ct * iscale;
   c.m15n = log2_15 - mnew;
   // error of the fused argument against x + log2(15) for scores that can
   // round to a code in 1..15 (|x| < 8), in log2 units:
   const float e = 0x1p-21f + ulp_pos(fabsf(mnew) + 8.0f);
   // 15.5 * ln 2 < 10.75; v_exp_f32 error < 1 ulp; 12x and +4e-6 are margin.
   c.delta = 12.0f * e + 4e-6f;
-  // c_t so small that c_t/256 is subnormal: never trust the fast path.
+  // c_t so small that c_t * iscale may be subnormal: never trust the fast path.
   if (ct != 0.0f && ct < 0x1p-100f) c.delta = 1.0f;
   return c;
 }
 
 __device__ __forceinline__ uint32_t wave_any(bool p) { return __ballot(p) != 0; }
 
-// Exact P code of one score (float f = 256*I exactly).
+// Exact P code of one score (float f = I / iscale exactly).
 __device__ __forceinline__ int exact_code(float f, const CodeCtx& cx, const float* tau) {
-  const float I = f * 0x1p-8f;     // exact
+  const float I = f * cx.iscale;   // exact (power of two)
   const float s = I * cx.ct;       // fl(I * c_t)
   const float x = s - cx.mnew;     // fl(s - m')
   int code = 0;
@@ -81,9 +84,14 @@ __device__ __forceinline__ int exact_code(float f, const CodeCtx& cx, const floa
 
 // 16 scores of one lane (one 32-key subtile) -> 16 u4 codes packed in byte
 // lanes (byte r = code of score r), and their unquantized 15*2^x added to lsum.
+//
+// fmax is the largest f of the group in this lane.  If in every lane of the
+// wave even that score maps below 1/2 - delta, every code of the group is 0
+// (exactly: exp2 and the fused argument are monotone, and the estimate is
+// within delta of 15*2^x), so rounding, packing and the guard are skipped.
 template <bool TAIL>
-__device__ __forceinline__ v4i pcode16(const float (&f)[16], const CodeCtx& cx, const float* tau,
-                                       float& lsum, uint32_t valid) {
+__device__ __forceinline__ v4i pcode16(const float (&f)[16], float fmax, const CodeCtx& cx,
+                                       const float* tau, float& lsum, uint32_t valid) {
   float y[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -92,6 +100,8 @@ __device__ __forceinline__ v4i pcode16(const float (&f)[16], const CodeCtx& cx, 
     y[r] = __builtin_amdgcn_exp2f(t);
     lsum += y[r];
   }
+  const float ymax = __builtin_amdgcn_exp2f(fmaf(fmax, cx.cq, cx.m15n));
+  if (!wave_any(ymax >= 0.5f - cx.delta)) return v4i{0, 0, 0, 0};
   float g = 1.0f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) g = fminf(g, fabsf(__builtin_amdgcn_fractf(y[r]) - 0.5f));
@@ -104,18 +114,71 @@ __device__ __forceinline__ v4i pcode16(const float (&f)[16], const CodeCtx& cx, 
     pk[i] = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * i + 3], 3, v);
   }
   if (wave_any(g < cx.delta)) {
+    // rare: some score of the group sits within delta of a rounding boundary;
+    // recompute the whole group exactly
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const bool near = fabsf(__builtin_amdgcn_fractf(y[r]) - 0.5f) < cx.delta;
-      if (wave_any(near)) {
+    for (int i = 0; i < 4; ++i) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * i + j;
         int code = exact_code(f[r], cx, tau);
         if (TAIL && !((valid >> r) & 1u)) code = 0;
-        const int sh = 8 * (r & 3);
-        pk[r >> 2] = (pk[r >> 2] & ~(0xFFu << sh)) | ((uint32_t)code << sh);
+        v |= (uint32_t)code << (8 * j);
       }
+      pk[i] = v;
     }
   }
   return v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+}
+
+// The same P code for the fp8 kernel: scores arrive as exact float I, the
+// rounding is v_rndne_f32 and the codes leave as E4M3 bytes (exact for the
+// integers 0..15).  rr receives the codes as floats (0 for an all-zero group).
+// Returns the four packed dwords (byte r = E4M3 of the code of score r).
+template <bool TAIL>
+__device__ __forceinline__ v4i pcode16_f8(const float (&f)[16], float fmax, const CodeCtx& cx,
+                                          const float* tau, float& lsum, uint32_t valid,
+                                          float (&rr)[16]) {
+  float y[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float t = fmaf(f[r], cx.cq, cx.m15n);
+    if (TAIL) t = ((valid >> r) & 1u) ? t : -INFINITY;
+    y[r] = __builtin_amdgcn_exp2f(t);
+    lsum += y[r];
+  }
+  const float ymax = __builtin_amdgcn_exp2f(fmaf(fmax, cx.cq, cx.m15n));
+  if (!wave_any(ymax >= 0.5f - cx.delta)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rr[r] = 0.0f;
+    return v4i{0, 0, 0, 0};
+  }
+  float g = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    rr[r] = __builtin_rintf(y[r]);
+    g = fmaxf(g, fabsf(y[r] - rr[r]));
+  }
+  if (wave_any(g > 0.5f - cx.delta)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int code = exact_code(f[r], cx, tau);
+      rr[r] = (TAIL && !((valid >> r) & 1u)) ? 0.0f : (float)code;
+    }
+  }
+  uint32_t pk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(rr[4 * i], rr[4 * i + 1], 0u, false);
+    pk[i] = __builtin_amdgcn_cvt_pk_fp8_f32(rr[4 * i + 2], rr[4 * i + 3], lo, true);
+  }
+  return v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+}
+
+__device__ __forceinline__ v16f mfma_f8(const v8i& a, const v8i& b, const v16f& c) {
+  // format 0/0: both operands FP8 E4M3; zero scales select the unscaled MFMA
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 template <int D, bool DBG>
@@ -164,11 +227,14 @@ struct Int4Kernel {
       }
     }
 
-    int mx = INT32_MIN;
+    int smx[4];
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub)
+    for (int sub = 0; sub < 4; ++sub) {
+      smx[sub] = S[sub][0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = max(mx, S[sub][r]);
+      for (int r = 1; r < 16; ++r) smx[sub] = max(smx[sub], S[sub][r]);
+    }
+    int mx = max(max(smx[0], smx[1]), max(smx[2], smx[3]));
     mx = max(mx, __shfl_xor(mx, 32, 64));
 
     const float ct = qs * a.k_scale[sidx];
@@ -192,7 +258,7 @@ struct Int4Kernel {
       float f[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) f[r] = (float)S[sub][r];
-      P[sub] = pcode16<TAIL>(f, cx, a.tau, ls, valid[sub]);
+      P[sub] = pcode16<TAIL>(f, (float)smx[sub], cx, a.tau, ls, valid[sub]);
     }
     l = fmaf(l, alpha, ls);
 
@@ -295,24 +361,31 @@ struct Int4Kernel {
     for (int db = 0; db < DB; ++db) O[db] = v16f{0.0f};
 
     const int NT = NB;
-    const bool ragged = (a.N % kBlock) != 0;
     gload(0);
     lstore(0);
     __syncthreads();
+    // every tile but the last is full; the last one is peeled off so that the
+    // loop body has a single path (no accumulator copies between variants)
 #pragma unroll 1
-    for (int t = 0; t < NT; ++t) {
+    for (int t = 0; t < NT - 1; ++t) {
       const int buf = t & 1;
       v4i P[4];
-      if (ragged && t == NT - 1)
+      scores<false>(a, dbg, bh, t, sk[buf], qf, qs, m, l, O, P);
+      // the next tile's global loads overlap the P.V products; issuing them
+      // here keeps their registers off the score phase's peak
+      gload(t + 1);
+      pv(a, dbg, bh, t, sv[buf], P, O);
+      lstore(buf ^ 1);
+      __syncthreads();
+    }
+    {
+      const int t = NT - 1, buf = t & 1;
+      v4i P[4];
+      if ((a.N % kBlock) != 0)
         scores<true>(a, dbg, bh, t, sk[buf], qf, qs, m, l, O, P);
       else
         scores<false>(a, dbg, bh, t, sk[buf], qf, qs, m, l, O, P);
-      // the next tile's global loads overlap the P.V products; issuing them
-      // here keeps their registers off the score phase's peak
-      if (t + 1 < NT) gload(t + 1);
       pv(a, dbg, bh, t, sv[buf], P, O);
-      if (t + 1 < NT) lstore(buf ^ 1);
-      __syncthreads();
     }
 
     l += __shfl_xor(l, 32, 64);
@@ -361,6 +434,260 @@ hipError_t launch_int4(int D, int BH, const Int4Args& a, const Int4Debug* dbg, h
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------- fp8 kernel
+//
+// Same work-group shape and pipeline, with the codes in E4M3 bytes:
+//   S^T  = K_t Q^T on v_mfma_f32_32x32x64_f8f6f4: the fp32 result is I exactly
+//          (integer products and partial sums below 2^24)
+//   O^T  accumulates V_t^T P^T straight into fp32 on the same MFMA, kept in
+//        units of the current V block scale u: O <- beta O + V^T P^T with
+//        beta = 2^(m-m') u_prev / u.  The final O is O * u / l.
+// No unpacking (the prologue stores operand-ready bytes) and no int->float
+// conversions; per score the VALU work is the fused argument, exp2, the l
+// sum and, for groups with a nonzero code, rndne + the guard + the packing.
+template <int D, bool DBG>
+struct Int4F8Kernel {
+  static constexpr int KS = D / 64;        // k-steps of 64 channels for QK^T
+  static constexpr int DB = D / 32;        // 32-channel blocks of O^T
+  static constexpr int KStride = D + 16;   // K tile row in LDS (bytes)
+  static constexpr int VStride = 128 + 16; // V^T tile row in LDS (bytes)
+  static constexpr int BPT = D / 2;        // bytes staged per thread for K and for V^T
+  static constexpr int TPR = 256 / D;      // threads per V^T row
+
+  __device__ __forceinline__ static v8i ld32(const uint8_t* p) {
+    const uint4 a = *(const uint4*)p, b = *(const uint4*)(p + 16);
+    return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+  }
+
+  template <bool TAIL>
+  __device__ __forceinline__ static void scores(const Int4Args& a, const Int4Debug& dbg, int bh,
+                                                int t, const uint8_t* sk, const v8i (&qf)[KS],
+                                                float qs, float& m, float& l, float& u,
+                                                v16f (&O)[DB], v8i (&P)[2]) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int col = lane & 31, hh = lane >> 5;
+    const size_t sidx = (size_t)bh * a.NB + t;
+
+    v16f S[4];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      S[sub] = v16f{0.0f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        S[sub] = mfma_f8(ld32(sk + (32 * sub + col) * KStride + 64 * ks + 32 * hh), qf[ks], S[sub]);
+    }
+
+    uint32_t valid[4] = {0xffffu, 0xffffu, 0xffffu, 0xffffu};
+    if (TAIL) {
+      const int nv = a.N - t * kBlock;
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        uint32_t vm = 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * sub + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key < nv) vm |= 1u << r;
+          else S[sub][r] = -INFINITY;
+        }
+        valid[sub] = vm;
+      }
+    }
+
+    float smx[4];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      smx[sub] = S[sub][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) smx[sub] = fmaxf(smx[sub], S[sub][r]);
+    }
+    float mx = fmaxf(fmaxf(smx[0], smx[1]), fmaxf(smx[2], smx[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+
+    const float ct = qs * a.k_scale[sidx];
+    const float smax = mx * ct;
+    const float mnew = fmaxf(m, smax);
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    const float sv = a.v_scale[sidx];
+    const float unew = sv > 0.0f ? sv : u;
+    const float beta = alpha * (u / unew);
+    u = unew;
+    if (wave_any(beta != 1.0f)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[db][r] *= beta;
+    }
+    m = mnew;
+    const CodeCtx cx = make_ctx(ct, mnew, a.log2_15, 1.0f);
+
+    float ls = 0.0f;
+    float rr[4][16];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      float f[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) f[r] = S[sub][r];
+      const v4i pk = pcode16_f8<TAIL>(f, smx[sub], cx, a.tau, ls, valid[sub], rr[sub]);
+      // 64-key chunk c = sub/2 holds subtile 2c in bytes 0-15, 2c+1 in 16-31
+#pragma unroll
+      for (int i = 0; i < 4; ++i) P[sub >> 1][4 * (sub & 1) + i] = pk[i];
+    }
+    l = fmaf(l, alpha, ls);
+
+    if (DBG) {
+      const int q = 32 * w + col;
+      const size_t npad = (size_t)a.NB * kBlock;
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const size_t key = (size_t)t * kBlock + 32 * sub + 8 * (r >> 2) + 4 * hh + (r & 3);
+          dbg.s_int[q * npad + key] = (TAIL && !((valid[sub] >> r) & 1u)) ? INT32_MIN : (int32_t)S[sub][r];
+          dbg.p_code[q * npad + key] = (uint8_t)rr[sub][r];
+        }
+    }
+  }
+
+  __device__ __forceinline__ static void pv(const Int4Args& a, const Int4Debug& dbg, int t,
+                                            const uint8_t* sv, const v8i (&P)[2], v16f (&O)[DB]) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int col = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      if (DBG) {
+        v16f pvt = v16f{0.0f};
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          pvt = mfma_f8(ld32(sv + (32 * db + col) * VStride + 64 * c + 32 * hh), P[c], pvt);
+        const int q = 32 * w + col;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int d = 32 * db + 8 * (r >> 2) + 4 * hh + (r & 3);
+          dbg.pv_int[((size_t)t * kBlock + q) * D + d] = (int32_t)pvt[r];
+          O[db][r] += pvt[r];
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          O[db] = mfma_f8(ld32(sv + (32 * db + col) * VStride + 64 * c + 32 * hh), P[c], O[db]);
+      }
+    }
+  }
+
+  __device__ static void run(const Int4Args& a, const Int4Debug& dbg) {
+    __shared__ __align__(16) uint8_t sk[2][kBlock * KStride];
+    __shared__ __align__(16) uint8_t sv[2][D * VStride];
+    const int qb = DBG ? dbg.q_block : blockIdx.x;
+    const int bh = DBG ? dbg.bh : blockIdx.y;
+    if (!DBG && !a.run.test(bh)) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int col = lane & 31, hh = lane >> 5;
+    const int NB = a.NB;
+    const size_t rows0 = (size_t)bh * NB * kBlock;
+
+    v8i qf[KS];
+    {
+      const uint8_t* qrow = a.q4 + (rows0 + (size_t)qb * kBlock + 32 * w + col) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = ld32(qrow + 64 * ks + 32 * hh);
+    }
+    const float qs = a.q_scale_l2[(size_t)bh * NB + qb];
+
+    uint4 kreg[BPT / 16], vreg[BPT / 16];
+    auto gload = [&](int t) {
+      const uint8_t* ks = a.k4 + (rows0 + (size_t)t * kBlock + (tid >> 1)) * D + (tid & 1) * BPT;
+      const uint8_t* vs = a.v4 + (((size_t)bh * NB + t) * D + tid / TPR) * 128 + (tid % TPR) * BPT;
+#pragma unroll
+      for (int i = 0; i < BPT / 16; ++i) {
+        kreg[i] = *(const uint4*)(ks + 16 * i);
+        vreg[i] = *(const uint4*)(vs + 16 * i);
+      }
+    };
+    auto lstore = [&](int buf) {
+      uint8_t* kd = sk[buf] + (tid >> 1) * KStride + (tid & 1) * BPT;
+      uint8_t* vd = sv[buf] + (tid / TPR) * VStride + (tid % TPR) * BPT;
+#pragma unroll
+      for (int i = 0; i < BPT / 16; ++i) {
+        *(uint4*)(kd + 16 * i) = kreg[i];
+        *(uint4*)(vd + 16 * i) = vreg[i];
+      }
+    };
+
+    float m = -INFINITY, l = 0.0f, u = 1.0f;
+    v16f O[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) O[db] = v16f{0.0f};
+
+    const int NT = NB;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+#pragma unroll 1
+    for (int t = 0; t < NT - 1; ++t) {
+      const int buf = t & 1;
+      v8i P[2];
+      scores<false>(a, dbg, bh, t, sk[buf], qf, qs, m, l, u, O, P);
+      gload(t + 1);
+      pv(a, dbg, t, sv[buf], P, O);
+      lstore(buf ^ 1);
+      __syncthreads();
+    }
+    {
+      const int t = NT - 1, buf = t & 1;
+      v8i P[2];
+      if ((a.N % kBlock) != 0)
+        scores<true>(a, dbg, bh, t, sk[buf], qf, qs, m, l, u, O, P);
+      else
+        scores<false>(a, dbg, bh, t, sk[buf], qf, qs, m, l, u, O, P);
+      pv(a, dbg, t, sv[buf], P, O);
+    }
+
+    l += __shfl_xor(l, 32, 64);
+    const int query = qb * kBlock + 32 * w + col;
+    if (DBG && hh == 0) {
+      dbg.m_final[32 * w + col] = m;
+      dbg.l_final[32 * w + col] = l * (1.0f / 15.0f);
+    }
+    if (query < a.N) {
+      const float il = u / l;
+      uint16_t* orow = a.o + ((size_t)bh * a.N + query) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * db + 8 * g + 4 * hh;
+          uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[db][4 * g] * il)) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[db][4 * g + 1] * il)) << 16);
+          uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[db][4 * g + 2] * il)) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[db][4 * g + 3] * il)) << 16);
+          *(uint2*)(orow + d0) = uint2{w0, w1};
+        }
+    }
+  }
+};
+
+template <int D, bool DBG>
+__global__ __launch_bounds__(kThreads, 2) void k_int4_attn_f8(Int4Args a, Int4Debug dbg) {
+  Int4F8Kernel<D, DBG>::run(a, dbg);
+}
+
+hipError_t launch_int4_f8(int D, int BH, const Int4Args& a, const Int4Debug* dbg, hipStream_t st) {
+  Int4Debug none{};
+  if (dbg == nullptr) {
+    dim3 grid(a.NB, BH);
+    if (D == 128)
+      hipLaunchKernelGGL((k_int4_attn_f8<128, false>), grid, dim3(kThreads), 0, st, a, none);
+    else
+      hipLaunchKernelGGL((k_int4_attn_f8<64, false>), grid, dim3(kThreads), 0, st, a, none);
+  } else {
+    if (D == 128)
+      hipLaunchKernelGGL((k_int4_attn_f8<128, true>), dim3(1), dim3(kThreads), 0, st, a, *dbg);
+    else
+      hipLaunchKernelGGL((k_int4_attn_f8<64, true>), dim3(1), dim3(kThreads), 0, st, a, *dbg);
+  }
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- self-tests
 
 struct SweepArgs {
@@ -370,13 +697,44 @@ struct SweepArgs {
   uint32_t *trans, *n_trans;
 };
 
+// The code path of the packed (i8) or the fp8 kernel over 16 scores given as
+// exact I (float), as u8 codes in byte lanes.
+template <bool F8>
+__device__ __forceinline__ v4i codes_of(const float (&I)[16], float c, float m, const SweepArgs& a,
+                                        const float* tau) {
+  float f[16], fm = -INFINITY, ls = 0.0f;
+  const float sc = F8 ? 1.0f : 256.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    f[r] = I[r] * sc;
+    fm = fmaxf(fm, f[r]);
+  }
+  if (F8) {
+    const CodeCtx cx = make_ctx(c, m, a.log2_15, 1.0f);
+    float rr[16];
+    pcode16_f8<false>(f, fm, cx, tau, ls, 0xffffu, rr);
+    uint32_t pk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t v = __builtin_amdgcn_cvt_pk_u8_f32(rr[4 * i], 0, 0u);
+      v = __builtin_amdgcn_cvt_pk_u8_f32(rr[4 * i + 1], 1, v);
+      v = __builtin_amdgcn_cvt_pk_u8_f32(rr[4 * i + 2], 2, v);
+      pk[i] = __builtin_amdgcn_cvt_pk_u8_f32(rr[4 * i + 3], 3, v);
+    }
+    return v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+  } else {
+    const CodeCtx cx = make_ctx(c, m, a.log2_15);
+    return pcode16<false>(f, fm, cx, tau, ls, 0xffffu);
+  }
+}
+
 // Each lane evaluates 16 consecutive magnitudes (x = -magnitude, c = 1, m = 0)
 // and the 16 magnitudes one below, then reports every change of code.
+template <bool F8>
 __global__ __launch_bounds__(256) void k_pcode_sweep(SweepArgs a) {
   const uint32_t idx = blockIdx.x * 256u + threadIdx.x;
   const uint32_t b0 = a.mag_lo + 16u * idx;
-  const CodeCtx cx = make_ctx(1.0f, 0.0f, a.log2_15);
-  float f[16], fp[16];
+  float I[16], Ip[16];
   uint32_t live = 0;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -384,12 +742,11 @@ __global__ __launch_bounds__(256) void k_pcode_sweep(SweepArgs a) {
     const bool in = (16u * idx + r) < a.count;
     live |= (in ? 1u : 0u) << r;
     const uint32_t bp = b == 0 ? 0u : b - 1u;
-    f[r] = -__uint_as_float(in ? b : 0u) * 256.0f;
-    fp[r] = -__uint_as_float(in ? bp : 0u) * 256.0f;
+    I[r] = -__uint_as_float(in ? b : 0u);
+    Ip[r] = -__uint_as_float(in ? bp : 0u);
   }
-  float ls = 0.0f;
-  const v4i c = pcode16<false>(f, cx, a.tau, ls, 0xffffu);
-  const v4i cp = pcode16<false>(fp, cx, a.tau, ls, 0xffffu);
+  const v4i c = codes_of<F8>(I, 1.0f, 0.0f, a, a.tau);
+  const v4i cp = codes_of<F8>(Ip, 1.0f, 0.0f, a, a.tau);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const uint32_t cc = ((uint32_t)c[r >> 2] >> (8 * (r & 3))) & 0xffu;
@@ -405,9 +762,9 @@ __global__ __launch_bounds__(256) void k_pcode_sweep(SweepArgs a) {
   }
 }
 
-hipError_t launch_pcode_sweep(uint32_t mag_lo, uint32_t count, const float tau[15], float log2_15,
-                              uint32_t* transitions, uint32_t max_transitions, uint32_t* n_trans,
-                              hipStream_t st) {
+hipError_t launch_pcode_sweep(bool f8, uint32_t mag_lo, uint32_t count, const float tau[15],
+                              float log2_15, uint32_t* transitions, uint32_t max_transitions,
+                              uint32_t* n_trans, hipStream_t st) {
   SweepArgs a;
   for (int k = 0; k < 15; ++k) a.tau[k] = tau[k];
   a.log2_15 = log2_15;
@@ -418,38 +775,42 @@ hipError_t launch_pcode_sweep(uint32_t mag_lo, uint32_t count, const float tau[1
   a.n_trans = n_trans;
   const uint32_t lanes = (count + 15u) / 16u;
   const uint32_t blocks = (lanes + 255u) / 256u;
-  hipLaunchKernelGGL(k_pcode_sweep, dim3(blocks), dim3(256), 0, st, a);
+  if (f8)
+    hipLaunchKernelGGL(k_pcode_sweep<true>, dim3(blocks), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_pcode_sweep<false>, dim3(blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 struct EvalArgs {
-  float tau[15];
-  float log2_15, c, m;
+  SweepArgs s;
+  float c, m;
   const int32_t* I;
   uint8_t* codes;
 };
 
+template <bool F8>
 __global__ __launch_bounds__(256) void k_pcode_eval(EvalArgs a) {
   const size_t base = ((size_t)blockIdx.x * 256u + threadIdx.x) * 16u;
-  const CodeCtx cx = make_ctx(a.c, a.m, a.log2_15);
-  float f[16];
+  float I[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) f[r] = (float)(a.I[base + r] * 256);
-  float ls = 0.0f;
-  const v4i c = pcode16<false>(f, cx, a.tau, ls, 0xffffu);
-  *(v4i*)(a.codes + base) = c;
+  for (int r = 0; r < 16; ++r) I[r] = (float)a.I[base + r];
+  *(v4i*)(a.codes + base) = codes_of<F8>(I, a.c, a.m, a.s, a.s.tau);
 }
 
-hipError_t launch_pcode_eval(const int32_t* I, uint32_t n, float c, float m, const float tau[15],
-                             float log2_15, uint8_t* codes, hipStream_t st) {
+hipError_t launch_pcode_eval(bool f8, const int32_t* I, uint32_t n, float c, float m,
+                             const float tau[15], float log2_15, uint8_t* codes, hipStream_t st) {
   EvalArgs a;
-  for (int k = 0; k < 15; ++k) a.tau[k] = tau[k];
-  a.log2_15 = log2_15;
+  for (int k = 0; k < 15; ++k) a.s.tau[k] = tau[k];
+  a.s.log2_15 = log2_15;
   a.c = c;
   a.m = m;
   a.I = I;
   a.codes = codes;
-  hipLaunchKernelGGL(k_pcode_eval, dim3(n / 4096u), dim3(256), 0, st, a);
+  if (f8)
+    hipLaunchKernelGGL(k_pcode_eval<true>, dim3(n / 4096u), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_pcode_eval<false>, dim3(n / 4096u), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -54,6 +54,37 @@ RATE_KERNEL(k_exp, a[j] = __builtin_amdgcn_exp2f(a[j]))
 RATE_KERNEL(k_fract, a[j] = __builtin_amdgcn_fractf(a[j] + 0.37f))
 RATE_KERNEL(k_cvt, a[j] = (float)(int)a[j] + 0.5f)
 
+__global__ __launch_bounds__(256) void k_fma64(float* out, int iters) {
+  double a[kChains];
+  for (int j = 0; j < kChains; ++j) a[j] = 1e-3 * (threadIdx.x + j);
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < kChains; ++j) a[j] = __builtin_fma(a[j], 0.999, -1e-4);
+  }
+  double s = 0;
+  for (int j = 0; j < kChains; ++j) s += a[j];
+  if (s == 12345.678) out[threadIdx.x] = (float)s;
+}
+
+// LDS read bandwidth: every lane reads 16 bytes per instruction from a 16 KB
+// tile (distinct rows per lane, 144-byte row stride as in the attention kernels)
+__global__ __launch_bounds__(256) void k_lds(float* out, int iters) {
+  __shared__ __align__(16) uint4 tile[1024];
+  for (int i = threadIdx.x; i < 1024; i += 256) tile[i] = uint4{(unsigned)i, 1u, 2u, 3u};
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  uint4 acc = uint4{0, 0, 0, 0};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int idx = ((lane & 31) * 9 + (lane >> 5) + 2 * j + (i & 1)) & 1023;
+      const uint4 v = tile[idx];
+      acc.x ^= v.x; acc.y += v.y; acc.z ^= v.z; acc.w += v.w;
+    }
+  }
+  if (acc.x == 0x12345u) out[threadIdx.x] = (float)(acc.y + acc.z + acc.w);
+}
+
 __global__ __launch_bounds__(256) void k_cvtpk(float* out, int iters) {
   float a[kChains];
   uint32_t acc = 0;
@@ -205,6 +236,18 @@ int main(int argc, char** argv) {
     const float ms = time_ms(launch_rate, &c, 3);
     const double lane_ops = (double)blocks * 256 * c.iters * v.per_iter;
     printf(", \"%s_G_per_s\": %.1f", v.name, lane_ops / (ms * 1e-3) / 1e9);
+  }
+  {
+    RateCtx c{k_fma64, out, 4000, blocks};
+    const float ms = time_ms(launch_rate, &c, 3);
+    const double lane_ops = (double)blocks * 256 * c.iters * kChains;
+    printf(", \"fma64_G_per_s\": %.1f", lane_ops / (ms * 1e-3) / 1e9);
+  }
+  {
+    RateCtx c{k_lds, out, 4000, blocks};
+    const float ms = time_ms(launch_rate, &c, 3);
+    const double bytes = (double)blocks * 256 * c.iters * 8 * 16;
+    printf(", \"lds_read_b128_TBps\": %.2f", bytes / (ms * 1e-3) / 1e12);
   }
   {
     RateCtx c{k_mfma_i8, out, 2000, blocks};

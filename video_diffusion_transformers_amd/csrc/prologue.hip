@@ -17,25 +17,11 @@
 //          fp32 x fp32 products are exact in fp64), one rounding to fp32
 //   INT4   per block: amax over the 128 tokens x D channels, inv = fl(7/amax),
 //          scale = fl(amax/7), code = clamp(rne(fl(z*inv)), -7, 7)
-// The rotation matrices are read as fp64 through the scalar unit (uniform
-// addresses), so every MAC is one v_fma_f64 with an SGPR operand.
+// The rotation matrices are staged once per work-group in LDS as fp64; every
+// MAC is one v_fma_f64 whose coefficient is a broadcast LDS read.
 #include "rotattn_internal.h"
 
 namespace rotattn {
-
-__global__ void k_rot_to_f64(const float* rt, const float* rh, const float* rw, int dt, int dh,
-                             int dw, double* out) {
-  const int a = blockIdx.x;
-  const float* src = a == 0 ? rt : (a == 1 ? rh : rw);
-  const int d = a == 0 ? dt : (a == 1 ? dh : dw);
-  for (int i = threadIdx.x; i < d * d; i += blockDim.x) out[a * 4096 + i] = (double)src[i];
-}
-
-hipError_t launch_rot_to_f64(const float* rt, const float* rh, const float* rw, int dt, int dh,
-                             int dw, double* out, hipStream_t st) {
-  hipLaunchKernelGGL(k_rot_to_f64, dim3(3), dim3(256), 0, st, rt, rh, rw, dt, dh, dw, out);
-  return hipGetLastError();
-}
 
 constexpr int kThreads = 384;
 constexpr int kCodeStride = 132;   // bytes per row of the int8 code buffers (33 dwords: no bank conflicts)
@@ -44,13 +30,14 @@ __device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_c
 __device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
 // RoPE of this lane's token over one partition of width DA at channel offset
-// off: y[0..DA) in fp32.
+// off: y[0..DA) in fp32.  xrow is the token's fp16 row staged in LDS (one
+// dword per channel pair).
 template <int DA>
-__device__ __forceinline__ void rope_part(const uint16_t* row, bool valid, const float* cos_a,
+__device__ __forceinline__ void rope_part(const uint32_t* xrow, const float* cos_a,
                                           const float* sin_a, int pos, int off, float (&y)[DA]) {
 #pragma unroll
   for (int j = 0; j < DA / 2; ++j) {
-    uint32_t pr = valid ? *(const uint32_t*)(row + off + 2 * j) : 0u;
+    const uint32_t pr = xrow[off / 2 + j];
     const float x0 = h2f((uint16_t)(pr & 0xffffu));
     const float x1 = h2f((uint16_t)(pr >> 16));
     const float c = cos_a[pos * (DA / 2) + j];
@@ -61,18 +48,29 @@ __device__ __forceinline__ void rope_part(const uint16_t* row, bool valid, const
 }
 
 // z = R y over one partition: fp64 accumulation, k ascending, one rounding.
+// R comes from LDS in k-major fp64 ([k][r]); G outputs are accumulated side by
+// side so that G independent v_fma_f64 chains hide the FMA latency, and their
+// G coefficients of one k are one broadcast LDS read.
 template <int DA>
-__device__ __forceinline__ void rotate_part(const float (&y)[DA], const double* __restrict__ R,
+__device__ __forceinline__ void rotate_part(const float (&y)[DA], const double* Rk,
                                             float (&z)[DA]) {
+  constexpr int G = (DA % 4 == 0) ? 4 : 6;
+  static_assert(DA % G == 0, "partition width must split into groups");
   double yd[DA];
 #pragma unroll
   for (int k = 0; k < DA; ++k) yd[k] = (double)y[k];
 #pragma unroll
-  for (int r = 0; r < DA; ++r) {
-    double acc = 0.0;
+  for (int r0 = 0; r0 < DA; r0 += G) {
+    double acc[G];
 #pragma unroll
-    for (int k = 0; k < DA; ++k) acc = __builtin_fma(R[r * DA + k], yd[k], acc);
-    z[r] = (float)acc;
+    for (int g = 0; g < G; ++g) acc[g] = 0.0;
+#pragma unroll
+    for (int k = 0; k < DA; ++k) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) acc[g] = __builtin_fma(Rk[k * DA + r0 + g], yd[k], acc[g]);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) z[r0 + g] = (float)acc[g];
   }
 }
 
@@ -104,14 +102,28 @@ __device__ __forceinline__ int quant(float z, float inv) {
   return (int)fminf(fmaxf(rintf(z * inv), -7.0f), 7.0f);
 }
 
+// FP8 E4M3 bits of an integer code in [-7, 7] (exact: 1 = 0x38, 2 = 0x40,
+// 3 = 0x44, ..., 7 = 0x4E; sign in bit 7).
+__device__ __forceinline__ uint32_t e4m3_of(int c) {
+  const uint64_t lut = 0x4E4C4A4844403800ull;
+  const uint32_t mag = (uint32_t)(c < 0 ? -c : c);
+  return (uint32_t)((lut >> (8 * mag)) & 0xFFu) | (c < 0 ? 0x80u : 0u);
+}
+
+// The byte stored for a code: int8 for the packed layout, E4M3 for FP8.
+template <bool F8>
+__device__ __forceinline__ int8_t code_byte(int c) {
+  return F8 ? (int8_t)e4m3_of(c) : (int8_t)c;
+}
+
 // One tensor (Q or K) of one partition for this lane's token: RoPE, rotation,
 // block scale, codes into the LDS code buffer (row = token, padded stride).
-template <int DA>
-__device__ __forceinline__ void qk_part(const uint16_t* row, bool valid, const float* cos_a,
+template <int DA, bool F8>
+__device__ __forceinline__ void qk_part(const uint32_t* xrow, const float* cos_a,
                                         const float* sin_a, int pos, int off, const double* R,
                                         float* red, int8_t* codes, int nl, float& scale_out) {
   float y[DA], z[DA];
-  rope_part<DA>(row, valid, cos_a, sin_a, pos, off, y);
+  rope_part<DA>(xrow, cos_a, sin_a, pos, off, y);
   rotate_part<DA>(y, R, z);
   float amax = 0.0f;
 #pragma unroll
@@ -119,32 +131,31 @@ __device__ __forceinline__ void qk_part(const uint16_t* row, bool valid, const f
   float inv, scale;
   block_scale(amax, red, inv, scale);
 #pragma unroll
-  for (int r = 0; r < DA; ++r) codes[nl * kCodeStride + off + r] = (int8_t)quant(z[r], inv);
+  for (int r = 0; r < DA; ++r) codes[nl * kCodeStride + off + r] = code_byte<F8>(quant(z[r], inv));
   scale_out = scale;
 }
 
+// Fallback head: RoPE'd fp16 pairs written back over the staged row (the
+// caller stores the tile with coalesced writes).
 template <int DA>
-__device__ __forceinline__ void rope_only_part(const uint16_t* row, bool valid, const float* cos_a,
-                                               const float* sin_a, int pos, int off,
-                                               uint16_t* out_row) {
+__device__ __forceinline__ void rope_only_part(uint32_t* xrow, const float* cos_a,
+                                               const float* sin_a, int pos, int off) {
   float y[DA];
-  rope_part<DA>(row, valid, cos_a, sin_a, pos, off, y);
-  if (!valid) return;
+  rope_part<DA>(xrow, cos_a, sin_a, pos, off, y);
+  __syncthreads();   // every lane has read its inputs before any row is overwritten
 #pragma unroll
-  for (int j = 0; j < DA / 2; ++j) {
-    const uint32_t pr = (uint32_t)f2h(y[2 * j]) | ((uint32_t)f2h(y[2 * j + 1]) << 16);
-    *(uint32_t*)(out_row + off + 2 * j) = pr;
-  }
+  for (int j = 0; j < DA / 2; ++j)
+    xrow[off / 2 + j] = (uint32_t)f2h(y[2 * j]) | ((uint32_t)f2h(y[2 * j + 1]) << 16);
 }
 
-template <int DA>
-__device__ __forceinline__ void v_part(const uint16_t* row, bool valid, int off, float* red,
+template <int DA, bool F8>
+__device__ __forceinline__ void v_part(const uint32_t* xrow, int off, float* red,
                                        int8_t* codesT, int nl, float& scale_out) {
   float x[DA];
   float amax = 0.0f;
 #pragma unroll
   for (int j = 0; j < DA / 2; ++j) {
-    uint32_t pr = valid ? *(const uint32_t*)(row + off + 2 * j) : 0u;
+    const uint32_t pr = xrow[off / 2 + j];
     x[2 * j] = h2f((uint16_t)(pr & 0xffffu));
     x[2 * j + 1] = h2f((uint16_t)(pr >> 16));
     amax = fmaxf(amax, fmaxf(fabsf(x[2 * j]), fabsf(x[2 * j + 1])));
@@ -152,8 +163,37 @@ __device__ __forceinline__ void v_part(const uint16_t* row, bool valid, int off,
   float inv, scale;
   block_scale(amax, red, inv, scale);
 #pragma unroll
-  for (int r = 0; r < DA; ++r) codesT[(off + r) * kCodeStride + nl] = (int8_t)quant(x[r], inv);
+  for (int r = 0; r < DA; ++r) codesT[(off + r) * kCodeStride + nl] = code_byte<F8>(quant(x[r], inv));
   scale_out = scale;
+}
+
+// Coalesced load of a block's fp16 rows [128][D] into LDS rows of D/2 + 1
+// dwords (the odd stride keeps the per-token reads conflict-free); rows past
+// N are zero.
+template <int D>
+__device__ __forceinline__ void load_tile(const uint16_t* src, int n0, int N, uint32_t* xs) {
+  constexpr int kChunks = D / 8;           // 16-byte chunks per row
+  constexpr int kRS = D / 2 + 1;
+  for (int i = threadIdx.x; i < kBlock * kChunks; i += kThreads) {
+    const int r = i / kChunks, c = i % kChunks;
+    uint4 v = uint4{0, 0, 0, 0};
+    if (n0 + r < N) v = *(const uint4*)(src + (size_t)(n0 + r) * D + 8 * c);
+    uint32_t* d = xs + r * kRS + 4 * c;
+    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+  }
+}
+
+// Coalesced store of the staged fp16 rows of the valid tokens.
+template <int D>
+__device__ __forceinline__ void store_tile(uint16_t* dst, int n0, int N, const uint32_t* xs) {
+  constexpr int kChunks = D / 8;
+  constexpr int kRS = D / 2 + 1;
+  for (int i = threadIdx.x; i < kBlock * kChunks; i += kThreads) {
+    const int r = i / kChunks, c = i % kChunks;
+    if (n0 + r >= N) continue;
+    const uint32_t* s_ = xs + r * kRS + 4 * c;
+    *(uint4*)(dst + (size_t)(n0 + r) * D + 8 * c) = uint4{s_[0], s_[1], s_[2], s_[3]};
+  }
 }
 
 // Q/K codes (LDS, [token][channel]) -> packed rows [128][D/2] in global memory.
@@ -168,6 +208,29 @@ __device__ __forceinline__ void store_qk_codes(const int8_t* codes, uint8_t* dst
   }
 }
 
+// FP8 layout: Q/K code bytes (LDS, [token][channel]) -> rows [128][D].
+template <int D>
+__device__ __forceinline__ void store_qk_codes_f8(const int8_t* codes, uint8_t* dst) {
+  constexpr int kDw = D / 4;
+  for (int i = threadIdx.x; i < kBlock * kDw; i += kThreads) {
+    const int n = i / kDw, g = i % kDw;
+    *(uint32_t*)(dst + (size_t)n * D + 4 * g) = *(const uint32_t*)(codes + n * kCodeStride + 4 * g);
+  }
+}
+
+// FP8 layout: V code bytes (LDS, [channel][token]) -> V^T block [D][128], each
+// 64-key half in the P.V operand order (byte 32h + j of a half holds key
+// 32(j/16) + 8((j%16)/4) + 4h + j%4).  Dwords move whole: j%4 is the byte.
+template <int D>
+__device__ __forceinline__ void store_v_codes_f8(const int8_t* codesT, uint8_t* dst) {
+  for (int i = threadIdx.x; i < D * 32; i += kThreads) {
+    const int d = i / 32, q = i % 32;                 // output dword q of row d
+    const int c = q / 16, h = (q / 8) & 1, j = 4 * (q & 7);
+    const int key = 64 * c + 32 * (j / 16) + 8 * ((j % 16) / 4) + 4 * h;
+    *(uint32_t*)(dst + (size_t)d * 128 + 4 * q) = *(const uint32_t*)(codesT + d * kCodeStride + key);
+  }
+}
+
 // V codes (LDS, [channel][token]) -> packed V^T block [D][64] in global memory.
 template <int D>
 __device__ __forceinline__ void store_v_codes(const int8_t* codesT, uint8_t* dst) {
@@ -179,19 +242,30 @@ __device__ __forceinline__ void store_v_codes(const int8_t* codesT, uint8_t* dst
   }
 }
 
-template <int D, int D0, int D1>
-__global__ __launch_bounds__(kThreads) void k_prologue(PrologueArgs a) {
+// 3 waves per SIMD: two 6-wave work-groups per CU, so one group's rotation
+// overlaps the other's memory phases
+template <int D, int D0, int D1, bool F8>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void k_prologue(PrologueArgs a) {
   static_assert(D0 + 2 * D1 == D, "split must be (D0, D1, D1)");
-  __shared__ __align__(16) int8_t codes[kBlock * kCodeStride];   // 128 token rows, or D <= 128 channel rows
+  constexpr int kRS = D / 2 + 1;   // staged fp16 row, in dwords
+  constexpr int kStage = (kBlock * kRS * 4 > kBlock * kCodeStride) ? kBlock * kRS * 4
+                                                                   : kBlock * kCodeStride;
+  // one buffer, two lives: the staged fp16 rows of a tensor, then its INT4 codes
+  // (128 token rows, or D <= 128 channel rows of 132 bytes)
+  __shared__ __align__(16) uint32_t stage[kStage / 4];
   __shared__ float red[16];
+  // rotation matrices in fp64, k-major: partition t at 0, h at D0^2, w at D0^2 + D1^2
+  __shared__ __align__(16) double rot[D0 * D0 + 2 * D1 * D1];
+  int8_t* codes = (int8_t*)stage;
 
   const int blk = blockIdx.x, bh = blockIdx.y;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   // wave-uniform: lets the rotation matrices and tables go through the scalar unit
   const int part = __builtin_amdgcn_readfirstlane(w >> 1);
   const int nl = (w & 1) * 64 + lane;
-  const int n = blk * kBlock + nl;
-  const bool valid = n < a.N;
+  const int n0 = blk * kBlock;
+  const int n = n0 + nl;
   const int HW = a.grid_h * a.grid_w;
   const int pos = part == 0 ? n / HW : (part == 1 ? (n / a.grid_w) % a.grid_h : n % a.grid_w);
   const int off = part == 0 ? 0 : (part == 1 ? D0 : D0 + D1);
@@ -199,32 +273,58 @@ __global__ __launch_bounds__(kThreads) void k_prologue(PrologueArgs a) {
   const float* sin_a = part == 0 ? a.sin_t : (part == 1 ? a.sin_h : a.sin_w);
   const size_t head_tok = (size_t)bh * a.N;
   const bool fallback = a.fallback.test(bh);
+  uint32_t* xrow = stage + nl * kRS;
+  // tables are read for every lane; clamp the position of a padding token
+  const int pos_c = n < a.N ? pos : 0;
 
   if (fallback) {
 #pragma unroll 1
     for (int s = 0; s < 2; ++s) {
-      const uint16_t* row = (s == 0 ? a.q : a.k) + (head_tok + (valid ? n : 0)) * D;
-      uint16_t* out_row = (s == 0 ? a.q_rope : a.k_rope) + (head_tok + (valid ? n : 0)) * D;
+      load_tile<D>((s == 0 ? a.q : a.k) + head_tok * D, n0, a.N, stage);
+      __syncthreads();
       if (part == 0)
-        rope_only_part<D0>(row, valid, cos_a, sin_a, pos, off, out_row);
+        rope_only_part<D0>(xrow, cos_a, sin_a, pos_c, off);
       else
-        rope_only_part<D1>(row, valid, cos_a, sin_a, pos, off, out_row);
+        rope_only_part<D1>(xrow, cos_a, sin_a, pos_c, off);
+      __syncthreads();
+      store_tile<D>((s == 0 ? a.q_rope : a.k_rope) + head_tok * D, n0, a.N, stage);
+      __syncthreads();
     }
     return;
   }
 
+  for (int i = threadIdx.x; i < D0 * D0 + 2 * D1 * D1; i += kThreads) {
+    int p = 0, j = i, w_ = D0;
+    const float* src = a.rot_t;
+    if (i >= D0 * D0) {
+      j = i - D0 * D0;
+      p = 1 + (j >= D1 * D1);
+      j -= (p - 1) * D1 * D1;
+      w_ = D1;
+      src = p == 1 ? a.rot_h : a.rot_w;
+    }
+    const int k = j / w_, r = j % w_;              // stored [k][r] from R[r][k]
+    rot[i] = (double)src[r * w_ + k];
+  }
+
   const size_t pad_row = ((size_t)bh * a.NB + blk) * kBlock;   // first packed row of this block
+  const double* Rk = rot + (part == 0 ? 0 : D0 * D0 + (part - 1) * D1 * D1);
 #pragma unroll 1
   for (int s = 0; s < 2; ++s) {
-    const uint16_t* row = (s == 0 ? a.q : a.k) + (head_tok + (valid ? n : 0)) * D;
-    float scale;
-    if (part == 0)
-      qk_part<D0>(row, valid, cos_a, sin_a, pos, off, a.rot64, red, codes, nl, scale);
-    else
-      qk_part<D1>(row, valid, cos_a, sin_a, pos, off, a.rot64 + part * 4096, red, codes, nl,
-                  scale);
+    load_tile<D>((s == 0 ? a.q : a.k) + head_tok * D, n0, a.N, stage);
     __syncthreads();
-    store_qk_codes<D>(codes, (s == 0 ? a.q4 : a.k4) + pad_row * (D / 2));
+    float scale;
+    // the rows are read before the first barrier of the block-scale reduction,
+    // and the codes written after it, so the two lives of `stage` never overlap
+    if (part == 0)
+      qk_part<D0, F8>(xrow, cos_a, sin_a, pos_c, off, Rk, red, codes, nl, scale);
+    else
+      qk_part<D1, F8>(xrow, cos_a, sin_a, pos_c, off, Rk, red, codes, nl, scale);
+    __syncthreads();
+    if (F8)
+      store_qk_codes_f8<D>(codes, (s == 0 ? a.q4 : a.k4) + pad_row * D);
+    else
+      store_qk_codes<D>(codes, (s == 0 ? a.q4 : a.k4) + pad_row * (D / 2));
     if (threadIdx.x == 0) {
       if (s == 0)
         a.q_scale_l2[(size_t)bh * a.NB + blk] = scale * a.kappa;
@@ -235,26 +335,37 @@ __global__ __launch_bounds__(kThreads) void k_prologue(PrologueArgs a) {
   }
 
   {
-    const uint16_t* row = a.v + (head_tok + (valid ? n : 0)) * D;
+    load_tile<D>(a.v + head_tok * D, n0, a.N, stage);
+    __syncthreads();
     float scale;
     if (part == 0)
-      v_part<D0>(row, valid, off, red, codes, nl, scale);
+      v_part<D0, F8>(xrow, off, red, codes, nl, scale);
     else
-      v_part<D1>(row, valid, off, red, codes, nl, scale);
+      v_part<D1, F8>(xrow, off, red, codes, nl, scale);
     __syncthreads();
-    store_v_codes<D>(codes, a.v4 + ((size_t)bh * a.NB + blk) * D * 64);
+    if (F8)
+      store_v_codes_f8<D>(codes, a.v4 + ((size_t)bh * a.NB + blk) * D * 128);
+    else
+      store_v_codes<D>(codes, a.v4 + ((size_t)bh * a.NB + blk) * D * 64);
     if (threadIdx.x == 0) a.v_scale[(size_t)bh * a.NB + blk] = scale;
   }
 }
 
-hipError_t launch_prologue(int D, int dt, int BH, const PrologueArgs& a, hipStream_t st) {
+hipError_t launch_prologue(int D, int dt, int BH, bool f8, const PrologueArgs& a, hipStream_t st) {
   dim3 grid(a.NB, BH);
-  if (D == 128 && dt == 44)
-    hipLaunchKernelGGL((k_prologue<128, 44, 42>), grid, dim3(kThreads), 0, st, a);
-  else if (D == 64 && dt == 24)
-    hipLaunchKernelGGL((k_prologue<64, 24, 20>), grid, dim3(kThreads), 0, st, a);
-  else
+  if (D == 128 && dt == 44) {
+    if (f8)
+      hipLaunchKernelGGL((k_prologue<128, 44, 42, true>), grid, dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_prologue<128, 44, 42, false>), grid, dim3(kThreads), 0, st, a);
+  } else if (D == 64 && dt == 24) {
+    if (f8)
+      hipLaunchKernelGGL((k_prologue<64, 24, 20, true>), grid, dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_prologue<64, 24, 20, false>), grid, dim3(kThreads), 0, st, a);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -111,36 +111,38 @@ float rotattn_kappa_host(int32_t D) {
   return (float)(1.0L / logl(2.0L) / sqrtl((long double)D));
 }
 
-size_t rotattn_prepared_bytes(const rotattn_shape* s, int with_rope) {
+size_t rotattn_prepared_bytes(const rotattn_shape* s, int with_rope, int layout) {
   if (rotattn_validate(s) != ROTATTN_OK) return 0;
+  if (layout != ROTATTN_LAYOUT_PACKED && layout != ROTATTN_LAYOUT_FP8) return 0;
   const size_t BH = (size_t)s->B * s->H, NB = nblocks(s), D = s->D;
-  const size_t packed = align_up(BH * NB * kBlock * D / 2);
+  const size_t per_code = layout == ROTATTN_LAYOUT_FP8 ? 2 : 1;   // half-bytes per code
+  const size_t packed = align_up(BH * NB * kBlock * D * per_code / 2);
   const size_t scales = align_up(BH * NB * sizeof(float));
-  const size_t rot = align_up(3 * 4096 * sizeof(double));
   const size_t rope = with_rope ? align_up(BH * (size_t)s->N * D * 2) : 0;
-  return 3 * packed + 3 * scales + rot + 2 * rope;
+  return 3 * packed + 3 * scales + 2 * rope;
 }
 
 int rotattn_prepared_carve(const rotattn_shape* s, void* base, size_t bytes, int with_rope,
-                           rotattn_prepared* out) {
+                           int layout, rotattn_prepared* out) {
   const int st = rotattn_validate(s);
   if (st != ROTATTN_OK) return st;
   if (!base || !out) return ROTATTN_E_NULL;
+  if (layout != ROTATTN_LAYOUT_PACKED && layout != ROTATTN_LAYOUT_FP8) return ROTATTN_E_ARG;
   if (((uintptr_t)base & (kAlign - 1)) != 0) return ROTATTN_E_ALIGN;
-  if (bytes < rotattn_prepared_bytes(s, with_rope)) return ROTATTN_E_WORKSPACE;
+  if (bytes < rotattn_prepared_bytes(s, with_rope, layout)) return ROTATTN_E_WORKSPACE;
   const size_t BH = (size_t)s->B * s->H, NB = nblocks(s), D = s->D;
-  const size_t packed = align_up(BH * NB * kBlock * D / 2);
+  const size_t per_code = layout == ROTATTN_LAYOUT_FP8 ? 2 : 1;
+  const size_t packed = align_up(BH * NB * kBlock * D * per_code / 2);
   const size_t scales = align_up(BH * NB * sizeof(float));
-  const size_t rot = align_up(3 * 4096 * sizeof(double));
   const size_t rope = align_up(BH * (size_t)s->N * D * 2);
   uint8_t* p = (uint8_t*)base;
+  out->layout = layout;
   out->q4 = p; p += packed;
   out->k4 = p; p += packed;
   out->v4 = p; p += packed;
   out->q_scale_l2 = (float*)p; p += scales;
   out->k_scale = (float*)p; p += scales;
   out->v_scale = (float*)p; p += scales;
-  out->rot64 = (double*)p; p += rot;
   if (with_rope) {
     out->q_rope = (uint16_t*)p; p += rope;
     out->k_rope = (uint16_t*)p; p += rope;
@@ -162,11 +164,11 @@ int rotattn_prepare_qkv(const rotattn_shape* s, const uint16_t* q, const uint16_
       !rr->rot_t || !rr->rot_h || !rr->rot_w)
     return ROTATTN_E_NULL;
   const int BH = s->B * s->H;
+  if (out->layout != ROTATTN_LAYOUT_PACKED && out->layout != ROTATTN_LAYOUT_FP8) return ROTATTN_E_ARG;
   int n_fb = 0;
   const HeadBits fb = make_bits(fallback_mask_host, BH, true, false, &n_fb);
   if (n_fb < BH) {
-    if (!out->q4 || !out->k4 || !out->v4 || !out->q_scale_l2 || !out->k_scale || !out->v_scale ||
-        !out->rot64)
+    if (!out->q4 || !out->k4 || !out->v4 || !out->q_scale_l2 || !out->k_scale || !out->v_scale)
       return ROTATTN_E_NULL;
     if (!aligned16(out->q4) || !aligned16(out->k4) || !aligned16(out->v4)) return ROTATTN_E_ALIGN;
   }
@@ -176,15 +178,12 @@ int rotattn_prepare_qkv(const rotattn_shape* s, const uint16_t* q, const uint16_
   }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return ROTATTN_E_ALIGN;
 
-  if (n_fb < BH && launch_rot_to_f64(rr->rot_t, rr->rot_h, rr->rot_w, s->d_t, s->d_h, s->d_w,
-                                     out->rot64, stream) != hipSuccess)
-    return ROTATTN_E_HIP;
   PrologueArgs a;
   a.q = q; a.k = k; a.v = v;
   a.cos_t = rr->cos_t; a.sin_t = rr->sin_t;
   a.cos_h = rr->cos_h; a.sin_h = rr->sin_h;
   a.cos_w = rr->cos_w; a.sin_w = rr->sin_w;
-  a.rot64 = out->rot64;
+  a.rot_t = rr->rot_t; a.rot_h = rr->rot_h; a.rot_w = rr->rot_w;
   a.q4 = out->q4; a.k4 = out->k4; a.v4 = out->v4;
   a.q_scale_l2 = out->q_scale_l2; a.k_scale = out->k_scale; a.v_scale = out->v_scale;
   a.q_rope = out->q_rope; a.k_rope = out->k_rope;
@@ -194,7 +193,9 @@ int rotattn_prepare_qkv(const rotattn_shape* s, const uint16_t* q, const uint16_
   a.grid_w = s->grid_w;
   a.kappa = rotattn_kappa_host(s->D);
   a.fallback = fb;
-  return launch_prologue(s->D, s->d_t, BH, a, stream) == hipSuccess ? ROTATTN_OK : ROTATTN_E_HIP;
+  return launch_prologue(s->D, s->d_t, BH, out->layout == ROTATTN_LAYOUT_FP8, a, stream) == hipSuccess
+             ? ROTATTN_OK
+             : ROTATTN_E_HIP;
 }
 
 int rotattn_int4_fwd(const rotattn_shape* s, const rotattn_prepared* p,
@@ -207,6 +208,8 @@ int rotattn_int4_fwd(const rotattn_shape* s, const rotattn_prepared* p,
     return ROTATTN_E_NULL;
   if (!aligned16(p->q4) || !aligned16(p->k4) || !aligned16(p->v4) || !aligned16(o))
     return ROTATTN_E_ALIGN;
+  if (p->layout != ROTATTN_LAYOUT_PACKED && p->layout != ROTATTN_LAYOUT_FP8) return ROTATTN_E_ARG;
+  const bool f8 = p->layout == ROTATTN_LAYOUT_FP8;
   const int BH = s->B * s->H;
   Int4Debug d{};
   if (dbg) {
@@ -233,8 +236,9 @@ int rotattn_int4_fwd(const rotattn_shape* s, const rotattn_prepared* p,
   a.NB = nblocks(s);
   a.log2_15 = log2_15_f();
   rotattn_pcode_thresholds_host(a.tau);
-  if (n_run > 0 && launch_int4(s->D, BH, a, nullptr, stream) != hipSuccess) return ROTATTN_E_HIP;
-  if (dbg && launch_int4(s->D, BH, a, &d, stream) != hipSuccess) return ROTATTN_E_HIP;
+  auto launch = f8 ? launch_int4_f8 : launch_int4;
+  if (n_run > 0 && launch(s->D, BH, a, nullptr, stream) != hipSuccess) return ROTATTN_E_HIP;
+  if (dbg && launch(s->D, BH, a, &d, stream) != hipSuccess) return ROTATTN_E_HIP;
   return ROTATTN_OK;
 }
 
@@ -258,7 +262,7 @@ int rotattn_fp16_fwd(const rotattn_shape* s, const uint16_t* q_rope, const uint1
 }
 
 size_t rotattn_workspace_bytes(const rotattn_shape* s) {
-  return rotattn_prepared_bytes(s, 1);
+  return rotattn_prepared_bytes(s, 1, ROTATTN_LAYOUT_FP8);
 }
 
 int rotattn_mixed_fwd(const rotattn_shape* s, const uint16_t* q, const uint16_t* k,
@@ -269,7 +273,7 @@ int rotattn_mixed_fwd(const rotattn_shape* s, const uint16_t* q, const uint16_t*
   if (st != ROTATTN_OK) return st;
   if (!q || !k || !v || !rr || !workspace || !o) return ROTATTN_E_NULL;
   rotattn_prepared p;
-  const int cs = rotattn_prepared_carve(s, workspace, workspace_bytes, 1, &p);
+  const int cs = rotattn_prepared_carve(s, workspace, workspace_bytes, 1, ROTATTN_LAYOUT_FP8, &p);
   if (cs != ROTATTN_OK) return cs;
   int r = rotattn_prepare_qkv(s, q, k, v, rr, fallback_mask_host, &p, stream);
   if (r != ROTATTN_OK) return r;
@@ -283,26 +287,29 @@ int rotattn_mixed_fwd(const rotattn_shape* s, const uint16_t* q, const uint16_t*
   return r;
 }
 
-int rotattn_pcode_sweep(uint32_t mag_lo, uint32_t count, uint32_t* transitions,
+int rotattn_pcode_sweep(int layout, uint32_t mag_lo, uint32_t count, uint32_t* transitions,
                         uint32_t max_transitions, uint32_t* n_transitions, hipStream_t stream) {
   if (!transitions || !n_transitions) return ROTATTN_E_NULL;
+  if (layout != ROTATTN_LAYOUT_PACKED && layout != ROTATTN_LAYOUT_FP8) return ROTATTN_E_ARG;
   if (count == 0 || (uint64_t)mag_lo + count > 0x7B800000ull) return ROTATTN_E_ARG;
   float tau[15];
   rotattn_pcode_thresholds_host(tau);
-  return launch_pcode_sweep(mag_lo, count, tau, log2_15_f(), transitions, max_transitions,
-                            n_transitions, stream) == hipSuccess
+  return launch_pcode_sweep(layout == ROTATTN_LAYOUT_FP8, mag_lo, count, tau, log2_15_f(),
+                            transitions, max_transitions, n_transitions, stream) == hipSuccess
              ? ROTATTN_OK
              : ROTATTN_E_HIP;
 }
 
-int rotattn_pcode_eval(const int32_t* I, uint32_t n, float c, float m, uint8_t* codes,
+int rotattn_pcode_eval(int layout, const int32_t* I, uint32_t n, float c, float m, uint8_t* codes,
                        hipStream_t stream) {
   if (!I || !codes) return ROTATTN_E_NULL;
+  if (layout != ROTATTN_LAYOUT_PACKED && layout != ROTATTN_LAYOUT_FP8) return ROTATTN_E_ARG;
   if (n == 0 || (n % 4096u) != 0) return ROTATTN_E_ARG;
   if (!(c >= 0.0f) || !isfinite(m)) return ROTATTN_E_ARG;
   float tau[15];
   rotattn_pcode_thresholds_host(tau);
-  return launch_pcode_eval(I, n, c, m, tau, log2_15_f(), codes, stream) == hipSuccess
+  return launch_pcode_eval(layout == ROTATTN_LAYOUT_FP8, I, n, c, m, tau, log2_15_f(), codes,
+                           stream) == hipSuccess
              ? ROTATTN_OK
              : ROTATTN_E_HIP;
 }

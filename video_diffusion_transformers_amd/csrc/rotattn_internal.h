@@ -19,6 +19,7 @@ struct HeadBits {
 };
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -39,7 +40,7 @@ __device__ __forceinline__ uint32_t pack_nibbles(uint32_t lo4, uint32_t hi4) {
 struct PrologueArgs {
   const uint16_t *q, *k, *v;
   const float *cos_t, *sin_t, *cos_h, *sin_h, *cos_w, *sin_w;
-  const double* rot64;          // [3][64*64], partition a at a*4096, [d_a][d_a] row-major
+  const float *rot_t, *rot_h, *rot_w;   // [d_a][d_a] row-major, row = output channel
   uint8_t *q4, *k4, *v4;
   float *q_scale_l2, *k_scale, *v_scale;
   uint16_t *q_rope, *k_rope;
@@ -75,15 +76,14 @@ struct Fp16Args {
 };
 
 // Launchers (each defined next to its kernel).  Return a hipError_t.
-hipError_t launch_rot_to_f64(const float* rt, const float* rh, const float* rw, int dt, int dh,
-                             int dw, double* out, hipStream_t st);
-hipError_t launch_prologue(int D, int dt, int BH, const PrologueArgs& a, hipStream_t st);
+hipError_t launch_prologue(int D, int dt, int BH, bool f8, const PrologueArgs& a, hipStream_t st);
 hipError_t launch_int4(int D, int BH, const Int4Args& a, const Int4Debug* dbg, hipStream_t st);
+hipError_t launch_int4_f8(int D, int BH, const Int4Args& a, const Int4Debug* dbg, hipStream_t st);
 hipError_t launch_fp16(int D, int BH, const Fp16Args& a, hipStream_t st);
-hipError_t launch_pcode_sweep(uint32_t mag_lo, uint32_t count, const float tau[15], float log2_15,
-                              uint32_t* transitions, uint32_t max_transitions, uint32_t* n_trans,
-                              hipStream_t st);
-hipError_t launch_pcode_eval(const int32_t* I, uint32_t n, float c, float m, const float tau[15],
-                             float log2_15, uint8_t* codes, hipStream_t st);
+hipError_t launch_pcode_sweep(bool f8, uint32_t mag_lo, uint32_t count, const float tau[15],
+                              float log2_15, uint32_t* transitions, uint32_t max_transitions,
+                              uint32_t* n_trans, hipStream_t st);
+hipError_t launch_pcode_eval(bool f8, const int32_t* I, uint32_t n, float c, float m,
+                             const float tau[15], float log2_15, uint8_t* codes, hipStream_t st);
 
 }  // namespace rotattn

@@ -19,6 +19,9 @@ LIB_PATH = os.path.join(_HERE, "librotattn.so")
 
 BLOCK = 128
 MAX_HEADS = 4096
+LAYOUT_PACKED = 0      # two INT4 codes per byte, i8 MFMA
+LAYOUT_FP8 = 1         # one INT4 code per byte as FP8 E4M3, f8f6f4 MFMA
+LAYOUTS = {"packed": LAYOUT_PACKED, "fp8": LAYOUT_FP8}
 
 STATUS = {0: "ok", -1: "null pointer argument", -2: "inconsistent shape",
           -3: "unsupported head dimension, RoPE split or head count", -4: "workspace too small",
@@ -43,8 +46,9 @@ class RopeRot(C.Structure):
 
 
 class Prepared(C.Structure):
-    _fields_ = [(n, C.c_void_p) for n in ("q4", "k4", "v4", "q_scale_l2", "k_scale", "v_scale",
-                                          "q_rope", "k_rope", "rot64")]
+    _fields_ = [("layout", C.c_int32)] + [
+        (n, C.c_void_p) for n in ("q4", "k4", "v4", "q_scale_l2", "k_scale", "v_scale", "q_rope",
+                                  "k_rope")]
 
 
 class Debug(C.Structure):
@@ -76,16 +80,17 @@ def lib() -> C.CDLL:
             "rotattn_rope_tables_host": (C.c_int, [S, C.c_double] + [P] * 6),
             "rotattn_pcode_thresholds_host": (C.c_int, [P]),
             "rotattn_kappa_host": (C.c_float, [C.c_int32]),
-            "rotattn_prepared_bytes": (C.c_size_t, [S, C.c_int]),
-            "rotattn_prepared_carve": (C.c_int, [S, P, C.c_size_t, C.c_int, C.POINTER(Prepared)]),
+            "rotattn_prepared_bytes": (C.c_size_t, [S, C.c_int, C.c_int]),
+            "rotattn_prepared_carve": (C.c_int, [S, P, C.c_size_t, C.c_int, C.c_int,
+                                                 C.POINTER(Prepared)]),
             "rotattn_prepare_qkv": (C.c_int, [S, P, P, P, C.POINTER(RopeRot), P,
                                               C.POINTER(Prepared), P]),
             "rotattn_int4_fwd": (C.c_int, [S, C.POINTER(Prepared), P, P, C.POINTER(Debug), P]),
             "rotattn_fp16_fwd": (C.c_int, [S, P, P, P, P, P, P]),
             "rotattn_workspace_bytes": (C.c_size_t, [S]),
             "rotattn_mixed_fwd": (C.c_int, [S, P, P, P, C.POINTER(RopeRot), P, P, C.c_size_t, P, P]),
-            "rotattn_pcode_sweep": (C.c_int, [C.c_uint32, C.c_uint32, P, C.c_uint32, P, P]),
-            "rotattn_pcode_eval": (C.c_int, [P, C.c_uint32, C.c_float, C.c_float, P, P]),
+            "rotattn_pcode_sweep": (C.c_int, [C.c_int, C.c_uint32, C.c_uint32, P, C.c_uint32, P, P]),
+            "rotattn_pcode_eval": (C.c_int, [C.c_int, P, C.c_uint32, C.c_float, C.c_float, P, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -180,17 +185,19 @@ class RopeRotDevice:
 class PreparedDevice:
     """Device buffers of a rotattn_prepared, carved from one allocation."""
 
-    def __init__(self, shape: Shape, with_rope: bool = True, device="cuda"):
+    def __init__(self, shape: Shape, with_rope: bool = True, layout: int = LAYOUT_FP8,
+                 device="cuda"):
         torch = _torch()
         self.shape = shape
-        nbytes = lib().rotattn_prepared_bytes(C.byref(shape), int(with_rope))
+        self.layout = layout
+        nbytes = lib().rotattn_prepared_bytes(C.byref(shape), int(with_rope), layout)
         if nbytes == 0:
-            check(validate(shape), "prepared_bytes")
+            check(validate(shape) or -7, "prepared_bytes")
         self.buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
         base = (self.buf.data_ptr() + 255) // 256 * 256
         self.struct = Prepared()
         check(lib().rotattn_prepared_carve(C.byref(shape), C.c_void_p(base), nbytes, int(with_rope),
-                                           C.byref(self.struct)), "prepared_carve")
+                                           layout, C.byref(self.struct)), "prepared_carve")
         self.base = base
 
     def view(self, field: str, dtype, count: int):
@@ -234,19 +241,20 @@ def mixed_fwd(shape: Shape, q, k, v, rr: RopeRotDevice, mask, workspace, o, stre
                                   _ptr(o), _stream(stream)), "mixed_fwd")
 
 
-def pcode_sweep(mag_lo: int, count: int, max_transitions: int = 4096, stream=None):
+def pcode_sweep(mag_lo: int, count: int, max_transitions: int = 4096, layout: int = LAYOUT_FP8,
+                stream=None):
     """Transitions (magnitude bits, code before, code after) of the device P code."""
     torch = _torch()
     trans = torch.zeros(3 * max_transitions, dtype=torch.int32, device="cuda")
     n = torch.zeros(1, dtype=torch.int32, device="cuda")
-    check(lib().rotattn_pcode_sweep(mag_lo, count, _ptr(trans), max_transitions, _ptr(n),
+    check(lib().rotattn_pcode_sweep(layout, mag_lo, count, _ptr(trans), max_transitions, _ptr(n),
                                     _stream(stream)), "pcode_sweep")
     return trans, n
 
 
-def pcode_eval(I, c: float, m: float, stream=None):
+def pcode_eval(I, c: float, m: float, layout: int = LAYOUT_FP8, stream=None):
     torch = _torch()
     codes = torch.empty(I.numel(), dtype=torch.uint8, device=I.device)
-    check(lib().rotattn_pcode_eval(_ptr(I), I.numel(), C.c_float(c), C.c_float(m), _ptr(codes),
-                                   _stream(stream)), "pcode_eval")
+    check(lib().rotattn_pcode_eval(layout, _ptr(I), I.numel(), C.c_float(c), C.c_float(m),
+                                   _ptr(codes), _stream(stream)), "pcode_eval")
     return codes
