@@ -114,6 +114,8 @@ typedef enum rotattn_layout {
  *          codes, each 64-key half in the operand order of the P.V product:
  *          byte 32h+j (h in {0,1}, j < 32) is key 8(j%16/4) + 4h + j%4, plus
  *          32 when j >= 16.
+ *  rot64:  library scratch, 3*64*64 doubles: the rotation in fp64, refilled
+ *          by every rotattn_prepare_qkv call.
  *  q_scale_l2, k_scale, v_scale: [B*H][NB] fp32 block scales (amax/7).
  *          q_scale_l2 = fl(q_scale * kappa), kappa = fl32(log2(e)/sqrt(D)), so
  *          that 2^(I * q_scale_l2 * k_scale) = exp(QK^T / sqrt(D)).
@@ -126,6 +128,7 @@ typedef struct rotattn_prepared {
   uint8_t *q4, *k4, *v4;
   float *q_scale_l2, *k_scale, *v_scale;
   uint16_t *q_rope, *k_rope;
+  double *rot64;
 } rotattn_prepared;
 
 /*

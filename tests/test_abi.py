@@ -88,7 +88,7 @@ def test_prepared_layout_sizes(layout, code_bytes):
     assert R.lib().rotattn_prepared_carve(C.byref(s), C.c_void_p(1 << 20), n1, 1, layout,
                                           C.byref(p)) == 0
     assert p.layout == layout
-    addrs = [p.q4, p.k4, p.v4, p.q_scale_l2, p.k_scale, p.v_scale, p.q_rope, p.k_rope]
+    addrs = [p.q4, p.k4, p.v4, p.q_scale_l2, p.k_scale, p.v_scale, p.rot64, p.q_rope, p.k_rope]
     assert all(a % 256 == 0 for a in addrs) and addrs == sorted(addrs)
     assert p.k4 - p.q4 >= codes and max(addrs) < (1 << 20) + n1
 

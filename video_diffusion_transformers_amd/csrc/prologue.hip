@@ -17,8 +17,8 @@
 //          fp32 x fp32 products are exact in fp64), one rounding to fp32
 //   INT4   per block: amax over the 128 tokens x D channels, inv = fl(7/amax),
 //          scale = fl(amax/7), code = clamp(rne(fl(z*inv)), -7, 7)
-// The rotation matrices are staged once per work-group in LDS as fp64; every
-// MAC is one v_fma_f64 whose coefficient is a broadcast LDS read.
+// The rotation matrices are converted once to fp64 (library scratch) and read
+// through the scalar unit: every MAC is one v_fma_f64 with an SGPR operand.
 #include "rotattn_internal.h"
 
 namespace rotattn {
@@ -47,13 +47,40 @@ __device__ __forceinline__ void rope_part(const uint32_t* xrow, const float* cos
   }
 }
 
+// The rotation in fp64, k-major ([k][r] per partition), read through the
+// constant address space: uniform addresses become s_load, and every MAC is one
+// v_fma_f64 with an SGPR coefficient (no LDS traffic, no vector loads).
+typedef const __attribute__((address_space(4))) double* rot_ptr;
+
+__global__ void k_rot_to_f64(const float* rt, const float* rh, const float* rw, int dt, int dh,
+                             double* out) {
+  const int total = dt * dt + 2 * dh * dh;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+    int j = i, w_ = dt;
+    const float* src = rt;
+    if (i >= dt * dt) {
+      j = i - dt * dt;
+      const int p = j >= dh * dh;
+      j -= p * dh * dh;
+      w_ = dh;
+      src = p ? rw : rh;
+    }
+    const int k = j / w_, r = j % w_;              // stored [k][r] from R[r][k]
+    out[i] = (double)src[r * w_ + k];
+  }
+}
+
+hipError_t launch_rot_to_f64(const float* rt, const float* rh, const float* rw, int dt, int dh,
+                             double* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_rot_to_f64, dim3(16), dim3(256), 0, st, rt, rh, rw, dt, dh, out);
+  return hipGetLastError();
+}
+
 // z = R y over one partition: fp64 accumulation, k ascending, one rounding.
-// R comes from LDS in k-major fp64 ([k][r]); G outputs are accumulated side by
-// side so that G independent v_fma_f64 chains hide the FMA latency, and their
-// G coefficients of one k are one broadcast LDS read.
+// G outputs are accumulated side by side so that G independent v_fma_f64
+// chains hide the FMA latency.
 template <int DA>
-__device__ __forceinline__ void rotate_part(const float (&y)[DA], const double* Rk,
-                                            float (&z)[DA]) {
+__device__ __forceinline__ void rotate_part(const float (&y)[DA], rot_ptr Rk, float (&z)[DA]) {
   constexpr int G = (DA % 4 == 0) ? 4 : 6;
   static_assert(DA % G == 0, "partition width must split into groups");
   double yd[DA];
@@ -120,7 +147,7 @@ __device__ __forceinline__ int8_t code_byte(int c) {
 // block scale, codes into the LDS code buffer (row = token, padded stride).
 template <int DA, bool F8>
 __device__ __forceinline__ void qk_part(const uint32_t* xrow, const float* cos_a,
-                                        const float* sin_a, int pos, int off, const double* R,
+                                        const float* sin_a, int pos, int off, rot_ptr R,
                                         float* red, int8_t* codes, int nl, float& scale_out) {
   float y[DA], z[DA];
   rope_part<DA>(xrow, cos_a, sin_a, pos, off, y);
@@ -255,8 +282,6 @@ void k_prologue(PrologueArgs a) {
   // (128 token rows, or D <= 128 channel rows of 132 bytes)
   __shared__ __align__(16) uint32_t stage[kStage / 4];
   __shared__ float red[16];
-  // rotation matrices in fp64, k-major: partition t at 0, h at D0^2, w at D0^2 + D1^2
-  __shared__ __align__(16) double rot[D0 * D0 + 2 * D1 * D1];
   int8_t* codes = (int8_t*)stage;
 
   const int blk = blockIdx.x, bh = blockIdx.y;
@@ -293,22 +318,9 @@ void k_prologue(PrologueArgs a) {
     return;
   }
 
-  for (int i = threadIdx.x; i < D0 * D0 + 2 * D1 * D1; i += kThreads) {
-    int p = 0, j = i, w_ = D0;
-    const float* src = a.rot_t;
-    if (i >= D0 * D0) {
-      j = i - D0 * D0;
-      p = 1 + (j >= D1 * D1);
-      j -= (p - 1) * D1 * D1;
-      w_ = D1;
-      src = p == 1 ? a.rot_h : a.rot_w;
-    }
-    const int k = j / w_, r = j % w_;              // stored [k][r] from R[r][k]
-    rot[i] = (double)src[r * w_ + k];
-  }
-
   const size_t pad_row = ((size_t)bh * a.NB + blk) * kBlock;   // first packed row of this block
-  const double* Rk = rot + (part == 0 ? 0 : D0 * D0 + (part - 1) * D1 * D1);
+  // rotation matrices: partition t at 0, h at D0^2, w at D0^2 + D1^2 (fp64, [k][r])
+  const rot_ptr Rk = (rot_ptr)a.rot64 + (part == 0 ? 0 : D0 * D0 + (part - 1) * D1 * D1);
 #pragma unroll 1
   for (int s = 0; s < 2; ++s) {
     load_tile<D>((s == 0 ? a.q : a.k) + head_tok * D, n0, a.N, stage);

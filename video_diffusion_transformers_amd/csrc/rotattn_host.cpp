@@ -11,6 +11,7 @@ using namespace rotattn;
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr size_t kRotBytes = 3 * 64 * 64 * sizeof(double);   // fp64 rotation scratch
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
@@ -119,7 +120,7 @@ size_t rotattn_prepared_bytes(const rotattn_shape* s, int with_rope, int layout)
   const size_t packed = align_up(BH * NB * kBlock * D * per_code / 2);
   const size_t scales = align_up(BH * NB * sizeof(float));
   const size_t rope = with_rope ? align_up(BH * (size_t)s->N * D * 2) : 0;
-  return 3 * packed + 3 * scales + 2 * rope;
+  return 3 * packed + 3 * scales + kRotBytes + 2 * rope;
 }
 
 int rotattn_prepared_carve(const rotattn_shape* s, void* base, size_t bytes, int with_rope,
@@ -143,6 +144,7 @@ int rotattn_prepared_carve(const rotattn_shape* s, void* base, size_t bytes, int
   out->q_scale_l2 = (float*)p; p += scales;
   out->k_scale = (float*)p; p += scales;
   out->v_scale = (float*)p; p += scales;
+  out->rot64 = (double*)p; p += kRotBytes;
   if (with_rope) {
     out->q_rope = (uint16_t*)p; p += rope;
     out->k_rope = (uint16_t*)p; p += rope;
@@ -168,7 +170,8 @@ int rotattn_prepare_qkv(const rotattn_shape* s, const uint16_t* q, const uint16_
   int n_fb = 0;
   const HeadBits fb = make_bits(fallback_mask_host, BH, true, false, &n_fb);
   if (n_fb < BH) {
-    if (!out->q4 || !out->k4 || !out->v4 || !out->q_scale_l2 || !out->k_scale || !out->v_scale)
+    if (!out->q4 || !out->k4 || !out->v4 || !out->q_scale_l2 || !out->k_scale || !out->v_scale ||
+        !out->rot64)
       return ROTATTN_E_NULL;
     if (!aligned16(out->q4) || !aligned16(out->k4) || !aligned16(out->v4)) return ROTATTN_E_ALIGN;
   }
@@ -178,12 +181,15 @@ int rotattn_prepare_qkv(const rotattn_shape* s, const uint16_t* q, const uint16_
   }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return ROTATTN_E_ALIGN;
 
+  if (n_fb < BH && launch_rot_to_f64(rr->rot_t, rr->rot_h, rr->rot_w, s->d_t, s->d_h, out->rot64,
+                                     stream) != hipSuccess)
+    return ROTATTN_E_HIP;
   PrologueArgs a;
   a.q = q; a.k = k; a.v = v;
   a.cos_t = rr->cos_t; a.sin_t = rr->sin_t;
   a.cos_h = rr->cos_h; a.sin_h = rr->sin_h;
   a.cos_w = rr->cos_w; a.sin_w = rr->sin_w;
-  a.rot_t = rr->rot_t; a.rot_h = rr->rot_h; a.rot_w = rr->rot_w;
+  a.rot64 = out->rot64;
   a.q4 = out->q4; a.k4 = out->k4; a.v4 = out->v4;
   a.q_scale_l2 = out->q_scale_l2; a.k_scale = out->k_scale; a.v_scale = out->v_scale;
   a.q_rope = out->q_rope; a.k_rope = out->k_rope;

@@ -48,7 +48,7 @@ class RopeRot(C.Structure):
 class Prepared(C.Structure):
     _fields_ = [("layout", C.c_int32)] + [
         (n, C.c_void_p) for n in ("q4", "k4", "v4", "q_scale_l2", "k_scale", "v_scale", "q_rope",
-                                  "k_rope")]
+                                  "k_rope", "rot64")]
 
 
 class Debug(C.Structure):
