@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="720p", choices=["720p", "480p", "small", "mixed"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time the step only: skip the packed-layout, mixed_fwd and all-FP16 "
+                         "side figures (used for counter collection)")
     ap.add_argument("--mixed-steps", type=int, default=1,
                     help="denoising steps of the mixed workload to time as a side figure (0: skip)")
     return ap.parse_args()
@@ -145,11 +148,11 @@ def main():
     achieved = int4_ops / (k2_ms * 1e-3) / 1e12 if n_int4 else 0.0
     traffic = traffic_from_profile(k2_ms)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_I8_TOPS,
-                "unit": "TOPS", "frac": round(achieved / PEAK_I8_TOPS, 4), "traffic": traffic,
+                "unit": "TOP/s", "frac": round(achieved / PEAK_I8_TOPS, 4), "traffic": traffic,
                 "kernel": "k_int4_attn_f8<128>", "algorithmic_ops_per_launch": int4_ops}
     # prologue: algorithmic HBM bytes per token per head (read Q,K,V fp16; write
-    # packed INT4 Q,K,V; block scales are negligible)
-    k1_bytes = BH * N * (3 * 2 * D + 3 * D / 2)
+    # Q,K,V codes one byte each in the FP8-lane layout; block scales are negligible)
+    k1_bytes = BH * N * (3 * 2 * D + 3 * D)
     kernels = {
         "prologue_ms": round(float(k1.mean()), 4),
         "prologue_hbm_frac": round(k1_bytes / (float(k1.mean()) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -160,47 +163,48 @@ def main():
         "event_step_ms": round(float(tot.mean()), 4),
     }
 
-    # the same INT4 attention on the nibble-packed layout (i8 MFMA kernel)
-    prep_p = R.PreparedDevice(shape, with_rope=False, layout=R.LAYOUT_PACKED)
-    R.prepare_qkv(shape, qd, kd, vd, rr, prep_p, mask)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    R.int4_fwd(shape, prep_p, o, mask=mask)
-    e0.record()
-    for _ in range(3):
+    if not args.no_extras:
+        # the same INT4 attention on the nibble-packed layout (i8 MFMA kernel)
+        prep_p = R.PreparedDevice(shape, with_rope=False, layout=R.LAYOUT_PACKED)
+        R.prepare_qkv(shape, qd, kd, vd, rr, prep_p, mask)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         R.int4_fwd(shape, prep_p, o, mask=mask)
-    e1.record()
-    torch.cuda.synchronize()
-    kernels["int4_attn_packed_i8_ms"] = round(e0.elapsed_time(e1) / 3, 4)
-    del prep_p
+        e0.record()
+        for _ in range(3):
+            R.int4_fwd(shape, prep_p, o, mask=mask)
+        e1.record()
+        torch.cuda.synchronize()
+        kernels["int4_attn_packed_i8_ms"] = round(e0.elapsed_time(e1) / 3, 4)
+        del prep_p
 
-    # mixed_fwd (one C call) on the same inputs, as a cross-check of the sequence
-    ws = torch.empty(R.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
-    R.mixed_fwd(shape, qd, kd, vd, rr, mask, ws, o)
-    e0.record()
-    for _ in range(3):
+        # mixed_fwd (one C call) on the same inputs, as a cross-check of the sequence
+        ws = torch.empty(R.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
         R.mixed_fwd(shape, qd, kd, vd, rr, mask, ws, o)
-    e1.record()
-    torch.cuda.synchronize()
-    kernels["mixed_fwd_call_ms"] = round(e0.elapsed_time(e1) / 3, 4)
-    del ws
+        e0.record()
+        for _ in range(3):
+            R.mixed_fwd(shape, qd, kd, vd, rr, mask, ws, o)
+        e1.record()
+        torch.cuda.synchronize()
+        kernels["mixed_fwd_call_ms"] = round(e0.elapsed_time(e1) / 3, 4)
+        del ws
 
-    # FP16 FlashAttention on every head of the same shape (kernel-level analogue
-    # of the full-precision baseline) -- context figure
-    all_fb = np.ones(BH, np.uint8)
-    R.prepare_qkv(shape, qd, kd, vd, rr, prep, all_fb)
-    e0.record()
-    R.fp16_fwd(shape, qr, kr, vd, o, head_select=all_fb)
-    e1.record()
-    torch.cuda.synchronize()
-    R.fp16_fwd(shape, qr, kr, vd, o, head_select=all_fb)
-    e2 = torch.cuda.Event(enable_timing=True)
-    e2.record()
-    torch.cuda.synchronize()
-    f16_ms = e1.elapsed_time(e2)
-    kernels["fp16_attn_all_heads_ms"] = round(f16_ms, 4)
-    kernels["fp16_attn_f16_peak_frac"] = round(ops / (f16_ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4)
-    kernels["int4_vs_fp16_kernel_speedup"] = round(f16_ms / k2_ms, 3) if n_int4 == BH else None
-    print(f"[bench] fp16 all heads {f16_ms:.3f} ms", file=sys.stderr, flush=True)
+        # FP16 FlashAttention on every head of the same shape (kernel-level analogue
+        # of the full-precision baseline) -- context figure
+        all_fb = np.ones(BH, np.uint8)
+        R.prepare_qkv(shape, qd, kd, vd, rr, prep, all_fb)
+        e0.record()
+        R.fp16_fwd(shape, qr, kr, vd, o, head_select=all_fb)
+        e1.record()
+        torch.cuda.synchronize()
+        R.fp16_fwd(shape, qr, kr, vd, o, head_select=all_fb)
+        e2 = torch.cuda.Event(enable_timing=True)
+        e2.record()
+        torch.cuda.synchronize()
+        f16_ms = e1.elapsed_time(e2)
+        kernels["fp16_attn_all_heads_ms"] = round(f16_ms, 4)
+        kernels["fp16_attn_f16_peak_frac"] = round(ops / (f16_ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4)
+        kernels["int4_vs_fp16_kernel_speedup"] = round(f16_ms / k2_ms, 3) if n_int4 == BH else None
+        print(f"[bench] fp16 all heads {f16_ms:.3f} ms", file=sys.stderr, flush=True)
     del qd, kd, vd, prep, o, qr, kr
     torch.cuda.empty_cache()
 
@@ -216,7 +220,7 @@ def main():
     line = {
         "metric": METRIC,
         "value": round(value, 2),
-        "unit": "TOPS",
+        "unit": "TOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -301,7 +305,7 @@ def cpu_baseline(cfg, q, k, v, r32, ops):
     full_s = t_tab + cfg.BH * t_pro + cfg.BH * t_att * cfg.N / rows_n
     print(f"[bench] cpu oracle: prologue {t_pro:.2f}s/head, attention {t_att:.2f}s/{rows_n} rows "
           f"-> {full_s / 3600:.1f} h extrapolated", file=sys.stderr, flush=True)
-    return {"value": round(ops / full_s / 1e12, 6), "unit": "TOPS", "cores": int(cores),
+    return {"value": round(ops / full_s / 1e12, 6), "unit": "TOP/s", "cores": int(cores),
             "kind": "oracle",
             "sample": f"head 0 of {cfg.name}: prologue over all {cfg.N} tokens ({t_pro:.2f} s) + "
                       f"INT4 attention of {rows_n} query rows ({t_att:.2f} s), extrapolated to "
