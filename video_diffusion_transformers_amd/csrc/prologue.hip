@@ -8,17 +8,21 @@
 // symmetric INT4 quantization.  Heads routed to the FP16 fallback only get
 // RoPE'd fp16 Q/K.
 //
-// One work-group per (128-token block, head); 384 threads = 6 waves; waves
-// 2a, 2a+1 own RoPE partition a (t, h, w) for tokens 0-63 / 64-127 of the
-// block, one token per lane.  Arithmetic (bit-exact by construction; this
-// file is built with -ffp-contract=off):
+// One work-group per (128-token block, head); 384 threads = 6 waves.
+// Arithmetic (bit-exact by construction; this file is built with
+// -ffp-contract=off):
 //   RoPE   y0 = fl(fl(x0*c) - fl(x1*s)), y1 = fl(fl(x0*s) + fl(x1*c))   fp32
-//   rotate z_r = fl32(sum_k R[r][k]*y_k): v_fma_f64 chain, k ascending (the
-//          fp32 x fp32 products are exact in fp64), one rounding to fp32
+//   rotate z_r = fl32(sum_k R[r][k]*y_k) in fp64, k ascending (the fp32 x fp32
+//          products are exact in fp64), one rounding to fp32
 //   INT4   per block: amax over the 128 tokens x D channels, inv = fl(7/amax),
 //          scale = fl(amax/7), code = clamp(rne(fl(z*inv)), -7, 7)
-// The rotation matrices are converted once to fp64 (library scratch) and read
-// through the scalar unit: every MAC is one v_fma_f64 with an SGPR operand.
+// The rotation of a partition is a [128 tokens x d_a] x [d_a x d_a] product and
+// runs on v_mfma_f64_16x16x4_f64, which accumulates D = C + a0 b0 + a1 b1 +
+// a2 b2 + a3 b3 as a chain of fused multiply-adds in ascending k (checked
+// bit for bit on the device against that chain), so 16x16x4 steps chained over
+// k reproduce the sequential fp64 sum exactly.  Wave 2a + h owns partition a
+// and tokens 64h..64h+63: R_a^T sits in its registers as B fragments, and the A
+// fragments are RoPE'd on the fly from the staged fp16 rows.
 #include "rotattn_internal.h"
 
 namespace rotattn {
@@ -47,11 +51,6 @@ __device__ __forceinline__ void rope_part(const uint32_t* xrow, const float* cos
   }
 }
 
-// The rotation in fp64, k-major ([k][r] per partition), read through the
-// constant address space: uniform addresses become s_load, and every MAC is one
-// v_fma_f64 with an SGPR coefficient (no LDS traffic, no vector loads).
-typedef const __attribute__((address_space(4))) double* rot_ptr;
-
 __global__ void k_rot_to_f64(const float* rt, const float* rh, const float* rw, int dt, int dh,
                              double* out) {
   const int total = dt * dt + 2 * dh * dh;
@@ -74,31 +73,6 @@ hipError_t launch_rot_to_f64(const float* rt, const float* rh, const float* rw, 
                              double* out, hipStream_t st) {
   hipLaunchKernelGGL(k_rot_to_f64, dim3(16), dim3(256), 0, st, rt, rh, rw, dt, dh, out);
   return hipGetLastError();
-}
-
-// z = R y over one partition: fp64 accumulation, k ascending, one rounding.
-// G outputs are accumulated side by side so that G independent v_fma_f64
-// chains hide the FMA latency.
-template <int DA>
-__device__ __forceinline__ void rotate_part(const float (&y)[DA], rot_ptr Rk, float (&z)[DA]) {
-  constexpr int G = (DA % 4 == 0) ? 4 : 6;
-  static_assert(DA % G == 0, "partition width must split into groups");
-  double yd[DA];
-#pragma unroll
-  for (int k = 0; k < DA; ++k) yd[k] = (double)y[k];
-#pragma unroll
-  for (int r0 = 0; r0 < DA; r0 += G) {
-    double acc[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = 0.0;
-#pragma unroll
-    for (int k = 0; k < DA; ++k) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) acc[g] = __builtin_fma(Rk[k * DA + r0 + g], yd[k], acc[g]);
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) z[r0 + g] = (float)acc[g];
-  }
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -143,23 +117,117 @@ __device__ __forceinline__ int8_t code_byte(int c) {
   return F8 ? (int8_t)e4m3_of(c) : (int8_t)c;
 }
 
-// One tensor (Q or K) of one partition for this lane's token: RoPE, rotation,
-// block scale, codes into the LDS code buffer (row = token, padded stride).
-template <int DA, bool F8>
-__device__ __forceinline__ void qk_part(const uint32_t* xrow, const float* cos_a,
-                                        const float* sin_a, int pos, int off, rot_ptr R,
-                                        float* red, int8_t* codes, int nl, float& scale_out) {
-  float y[DA], z[DA];
-  rope_part<DA>(xrow, cos_a, sin_a, pos, off, y);
-  rotate_part<DA>(y, R, z);
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+// Shape of one partition's rotation on 16x16x4 fp64 MFMA steps.
+template <int DA>
+struct Part {
+  static constexpr int KS = (DA + 3) / 4;     // k-steps (channels, zero-padded to 4)
+  static constexpr int JB = (DA + 15) / 16;   // 16-wide output blocks (zero-padded)
+};
+
+// B fragments of R_a^T: lane l holds B[k][j] = R[j][k] for k = 4 ks + l/16,
+// j = 16 jb + l%16 (zero outside d_a), kept as fp32 (R is fp32-valued; the
+// conversion to fp64 at each use is exact).  rot is [k][r] in fp64.
+template <int DA>
+__device__ __forceinline__ void load_rot_frags(const double* rot,
+                                               float (&b)[Part<DA>::KS][Part<DA>::JB]) {
+  const int l = threadIdx.x & 63;
+#pragma unroll
+  for (int ks = 0; ks < Part<DA>::KS; ++ks)
+#pragma unroll
+    for (int jb = 0; jb < Part<DA>::JB; ++jb) {
+      const int k = 4 * ks + (l >> 4), j = 16 * jb + (l & 15);
+      b[ks][jb] = (k < DA && j < DA) ? (float)rot[k * DA + j] : 0.0f;
+    }
+}
+
+// RoPE + rotation of one tensor over this wave's partition (width DA at channel
+// offset off) and 64 tokens (tok0..tok0+63 of the block): z in the MFMA output
+// layout (token row tok0 + 16 tb + l/16 + 4 r, channel 16 jb + l%16), returns
+// the lane's max |z|.  xs: staged fp16 rows of the tensor (kRS dwords per row).
+template <int DA, int kRS>
+__device__ __forceinline__ float rotate_tensor(const uint32_t* xs, const float* cos_a,
+                                               const float* sin_a,
+                                               float (&b)[Part<DA>::KS][Part<DA>::JB], int off,
+                                               int tok0, int n0, int N, int axis, int HW, int gh,
+                                               int gw, float (&z)[4][Part<DA>::JB][4]) {
+  constexpr int KS = Part<DA>::KS, JB = Part<DA>::JB;
+  const int l = threadIdx.x & 63;
   float amax = 0.0f;
 #pragma unroll
-  for (int r = 0; r < DA; ++r) amax = fmaxf(amax, fabsf(z[r]));
-  float inv, scale;
-  block_scale(amax, red, inv, scale);
+  for (int tb = 0; tb < 4; ++tb) {
+    // the fp32 fragments are marked as changing here so that their fp64
+    // conversions stay next to the MFMAs instead of being hoisted into
+    // 2 x KS x JB live registers
 #pragma unroll
-  for (int r = 0; r < DA; ++r) codes[nl * kCodeStride + off + r] = code_byte<F8>(quant(z[r], inv));
-  scale_out = scale;
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) asm volatile("" : "+v"(b[ks][jb]));
+    const int i = tok0 + 16 * tb + (l & 15);   // this lane's A row (token in the block)
+    const int n = n0 + i;
+    // padding tokens have zero rows; any valid table row will do
+    const int pos = n < N ? (axis == 0 ? n / HW : (axis == 1 ? (n / gw) % gh : n % gw)) : 0;
+    const uint32_t* xrow = xs + i * kRS + off / 2;
+    const float* crow = cos_a + pos * (DA / 2);
+    const float* srow = sin_a + pos * (DA / 2);
+    // RoPE'd A fragments of this token block, then the MFMA chain over k
+    double av[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = 4 * ks + (l >> 4);                      // channel in the partition
+      const int jp = (c >> 1) < DA / 2 ? (c >> 1) : DA / 2 - 1;   // pair (clamped on padding)
+      const uint32_t pr = xrow[jp];
+      const float x0 = h2f((uint16_t)(pr & 0xffffu));
+      const float x1 = h2f((uint16_t)(pr >> 16));
+      const float cs = crow[jp], sn = srow[jp];
+      // even channel: fl(x0 c) - fl(x1 s); odd: fl(x0 s) + fl(x1 c); operands
+      // are selected instead of branching (negation is exact)
+      const bool odd = (c & 1) != 0;
+      const float p0 = x0 * (odd ? sn : cs);
+      const float p1 = x1 * (odd ? cs : sn);
+      const float y = p0 + (odd ? p1 : -p1);
+      av[ks] = c < DA ? (double)y : 0.0;
+    }
+    v4d acc[JB];
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) acc[jb] = v4d{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb)
+        acc[jb] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ks], (double)b[ks][jb], acc[jb], 0, 0, 0);
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        z[tb][jb][r] = (float)acc[jb][r];
+        amax = fmaxf(amax, fabsf(z[tb][jb][r]));
+      }
+  }
+  return amax;
+}
+
+// Codes of one tensor's z (MFMA output layout) into the LDS code buffer
+// ([token][channel], kCodeStride bytes per row).
+template <int DA, bool F8>
+__device__ __forceinline__ void quant_tensor(const float (&z)[4][Part<DA>::JB][4], float inv,
+                                             int off, int tok0, int8_t* codes) {
+  constexpr int JBX = Part<DA>::JB;
+  const int l = threadIdx.x & 63;
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int jb = 0; jb < JBX; ++jb) {
+      const int j = 16 * jb + (l & 15);
+      if (j < DA) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = tok0 + 16 * tb + (l >> 4) + 4 * r;
+          codes[row * kCodeStride + off + j] = code_byte<F8>(quant(z[tb][jb][r], inv));
+        }
+      }
+    }
 }
 
 // Fallback head: RoPE'd fp16 pairs written back over the staged row (the
@@ -269,69 +337,42 @@ __device__ __forceinline__ void store_v_codes(const int8_t* codesT, uint8_t* dst
   }
 }
 
-// 3 waves per SIMD: two 6-wave work-groups per CU, so one group's rotation
-// overlaps the other's memory phases
-template <int D, int D0, int D1, bool F8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
-void k_prologue(PrologueArgs a) {
-  static_assert(D0 + 2 * D1 == D, "split must be (D0, D1, D1)");
-  constexpr int kRS = D / 2 + 1;   // staged fp16 row, in dwords
-  constexpr int kStage = (kBlock * kRS * 4 > kBlock * kCodeStride) ? kBlock * kRS * 4
-                                                                   : kBlock * kCodeStride;
-  // one buffer, two lives: the staged fp16 rows of a tensor, then its INT4 codes
-  // (128 token rows, or D <= 128 channel rows of 132 bytes)
-  __shared__ __align__(16) uint32_t stage[kStage / 4];
-  __shared__ float red[16];
-  int8_t* codes = (int8_t*)stage;
-
-  const int blk = blockIdx.x, bh = blockIdx.y;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  // wave-uniform: lets the rotation matrices and tables go through the scalar unit
-  const int part = __builtin_amdgcn_readfirstlane(w >> 1);
-  const int nl = (w & 1) * 64 + lane;
+// A head that is not a fallback head, as seen by one wave (partition of width
+// DA at channel offset off, RoPE axis `axis`): per tensor, RoPE + rotation on
+// the MFMA, block amax, codes into the LDS buffer that held the tensor's rows,
+// coalesced store; then V: block amax and codes, stored transposed.  Every
+// wave runs the same sequence of barriers whatever its partition.
+template <int D, int DA, bool F8>
+__device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* stage_q,
+                                            uint32_t* stage_k, float* red, int blk, int bh,
+                                            int off, int axis, const float* cos_a,
+                                            const float* sin_a, const double* rot) {
+  constexpr int kRS = D / 2 + 1;
+  const int w = threadIdx.x >> 6;
+  const int tok0 = (w & 1) * 64;
   const int n0 = blk * kBlock;
-  const int n = n0 + nl;
   const int HW = a.grid_h * a.grid_w;
-  const int pos = part == 0 ? n / HW : (part == 1 ? (n / a.grid_w) % a.grid_h : n % a.grid_w);
-  const int off = part == 0 ? 0 : (part == 1 ? D0 : D0 + D1);
-  const float* cos_a = part == 0 ? a.cos_t : (part == 1 ? a.cos_h : a.cos_w);
-  const float* sin_a = part == 0 ? a.sin_t : (part == 1 ? a.sin_h : a.sin_w);
   const size_t head_tok = (size_t)bh * a.N;
-  const bool fallback = a.fallback.test(bh);
-  uint32_t* xrow = stage + nl * kRS;
-  // tables are read for every lane; clamp the position of a padding token
-  const int pos_c = n < a.N ? pos : 0;
+  const size_t pad_row = ((size_t)bh * a.NB + blk) * kBlock;   // first code row of this block
 
-  if (fallback) {
-#pragma unroll 1
-    for (int s = 0; s < 2; ++s) {
-      load_tile<D>((s == 0 ? a.q : a.k) + head_tok * D, n0, a.N, stage);
-      __syncthreads();
-      if (part == 0)
-        rope_only_part<D0>(xrow, cos_a, sin_a, pos_c, off);
-      else
-        rope_only_part<D1>(xrow, cos_a, sin_a, pos_c, off);
-      __syncthreads();
-      store_tile<D>((s == 0 ? a.q_rope : a.k_rope) + head_tok * D, n0, a.N, stage);
-      __syncthreads();
-    }
-    return;
-  }
+  load_tile<D>(a.q + head_tok * D, n0, a.N, stage_q);
+  load_tile<D>(a.k + head_tok * D, n0, a.N, stage_k);
+  float b[Part<DA>::KS][Part<DA>::JB];   // R_a^T of this wave's partition
+  load_rot_frags<DA>(rot, b);
+  __syncthreads();
 
-  const size_t pad_row = ((size_t)bh * a.NB + blk) * kBlock;   // first packed row of this block
-  // rotation matrices: partition t at 0, h at D0^2, w at D0^2 + D1^2 (fp64, [k][r])
-  const rot_ptr Rk = (rot_ptr)a.rot64 + (part == 0 ? 0 : D0 * D0 + (part - 1) * D1 * D1);
 #pragma unroll 1
   for (int s = 0; s < 2; ++s) {
-    load_tile<D>((s == 0 ? a.q : a.k) + head_tok * D, n0, a.N, stage);
-    __syncthreads();
-    float scale;
-    // the rows are read before the first barrier of the block-scale reduction,
-    // and the codes written after it, so the two lives of `stage` never overlap
-    if (part == 0)
-      qk_part<D0, F8>(xrow, cos_a, sin_a, pos_c, off, Rk, red, codes, nl, scale);
-    else
-      qk_part<D1, F8>(xrow, cos_a, sin_a, pos_c, off, Rk, red, codes, nl, scale);
+    uint32_t* xs = s == 0 ? stage_q : stage_k;
+    float z[4][Part<DA>::JB][4];
+    const float amax = rotate_tensor<DA, kRS>(xs, cos_a, sin_a, b, off, tok0, n0, a.N, axis, HW,
+                                              a.grid_h, a.grid_w, z);
+    float inv, scale;
+    // every wave is past its last read of xs once the reduction's barriers are
+    // passed: the buffer takes the codes next
+    block_scale(amax, red, inv, scale);
+    int8_t* codes = (int8_t*)xs;
+    quant_tensor<DA, F8>(z, inv, off, tok0, codes);
     __syncthreads();
     if (F8)
       store_qk_codes_f8<D>(codes, (s == 0 ? a.q4 : a.k4) + pad_row * D);
@@ -343,24 +384,87 @@ void k_prologue(PrologueArgs a) {
       else
         a.k_scale[(size_t)bh * a.NB + blk] = scale;
     }
-    __syncthreads();
   }
+  __syncthreads();
 
-  {
-    load_tile<D>(a.v + head_tok * D, n0, a.N, stage);
+  // V: staged in the Q buffer, codes (channel rows) in the K buffer
+  const int nl = tok0 + (threadIdx.x & 63);
+  load_tile<D>(a.v + head_tok * D, n0, a.N, stage_q);
+  __syncthreads();
+  int8_t* codes = (int8_t*)stage_k;
+  float scale;
+  v_part<DA, F8>(stage_q + nl * kRS, off, red, codes, nl, scale);
+  __syncthreads();
+  if (F8)
+    store_v_codes_f8<D>(codes, a.v4 + ((size_t)bh * a.NB + blk) * D * 128);
+  else
+    store_v_codes<D>(codes, a.v4 + ((size_t)bh * a.NB + blk) * D * 64);
+  if (threadIdx.x == 0) a.v_scale[(size_t)bh * a.NB + blk] = scale;
+}
+
+// Fallback head: RoPE'd fp16 Q and K only, one token per lane, wave pair a on
+// partition a.
+template <int D, int D0, int D1>
+__device__ __forceinline__ void prologue_fallback(const PrologueArgs& a, uint32_t* stage, int blk,
+                                                  int bh) {
+  constexpr int kRS = D / 2 + 1;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int part = __builtin_amdgcn_readfirstlane(w >> 1);
+  const int nl = (w & 1) * 64 + lane;
+  const int n0 = blk * kBlock;
+  const int n = n0 + nl;
+  const int HW = a.grid_h * a.grid_w;
+  const int pos = part == 0 ? n / HW : (part == 1 ? (n / a.grid_w) % a.grid_h : n % a.grid_w);
+  const int off = part == 0 ? 0 : (part == 1 ? D0 : D0 + D1);
+  const float* cos_a = part == 0 ? a.cos_t : (part == 1 ? a.cos_h : a.cos_w);
+  const float* sin_a = part == 0 ? a.sin_t : (part == 1 ? a.sin_h : a.sin_w);
+  const size_t head_tok = (size_t)bh * a.N;
+  uint32_t* xrow = stage + nl * kRS;
+  // tables are read for every lane; clamp the position of a padding token
+  const int pos_c = n < a.N ? pos : 0;
+#pragma unroll 1
+  for (int s = 0; s < 2; ++s) {
+    load_tile<D>((s == 0 ? a.q : a.k) + head_tok * D, n0, a.N, stage);
     __syncthreads();
-    float scale;
     if (part == 0)
-      v_part<D0, F8>(xrow, off, red, codes, nl, scale);
+      rope_only_part<D0>(xrow, cos_a, sin_a, pos_c, off);
     else
-      v_part<D1, F8>(xrow, off, red, codes, nl, scale);
+      rope_only_part<D1>(xrow, cos_a, sin_a, pos_c, off);
     __syncthreads();
-    if (F8)
-      store_v_codes_f8<D>(codes, a.v4 + ((size_t)bh * a.NB + blk) * D * 128);
-    else
-      store_v_codes<D>(codes, a.v4 + ((size_t)bh * a.NB + blk) * D * 64);
-    if (threadIdx.x == 0) a.v_scale[(size_t)bh * a.NB + blk] = scale;
+    store_tile<D>((s == 0 ? a.q_rope : a.k_rope) + head_tok * D, n0, a.N, stage);
+    __syncthreads();
   }
+}
+
+// 3 waves per SIMD: two 6-wave work-groups per CU, so that one group's MFMA
+// phase overlaps the other's memory phases.
+template <int D, int D0, int D1, bool F8>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void k_prologue(PrologueArgs a) {
+  static_assert(D0 + 2 * D1 == D, "split must be (D0, D1, D1)");
+  constexpr int kRS = D / 2 + 1;   // staged fp16 row, in dwords
+  static_assert(kBlock * kCodeStride <= kBlock * kRS * 4, "codes fit in a staging buffer");
+  static_assert(D * kCodeStride <= kBlock * kRS * 4, "transposed codes fit in a staging buffer");
+  // two buffers of 128 staged fp16 rows (Q and K; later V and the codes)
+  __shared__ __align__(16) uint32_t stage_q[kBlock * kRS];
+  __shared__ __align__(16) uint32_t stage_k[kBlock * kRS];
+  __shared__ float red[16];
+  const int blk = blockIdx.x, bh = blockIdx.y;
+  if (a.fallback.test(bh)) {
+    prologue_fallback<D, D0, D1>(a, stage_q, blk, bh);
+    return;
+  }
+  // wave pair 2a, 2a+1 on partition a; rotation matrices in fp64 [k][r]:
+  // t at 0, h at D0^2, w at D0^2 + D1^2
+  const int part = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) >> 1);
+  if (part == 0)
+    prologue_qk<D, D0, F8>(a, stage_q, stage_k, red, blk, bh, 0, 0, a.cos_t, a.sin_t, a.rot64);
+  else if (part == 1)
+    prologue_qk<D, D1, F8>(a, stage_q, stage_k, red, blk, bh, D0, 1, a.cos_h, a.sin_h,
+                           a.rot64 + D0 * D0);
+  else
+    prologue_qk<D, D1, F8>(a, stage_q, stage_k, red, blk, bh, D0 + D1, 2, a.cos_w, a.sin_w,
+                           a.rot64 + D0 * D0 + D1 * D1);
 }
 
 hipError_t launch_prologue(int D, int dt, int BH, bool f8, const PrologueArgs& a, hipStream_t st) {
