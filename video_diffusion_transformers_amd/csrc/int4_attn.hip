@@ -45,6 +45,7 @@ struct CodeCtx {
   float ct;      // c_t
   float mnew;    // m'
   float delta;   // half-width of the band around each half-integer that takes the exact path
+  float tz;      // exponent-domain bound: a group whose largest argument is below it has only code 0
 };
 
 __device__ __forceinline__ float ulp_pos(float v) {   // ulp of a positive normal float
@@ -57,15 +58,24 @@ __device__ __forceinline__ CodeCtx make_ctx(float ct, float mnew, float log2_15,
   c.iscale = iscale;
   c.ct = ct;
   c.mnew = mnew;
-  c.cq = ct * iscale;
+  // cq >= 2^-126: a score of -inf (a masked key of the last tile) then gives
+  // t = -inf and y = 0 even when c_t = 0; for |I| < 2^14 the clamp moves t by
+  // less than 2^-112, far inside the error bound below
+  c.cq = fmaxf(ct * iscale, 0x1p-126f);
   c.m15n = log2_15 - mnew;
   // error of the fused argument against x + log2(15) for scores that can
   // round to a code in 1..15 (|x| < 8), in log2 units:
   const float e = 0x1p-21f + ulp_pos(fabsf(mnew) + 8.0f);
   // 15.5 * ln 2 < 10.75; v_exp_f32 error < 1 ulp; 12x and +4e-6 are margin.
   c.delta = 12.0f * e + 4e-6f;
+  // The fused argument t is within e of x + log2(15).  If t < -1 - 2e then
+  // 15*2^x < 1/2, so x < tau_1 and the code is 0; -1 - 4e leaves a factor 2.
+  c.tz = -1.0f - 4.0f * e;
   // c_t so small that c_t * iscale may be subnormal: never trust the fast path.
-  if (ct != 0.0f && ct < 0x1p-100f) c.delta = 1.0f;
+  if (ct != 0.0f && ct < 0x1p-100f) {
+    c.delta = 1.0f;
+    c.tz = -INFINITY;
+  }
   return c;
 }
 
@@ -132,24 +142,44 @@ __device__ __forceinline__ v4i pcode16(const float (&f)[16], float fmax, const C
   return v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
 }
 
-// The same P code for the fp8 kernel: scores arrive as exact float I, the
-// rounding is v_rndne_f32 and the codes leave as E4M3 bytes (exact for the
-// integers 0..15).  rr receives the codes as floats (0 for an all-zero group).
-// Returns the four packed dwords (byte r = E4M3 of the code of score r).
-template <bool TAIL>
+// P-code thresholds as the exact fix-up reads them: [0] = -inf, [k] = tau_k
+// (k = 1..15), [16] = +inf.  Staged in LDS by every kernel that uses them.
+constexpr int kTauTable = 17;
+
+template <typename TauSrc>
+__device__ __forceinline__ void stage_tau(const TauSrc& tau, float* t_lds) {
+  for (int i = threadIdx.x; i < kTauTable; i += blockDim.x)
+    t_lds[i] = i == 0 ? -INFINITY : (i == kTauTable - 1 ? INFINITY : tau[i - 1]);
+}
+
+// Sign bit of a float as 0/1: x >= t  <=>  sign(fl(x - t)) == 0 exactly
+// (-0 and +0 included).
+__device__ __forceinline__ int signbit01(float v) { return (int)(__float_as_uint(v) >> 31); }
+
+// The P code of the fp8 kernel for one lane's 16 scores of a 32-key group
+// (exact float I), as E4M3 bytes (byte r = code of score r; exact for the
+// integers 0..15).  rr receives the codes as floats; lp[] accumulates the
+// unquantized 15*2^x in four partial sums.
+//
+// y = v_exp_f32(t), t = fma(I, c_t, log2(15) - m'), is within delta of
+// 15*2^x.  If no lane's largest t reaches tz, every code of the group is 0.
+// Otherwise code = rne(y) unless some |y - rne(y)| exceeds 1/2 - delta in the
+// wave; then every score of the group is fixed exactly: the true value lies
+// within delta of y, so the code is j - 1 or j for the half-integer boundary
+// j - 1/2 nearest y (j = rne(y) + [y > rne(y)]), and it is j iff x >= tau_j
+// with x = fl(fl(I c_t) - m') -- one comparison against the staged table.
+// Masked keys (last tile) arrive as I = -inf: t = -inf, y = 0, code 0 on both
+// paths (the exact one sees x = -inf or NaN against tau_0 = -inf with j = 0).
 __device__ __forceinline__ v4i pcode16_f8(const float (&f)[16], float fmax, const CodeCtx& cx,
-                                          const float* tau, float& lsum, uint32_t valid,
+                                          const float* tau_lds, float& lsum,
                                           float (&rr)[16]) {
   float y[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    float t = fmaf(f[r], cx.cq, cx.m15n);
-    if (TAIL) t = ((valid >> r) & 1u) ? t : -INFINITY;
-    y[r] = __builtin_amdgcn_exp2f(t);
+    y[r] = __builtin_amdgcn_exp2f(fmaf(f[r], cx.cq, cx.m15n));
     lsum += y[r];
   }
-  const float ymax = __builtin_amdgcn_exp2f(fmaf(fmax, cx.cq, cx.m15n));
-  if (!wave_any(ymax >= 0.5f - cx.delta)) {
+  if (!wave_any(fmaf(fmax, cx.cq, cx.m15n) >= cx.tz)) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) rr[r] = 0.0f;
     return v4i{0, 0, 0, 0};
@@ -163,14 +193,19 @@ __device__ __forceinline__ v4i pcode16_f8(const float (&f)[16], float fmax, cons
   if (wave_any(g > 0.5f - cx.delta)) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int code = exact_code(f[r], cx, tau);
-      rr[r] = (TAIL && !((valid >> r) & 1u)) ? 0.0f : (float)code;
+      int j = (int)rr[r] + signbit01(rr[r] - y[r]);          // rne(y) + [y > rne(y)]
+      j = j < 0 ? 0 : (j > kTauTable - 1 ? kTauTable - 1 : j);
+      const float x = f[r] * cx.iscale * cx.ct - cx.mnew;   // fl(fl(I c_t) - m')
+      const int code = j - signbit01(x - tau_lds[j]);       // j - 1 + [x >= tau_j]
+      rr[r] = (float)(code < 0 ? 0 : code);
     }
   }
   uint32_t pk[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(rr[4 * i], rr[4 * i + 1], 0u, false);
+    // the untouched half of the first conversion is overwritten by the second
+    const uint32_t lo =
+        __builtin_amdgcn_cvt_pk_fp8_f32(rr[4 * i], rr[4 * i + 1], __float_as_uint(y[4 * i]), false);
     pk[i] = __builtin_amdgcn_cvt_pk_fp8_f32(rr[4 * i + 2], rr[4 * i + 3], lo, true);
   }
   return v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
@@ -436,7 +471,7 @@ hipError_t launch_int4(int D, int BH, const Int4Args& a, const Int4Debug* dbg, h
 
 // ------------------------------------------------------------- fp8 kernel
 //
-// Same work-group shape and pipeline, with the codes in E4M3 bytes:
+// The INT4 attention on the FP8-lane layout (codes as E4M3 bytes):
 //   S^T  = K_t Q^T on v_mfma_f32_32x32x64_f8f6f4: the fp32 result is I exactly
 //          (integer products and partial sums below 2^24)
 //   O^T  accumulates V_t^T P^T straight into fp32 on the same MFMA, kept in
@@ -445,120 +480,69 @@ hipError_t launch_int4(int D, int BH, const Int4Args& a, const Int4Debug* dbg, h
 // No unpacking (the prologue stores operand-ready bytes) and no int->float
 // conversions; per score the VALU work is the fused argument, exp2, the l
 // sum and, for groups with a nonzero code, rndne + the guard + the packing.
+// One work-group = 4 waves = one 128-query block of one head, 32 queries per
+// wave; two work-groups per CU, so that on each SIMD one wave's softmax (VALU)
+// overlaps the other's MFMAs, which run at raised wave priority.  Per tile:
+// S, softmax, then the K/V tiles of t+1 are requested straight into the other
+// LDS buffers (global_load_lds) while P.V of tile t runs; one barrier per tile.
 template <int D, bool DBG>
 struct Int4F8Kernel {
   static constexpr int KS = D / 64;        // k-steps of 64 channels for QK^T
   static constexpr int DB = D / 32;        // 32-channel blocks of O^T
-  static constexpr int KStride = D + 16;   // K tile row in LDS (bytes)
-  static constexpr int VStride = 128 + 16; // V^T tile row in LDS (bytes)
-  static constexpr int BPT = D / 2;        // bytes staged per thread for K and for V^T
-  static constexpr int TPR = 256 / D;      // threads per V^T row
+  static constexpr int NTHR = 256;
+  // K tiles ([128 keys][D]) and V^T tiles ([D][128 keys]) sit unpadded in LDS,
+  // filled by global_load_lds_dwordx4 (lane L of a wave writes bytes 16L..16L+15
+  // of the wave's 1 KiB window); their 16-byte chunks are XOR-swizzled per row
+  // so that the MFMA operand reads of 8 consecutive rows hit 8 different chunk
+  // columns (all 32 banks).
+  static constexpr int KCPR = D / 16;                  // chunks per K row
+  static constexpr int KROWS128 = 128 / D;             // K rows per 128 bytes
+  static constexpr int KCHUNKS = kBlock * D / 16;      // chunks per tile (K or V^T)
+  static constexpr int LOADS = KCHUNKS / NTHR;         // load instructions per thread per tile
+  static constexpr int NW = NTHR / 64;                 // waves
+  static_assert(KCHUNKS % NTHR == 0, "whole waves per tile");
+
+  __device__ __forceinline__ static int kswz(int row) { return (row / (2 * KROWS128)) & (KCPR - 1); }
+  __device__ __forceinline__ static int vswz(int row) { return (row >> 1) & 7; }
 
   __device__ __forceinline__ static v8i ld32(const uint8_t* p) {
     const uint4 a = *(const uint4*)p, b = *(const uint4*)(p + 16);
     return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
   }
+  // 32 bytes of a swizzled row: logical chunks c0, c0 + 1
+  __device__ __forceinline__ static v8i ld32s(const uint8_t* row, int c0, int key) {
+    const uint4 a = *(const uint4*)(row + 16 * (c0 ^ key));
+    const uint4 b = *(const uint4*)(row + 16 * ((c0 + 1) ^ key));
+    return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+  }
 
-  template <bool TAIL>
-  __device__ __forceinline__ static void scores(const Int4Args& a, const Int4Debug& dbg, int bh,
-                                                int t, const uint8_t* sk, const v8i (&qf)[KS],
-                                                float qs, float& m, float& l, float& u,
-                                                v16f (&O)[DB], v8i (&P)[2]) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // S^T = K_t Q^T
+  __device__ __forceinline__ static void qk(const uint8_t* sk, const v8i (&qf)[KS], v16f (&S)[4]) {
+    const int lane = threadIdx.x & 63;
     const int col = lane & 31, hh = lane >> 5;
-    const size_t sidx = (size_t)bh * a.NB + t;
-
-    v16f S[4];
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
+      const int row = 32 * sub + col;
       S[sub] = v16f{0.0f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        S[sub] = mfma_f8(ld32(sk + (32 * sub + col) * KStride + 64 * ks + 32 * hh), qf[ks], S[sub]);
-    }
-
-    uint32_t valid[4] = {0xffffu, 0xffffu, 0xffffu, 0xffffu};
-    if (TAIL) {
-      const int nv = a.N - t * kBlock;
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        uint32_t vm = 0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * sub + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key < nv) vm |= 1u << r;
-          else S[sub][r] = -INFINITY;
-        }
-        valid[sub] = vm;
-      }
-    }
-
-    float smx[4];
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-      smx[sub] = S[sub][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) smx[sub] = fmaxf(smx[sub], S[sub][r]);
-    }
-    float mx = fmaxf(fmaxf(smx[0], smx[1]), fmaxf(smx[2], smx[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-
-    const float ct = qs * a.k_scale[sidx];
-    const float smax = mx * ct;
-    const float mnew = fmaxf(m, smax);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-    const float sv = a.v_scale[sidx];
-    const float unew = sv > 0.0f ? sv : u;
-    const float beta = alpha * (u / unew);
-    u = unew;
-    if (wave_any(beta != 1.0f)) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) O[db][r] *= beta;
-    }
-    m = mnew;
-    const CodeCtx cx = make_ctx(ct, mnew, a.log2_15, 1.0f);
-
-    float ls = 0.0f;
-    float rr[4][16];
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-      float f[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) f[r] = S[sub][r];
-      const v4i pk = pcode16_f8<TAIL>(f, smx[sub], cx, a.tau, ls, valid[sub], rr[sub]);
-      // 64-key chunk c = sub/2 holds subtile 2c in bytes 0-15, 2c+1 in 16-31
-#pragma unroll
-      for (int i = 0; i < 4; ++i) P[sub >> 1][4 * (sub & 1) + i] = pk[i];
-    }
-    l = fmaf(l, alpha, ls);
-
-    if (DBG) {
-      const int q = 32 * w + col;
-      const size_t npad = (size_t)a.NB * kBlock;
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const size_t key = (size_t)t * kBlock + 32 * sub + 8 * (r >> 2) + 4 * hh + (r & 3);
-          dbg.s_int[q * npad + key] = (TAIL && !((valid[sub] >> r) & 1u)) ? INT32_MIN : (int32_t)S[sub][r];
-          dbg.p_code[q * npad + key] = (uint8_t)rr[sub][r];
-        }
+        S[sub] = mfma_f8(ld32s(sk + row * D, 4 * ks + 2 * hh, kswz(row)), qf[ks], S[sub]);
     }
   }
 
-  __device__ __forceinline__ static void pv(const Int4Args& a, const Int4Debug& dbg, int t,
-                                            const uint8_t* sv, const v8i (&P)[2], v16f (&O)[DB]) {
+  // O^T += V_t^T P^T
+  __device__ __forceinline__ static void pv(const Int4Debug& dbg, int t, const uint8_t* sv,
+                                            const v8i (&P)[2], v16f (&O)[DB]) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int col = lane & 31, hh = lane >> 5;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
+      const int row = 32 * db + col;
       if (DBG) {
         v16f pvt = v16f{0.0f};
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          pvt = mfma_f8(ld32(sv + (32 * db + col) * VStride + 64 * c + 32 * hh), P[c], pvt);
+          pvt = mfma_f8(ld32s(sv + row * kBlock, 4 * c + 2 * hh, vswz(row)), P[c], pvt);
         const int q = 32 * w + col;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -569,21 +553,105 @@ struct Int4F8Kernel {
       } else {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          O[db] = mfma_f8(ld32(sv + (32 * db + col) * VStride + 64 * c + 32 * hh), P[c], O[db]);
+          O[db] = mfma_f8(ld32s(sv + row * kBlock, 4 * c + 2 * hh, vswz(row)), P[c], O[db]);
       }
     }
   }
 
+  // Keys >= nv of the tile (last tile only) get S = -inf: they then take no
+  // part in the max, and give y = 0 and code 0.
+  __device__ __forceinline__ static void mask_tail(v16f (&S)[4], int nv) {
+    const int hh = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * sub + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (key >= nv) S[sub][r] = -INFINITY;
+      }
+  }
+
+  // Softmax of key tile t (nv valid keys): running max, rescale of O, P codes,
+  // row sum.
+  __device__ __forceinline__ static void softmax(const Int4Args& a, const Int4Debug& dbg,
+                                                 const float* tau_lds, int bh, int t, int nv,
+                                                 v16f (&S)[4], float qs, float& m, float& l,
+                                                 float& u, v16f (&O)[DB], v8i (&P)[2]) {
+    const int lane = threadIdx.x & 63, wl = threadIdx.x >> 6;
+    const int hh = lane >> 5, col = lane & 31;
+    const size_t sidx = (size_t)bh * a.NB + t;
+
+    // a running chain: it compiles to v_max3 with one canonicalisation per group
+    float smx[4];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      smx[sub] = S[sub][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) smx[sub] = fmaxf(smx[sub], S[sub][r]);
+    }
+    float mx = fmaxf(fmaxf(smx[0], smx[1]), fmaxf(smx[2], smx[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+
+    // the block scales are read through the scalar unit (uniform address):
+    // as vector loads they would sit behind the next tile's loads in vmcnt order
+    typedef const __attribute__((address_space(4))) float* cfloat_ptr;
+    const float ct = qs * ((cfloat_ptr)a.k_scale)[sidx];
+    const float mnew = fmaxf(m, mx * ct);
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    // O is kept in units of the current tile's V scale; a rescale error of an
+    // ulp is far below the fp16 output rounding
+    const float sv = ((cfloat_ptr)a.v_scale)[sidx];
+    const float unew = sv > 0.0f ? sv : u;
+    const float beta = alpha * (u * __builtin_amdgcn_rcpf(unew));
+    u = unew;
+    m = mnew;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) O[db][r] *= beta;
+    const CodeCtx cx = make_ctx(ct, mnew, a.log2_15, 1.0f);
+
+    float ls = 0.0f;
+    float rr[4][16];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      float f[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) f[r] = S[sub][r];
+      const v4i pk = pcode16_f8(f, smx[sub], cx, tau_lds, ls, rr[sub]);
+      // 64-key chunk c = sub/2 holds subtile 2c in bytes 0-15, 2c+1 in 16-31
+#pragma unroll
+      for (int i = 0; i < 4; ++i) P[sub >> 1][4 * (sub & 1) + i] = pk[i];
+    }
+    l = fmaf(l, alpha, ls);
+
+    if (DBG) {
+      const int q = 32 * wl + col;
+      const size_t npad = (size_t)a.NB * kBlock;
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kt = 32 * sub + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const size_t key = (size_t)t * kBlock + kt;
+          dbg.s_int[q * npad + key] = kt >= nv ? INT32_MIN : (int32_t)S[sub][r];
+          dbg.p_code[q * npad + key] = (uint8_t)rr[sub][r];
+        }
+    }
+  }
+
   __device__ static void run(const Int4Args& a, const Int4Debug& dbg) {
-    __shared__ __align__(16) uint8_t sk[2][kBlock * KStride];
-    __shared__ __align__(16) uint8_t sv[2][D * VStride];
+    __shared__ __align__(16) uint8_t sk[2][kBlock * D];
+    __shared__ __align__(16) uint8_t sv[2][D * kBlock];
+    __shared__ float tau_lds[kTauTable];
     const int qb = DBG ? dbg.q_block : blockIdx.x;
     const int bh = DBG ? dbg.bh : blockIdx.y;
     if (!DBG && !a.run.test(bh)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int col = lane & 31, hh = lane >> 5;
-    const int NB = a.NB;
+    const int NB = a.NB, NT = NB;
     const size_t rows0 = (size_t)bh * NB * kBlock;
+    stage_tau(a.tau, tau_lds);
 
     v8i qf[KS];
     {
@@ -593,23 +661,28 @@ struct Int4F8Kernel {
     }
     const float qs = a.q_scale_l2[(size_t)bh * NB + qb];
 
-    uint4 kreg[BPT / 16], vreg[BPT / 16];
-    auto gload = [&](int t) {
-      const uint8_t* ks = a.k4 + (rows0 + (size_t)t * kBlock + (tid >> 1)) * D + (tid & 1) * BPT;
-      const uint8_t* vs = a.v4 + (((size_t)bh * NB + t) * D + tid / TPR) * 128 + (tid % TPR) * BPT;
+    // tile loads straight into LDS (no registers): wave w, instruction i fills
+    // chunks (NW i + w) * 64 + lane of the tile.  The per-lane byte offsets
+    // within a tile are fixed; only the tile base (uniform) moves.
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    const int wu = __builtin_amdgcn_readfirstlane(w);   // wave index in an SGPR (LDS window base)
+    uint32_t koff[LOADS], voff[LOADS];
 #pragma unroll
-      for (int i = 0; i < BPT / 16; ++i) {
-        kreg[i] = *(const uint4*)(ks + 16 * i);
-        vreg[i] = *(const uint4*)(vs + 16 * i);
-      }
-    };
-    auto lstore = [&](int buf) {
-      uint8_t* kd = sk[buf] + (tid >> 1) * KStride + (tid & 1) * BPT;
-      uint8_t* vd = sv[buf] + (tid / TPR) * VStride + (tid % TPR) * BPT;
+    for (int i = 0; i < LOADS; ++i) {
+      const int pc = (NW * i + w) * 64 + lane;             // physical chunk
+      const int krow = pc / KCPR, vrow = pc / 8;
+      koff[i] = krow * D + 16 * ((pc % KCPR) ^ kswz(krow));
+      voff[i] = vrow * kBlock + 16 * ((pc % 8) ^ vswz(vrow));
+    }
+    auto gload = [&](int t, int buf) {
+      const uint8_t* kb = a.k4 + (rows0 + (size_t)t * kBlock) * D;
+      const uint8_t* vb = a.v4 + ((size_t)bh * NB + t) * D * kBlock;
 #pragma unroll
-      for (int i = 0; i < BPT / 16; ++i) {
-        *(uint4*)(kd + 16 * i) = kreg[i];
-        *(uint4*)(vd + 16 * i) = vreg[i];
+      for (int i = 0; i < LOADS; ++i) {
+        __builtin_amdgcn_global_load_lds((const void*)(kb + koff[i]),
+                                         (lds_ptr)(sk[buf] + (NW * i + wu) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vb + voff[i]),
+                                         (lds_ptr)(sv[buf] + (NW * i + wu) * 1024), 16, 0, 0);
       }
     };
 
@@ -617,29 +690,36 @@ struct Int4F8Kernel {
     v16f O[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) O[db] = v16f{0.0f};
+    const int nv_last = a.N - (NT - 1) * kBlock;   // valid keys of the last tile
 
-    const int NT = NB;
-    gload(0);
-    lstore(0);
+    gload(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 #pragma unroll 1
-    for (int t = 0; t < NT - 1; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const int buf = t & 1;
+      v16f S[4];
       v8i P[2];
-      scores<false>(a, dbg, bh, t, sk[buf], qf, qs, m, l, u, O, P);
-      gload(t + 1);
-      pv(a, dbg, t, sv[buf], P, O);
-      lstore(buf ^ 1);
+      __builtin_amdgcn_s_setprio(1);
+      qk(sk[buf], qf, S);
+      __builtin_amdgcn_s_setprio(0);
+      int nv = kBlock;
+      if (t == NT - 1 && nv_last < kBlock) {
+        // opaque: nv_last is loop-invariant, and the 64 comparisons would be
+        // hoisted out of the loop and kept live (as SGPR masks) throughout it
+        nv = nv_last;
+        asm volatile("" : "+v"(nv));
+        mask_tail(S, nv);
+      }
+      softmax(a, dbg, tau_lds, bh, t, nv, S, qs, m, l, u, O, P);
+      // tile t+1 -> the other buffers, last read in tile t-1 (before the barrier)
+      if (t + 1 < NT) gload(t + 1, buf ^ 1);
+      __builtin_amdgcn_s_setprio(1);
+      pv(dbg, t, sv[buf], P, O);
+      __builtin_amdgcn_s_setprio(0);
+      // this thread's tile loads have landed in LDS before anyone passes the barrier
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-    }
-    {
-      const int t = NT - 1, buf = t & 1;
-      v8i P[2];
-      if ((a.N % kBlock) != 0)
-        scores<true>(a, dbg, bh, t, sk[buf], qf, qs, m, l, u, O, P);
-      else
-        scores<false>(a, dbg, bh, t, sk[buf], qf, qs, m, l, u, O, P);
-      pv(a, dbg, t, sv[buf], P, O);
     }
 
     l += __shfl_xor(l, 32, 64);
@@ -654,12 +734,12 @@ struct Int4F8Kernel {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = 32 * db + 8 * g + 4 * hh;
-          uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[db][4 * g] * il)) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[db][4 * g + 1] * il)) << 16);
-          uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[db][4 * g + 2] * il)) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[db][4 * g + 3] * il)) << 16);
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d0 = 32 * db + 8 * gq + 4 * hh;
+          uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[db][4 * gq] * il)) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[db][4 * gq + 1] * il)) << 16);
+          uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[db][4 * gq + 2] * il)) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(O[db][4 * gq + 3] * il)) << 16);
           *(uint2*)(orow + d0) = uint2{w0, w1};
         }
     }
@@ -667,7 +747,7 @@ struct Int4F8Kernel {
 };
 
 template <int D, bool DBG>
-__global__ __launch_bounds__(kThreads, 2) void k_int4_attn_f8(Int4Args a, Int4Debug dbg) {
+__global__ __launch_bounds__(256, 2) void k_int4_attn_f8(Int4Args a, Int4Debug dbg) {
   Int4F8Kernel<D, DBG>::run(a, dbg);
 }
 
@@ -676,14 +756,14 @@ hipError_t launch_int4_f8(int D, int BH, const Int4Args& a, const Int4Debug* dbg
   if (dbg == nullptr) {
     dim3 grid(a.NB, BH);
     if (D == 128)
-      hipLaunchKernelGGL((k_int4_attn_f8<128, false>), grid, dim3(kThreads), 0, st, a, none);
+      hipLaunchKernelGGL((k_int4_attn_f8<128, false>), grid, dim3(256), 0, st, a, none);
     else
-      hipLaunchKernelGGL((k_int4_attn_f8<64, false>), grid, dim3(kThreads), 0, st, a, none);
+      hipLaunchKernelGGL((k_int4_attn_f8<64, false>), grid, dim3(256), 0, st, a, none);
   } else {
     if (D == 128)
-      hipLaunchKernelGGL((k_int4_attn_f8<128, true>), dim3(1), dim3(kThreads), 0, st, a, *dbg);
+      hipLaunchKernelGGL((k_int4_attn_f8<128, true>), dim3(1), dim3(256), 0, st, a, *dbg);
     else
-      hipLaunchKernelGGL((k_int4_attn_f8<64, true>), dim3(1), dim3(kThreads), 0, st, a, *dbg);
+      hipLaunchKernelGGL((k_int4_attn_f8<64, true>), dim3(1), dim3(256), 0, st, a, *dbg);
   }
   return hipGetLastError();
 }
@@ -701,7 +781,7 @@ struct SweepArgs {
 // exact I (float), as u8 codes in byte lanes.
 template <bool F8>
 __device__ __forceinline__ v4i codes_of(const float (&I)[16], float c, float m, const SweepArgs& a,
-                                        const float* tau) {
+                                        const float* tau, const float* tau_lds) {
   float f[16], fm = -INFINITY, ls = 0.0f;
   const float sc = F8 ? 1.0f : 256.0f;
 #pragma unroll
@@ -711,8 +791,8 @@ __device__ __forceinline__ v4i codes_of(const float (&I)[16], float c, float m, 
   }
   if (F8) {
     const CodeCtx cx = make_ctx(c, m, a.log2_15, 1.0f);
-    float rr[16];
-    pcode16_f8<false>(f, fm, cx, tau, ls, 0xffffu, rr);
+    float rr[16], lsum = 0.0f;
+    pcode16_f8(f, fm, cx, tau_lds, lsum, rr);
     uint32_t pk[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -745,8 +825,11 @@ __global__ __launch_bounds__(256) void k_pcode_sweep(SweepArgs a) {
     I[r] = -__uint_as_float(in ? b : 0u);
     Ip[r] = -__uint_as_float(in ? bp : 0u);
   }
-  const v4i c = codes_of<F8>(I, 1.0f, 0.0f, a, a.tau);
-  const v4i cp = codes_of<F8>(Ip, 1.0f, 0.0f, a, a.tau);
+  __shared__ float tau_lds[kTauTable];
+  stage_tau(a.tau, tau_lds);
+  __syncthreads();
+  const v4i c = codes_of<F8>(I, 1.0f, 0.0f, a, a.tau, tau_lds);
+  const v4i cp = codes_of<F8>(Ip, 1.0f, 0.0f, a, a.tau, tau_lds);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const uint32_t cc = ((uint32_t)c[r >> 2] >> (8 * (r & 3))) & 0xffu;
@@ -795,7 +878,10 @@ __global__ __launch_bounds__(256) void k_pcode_eval(EvalArgs a) {
   float I[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) I[r] = (float)a.I[base + r];
-  *(v4i*)(a.codes + base) = codes_of<F8>(I, a.c, a.m, a.s, a.s.tau);
+  __shared__ float tau_lds[kTauTable];
+  stage_tau(a.s.tau, tau_lds);
+  __syncthreads();
+  *(v4i*)(a.codes + base) = codes_of<F8>(I, a.c, a.m, a.s, a.s.tau, tau_lds);
 }
 
 hipError_t launch_pcode_eval(bool f8, const int32_t* I, uint32_t n, float c, float m,
