@@ -105,8 +105,6 @@ def main():
     prep = R.PreparedDevice(shape, with_rope=True)
     o = torch.empty((B, H, N, D), dtype=torch.float16, device="cuda")
     BH = B * H
-    qr = prep.view("q_rope", torch.float16, BH * N * D)
-    kr = prep.view("k_rope", torch.float16, BH * N * D)
     n_fb = int(mask.sum())
     print(f"[bench] inputs ready in {time.time() - t0:.1f}s: {cfg.name} B={B} H={H} N={N} D={D} "
           f"fallback heads={n_fb}", file=sys.stderr, flush=True)
@@ -118,7 +116,7 @@ def main():
         R.int4_fwd(shape, prep, o, mask=mask)
         if ev: ev[2].record()
         if n_fb:
-            R.fp16_fwd(shape, qr, kr, vd, o, head_select=mask)
+            R.fp16_fwd(shape, prep, o, head_select=mask)
         if ev: ev[3].record()
 
     for _ in range(args.warmup):
@@ -193,10 +191,10 @@ def main():
         all_fb = np.ones(BH, np.uint8)
         R.prepare_qkv(shape, qd, kd, vd, rr, prep, all_fb)
         e0.record()
-        R.fp16_fwd(shape, qr, kr, vd, o, head_select=all_fb)
+        R.fp16_fwd(shape, prep, o, head_select=all_fb)
         e1.record()
         torch.cuda.synchronize()
-        R.fp16_fwd(shape, qr, kr, vd, o, head_select=all_fb)
+        R.fp16_fwd(shape, prep, o, head_select=all_fb)
         e2 = torch.cuda.Event(enable_timing=True)
         e2.record()
         torch.cuda.synchronize()
@@ -205,7 +203,7 @@ def main():
         kernels["fp16_attn_f16_peak_frac"] = round(ops / (f16_ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4)
         kernels["int4_vs_fp16_kernel_speedup"] = round(f16_ms / k2_ms, 3) if n_int4 == BH else None
         print(f"[bench] fp16 all heads {f16_ms:.3f} ms", file=sys.stderr, flush=True)
-    del qd, kd, vd, prep, o, qr, kr
+    del qd, kd, vd, prep, o
     torch.cuda.empty_cache()
 
     mixed = None

@@ -119,15 +119,21 @@ typedef enum rotattn_layout {
  *  q_scale_l2, k_scale, v_scale: [B*H][NB] fp32 block scales (amax/7).
  *          q_scale_l2 = fl(q_scale * kappa), kappa = fl32(log2(e)/sqrt(D)), so
  *          that 2^(I * q_scale_l2 * k_scale) = exp(QK^T / sqrt(D)).
- *  q_rope, k_rope: [B*H][N][D] fp16 RoPE'd (not rotated, not quantized) Q/K,
- *          written for fallback heads only; may be NULL when no head falls
- *          back.
+ *  q_rope, k_rope: [B*H][N_pad][D] fp16 RoPE'd (not rotated, not quantized)
+ *          Q/K, rows N..N_pad-1 zero.
+ *  v_t:    [B*H][N_pad/64][D][64] fp16: V transposed per 64-key tile, row d
+ *          holding the tile's keys in the operand order of the fp16 P.V
+ *          product: position 32s + 4c + i (s, i in {0..1}, {0..3}, c < 8) is
+ *          key 32s + 4c' + i, c' = c with its two low bits swapped; keys >= N
+ *          zero.
+ *          q_rope, k_rope and v_t are written for fallback heads only and may
+ *          be NULL when no head falls back.
  */
 typedef struct rotattn_prepared {
   int32_t layout;
   uint8_t *q4, *k4, *v4;
   float *q_scale_l2, *k_scale, *v_scale;
-  uint16_t *q_rope, *k_rope;
+  uint16_t *q_rope, *k_rope, *v_t;
   double *rot64;
 } rotattn_prepared;
 
@@ -185,7 +191,8 @@ int rotattn_prepared_carve(const rotattn_shape* s, void* base, size_t bytes,
  * when the mask is NULL): 3D RoPE on Q and K in fp32, the partition-wise
  * rotation (fp64 accumulation, one rounding to fp32), per-block symmetric
  * INT4 quantization of Q, K, V, stored in out->layout.  For a fallback head:
- * RoPE'd fp16 Q'/K' into out->q_rope / out->k_rope only.
+ * RoPE'd fp16 Q'/K' into out->q_rope / out->k_rope and V^T tiles into
+ * out->v_t only.
  */
 int rotattn_prepare_qkv(const rotattn_shape* s, const uint16_t* q,
                         const uint16_t* k, const uint16_t* v,
@@ -209,15 +216,15 @@ int rotattn_int4_fwd(const rotattn_shape* s, const rotattn_prepared* p,
 /*
  * FP16 FlashAttention: O = softmax(Q'K'^T / sqrt(D)) V on fp16 MFMA with fp32
  * softmax and accumulation, for the heads with head_select_host[...] != 0
- * (all heads when NULL).  q_rope, k_rope, v, o: [B][H][N][D] fp16.
+ * (all heads when NULL).  Reads p->q_rope, p->k_rope and p->v_t as written by
+ * rotattn_prepare_qkv for those heads (fallback heads); o: [B][H][N][D] fp16.
  */
-int rotattn_fp16_fwd(const rotattn_shape* s, const uint16_t* q_rope,
-                     const uint16_t* k_rope, const uint16_t* v,
+int rotattn_fp16_fwd(const rotattn_shape* s, const rotattn_prepared* p,
                      const uint8_t* head_select_host, uint16_t* o,
                      hipStream_t stream);
 
 /* Workspace bytes for rotattn_mixed_fwd (a FP8-layout rotattn_prepared with
- * fp16 Q'/K'). */
+ * the fp16 fallback buffers). */
 size_t rotattn_workspace_bytes(const rotattn_shape* s);
 
 /*

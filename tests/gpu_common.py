@@ -58,6 +58,22 @@ def fp8_vt_blocks(codes: np.ndarray, N_pad: int) -> np.ndarray:
     return np.stack(out)
 
 
+def fp16_vt_tiles(v: np.ndarray, N_pad: int) -> np.ndarray:
+    """fp16 V [N, D] -> [N_pad/64, D, 64] V^T tiles in the fp16 P.V operand
+    order: position 32s + 4c + i holds key 32s + 4c' + i, c' = c with bits 0
+    and 1 swapped; keys >= N zero (bit patterns as uint16)."""
+    N, D = v.shape
+    full = np.zeros((N_pad, D), np.uint16)
+    full[:N] = v.view(np.uint16)
+    perm = np.empty(64, np.int64)
+    for pos in range(64):
+        s_, pc, i = pos // 32, (pos % 32) // 4, pos % 4
+        c = (pc & 4) | ((pc & 1) << 1) | ((pc >> 1) & 1)
+        perm[pos] = 32 * s_ + 4 * c + i
+    assert sorted(perm) == list(range(64))
+    return np.stack([full[64 * t:64 * (t + 1)][perm].T for t in range(N_pad // 64)])
+
+
 def pack_vt_blocks(codes: np.ndarray, N_pad: int) -> np.ndarray:
     """V codes [N, D] -> [NB, D, 64]: per 128-token block, transposed, packed along keys."""
     N, D = codes.shape
@@ -110,7 +126,10 @@ class Run:
         for f in ("q_scale_l2", "k_scale", "v_scale"):
             out[f] = p.view(f, torch.float32, BH * NB).cpu().numpy().reshape(BH, NB)
         for f in ("q_rope", "k_rope"):
-            out[f] = p.view(f, torch.int16, BH * N * D).cpu().numpy().view(np.uint16).reshape(BH, N, D)
+            out[f] = (p.view(f, torch.int16, BH * self.N_pad * D).cpu().numpy().view(np.uint16)
+                      .reshape(BH, self.N_pad, D))
+        out["v_t"] = (p.view("v_t", torch.int16, BH * self.N_pad * D).cpu().numpy().view(np.uint16)
+                      .reshape(BH, self.N_pad // 64, D, 64))
         return out
 
     def empty_out(self):

@@ -55,7 +55,7 @@ def test_entry_points_reject_bad_arguments_before_launch():
     nul = C.c_void_p(0)
     assert L.rotattn_prepare_qkv(C.byref(s), nul, nul, nul, None, nul, None, nul) == -1
     assert L.rotattn_int4_fwd(C.byref(s), None, nul, nul, None, nul) == -1
-    assert L.rotattn_fp16_fwd(C.byref(s), nul, nul, nul, nul, nul, nul) == -1
+    assert L.rotattn_fp16_fwd(C.byref(s), None, nul, nul, nul) == -1
     assert L.rotattn_mixed_fwd(C.byref(s), nul, nul, nul, None, nul, nul, 0, nul, nul) == -1
     bad = R.make_shape(1, 2, (2, 4, 4), 64, (24, 20, 22))
     assert L.rotattn_mixed_fwd(C.byref(bad), nul, nul, nul, None, nul, nul, 0, nul, nul) == -2
@@ -81,14 +81,16 @@ def test_prepared_layout_sizes(layout, code_bytes):
     n1 = R.lib().rotattn_prepared_bytes(C.byref(s), 1, layout)
     codes = 40 * NB * 128 * code_bytes
     assert n0 >= 3 * codes + 3 * 40 * NB * 4
-    assert n1 - n0 >= 2 * 40 * 75600 * 128 * 2
+    # fallback buffers: q_rope, k_rope and v_t, each [B*H][N_pad][D] fp16
+    assert n1 - n0 >= 3 * 40 * NB * 128 * 128 * 2
     if layout == R.LAYOUT_FP8:
         assert R.workspace_bytes(s) == n1
     p = R.Prepared()
     assert R.lib().rotattn_prepared_carve(C.byref(s), C.c_void_p(1 << 20), n1, 1, layout,
                                           C.byref(p)) == 0
     assert p.layout == layout
-    addrs = [p.q4, p.k4, p.v4, p.q_scale_l2, p.k_scale, p.v_scale, p.rot64, p.q_rope, p.k_rope]
+    addrs = [p.q4, p.k4, p.v4, p.q_scale_l2, p.k_scale, p.v_scale, p.rot64, p.q_rope, p.k_rope,
+             p.v_t]
     assert all(a % 256 == 0 for a in addrs) and addrs == sorted(addrs)
     assert p.k4 - p.q4 >= codes and max(addrs) < (1 << 20) + n1
 

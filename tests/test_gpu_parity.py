@@ -12,7 +12,8 @@ import pytest
 import oracle as O
 from video_diffusion_transformers_amd import synth
 
-from gpu_common import (Run, check_out, fp8_bytes, fp8_vt_blocks, pack_rows, pack_vt_blocks,
+from gpu_common import (Run, check_out, fp8_bytes, fp8_vt_blocks, fp16_vt_tiles, pack_rows,
+                        pack_vt_blocks,
                         torch_cuda)
 
 pytestmark = pytest.mark.gpu
@@ -99,8 +100,12 @@ def test_prologue_bit_exact(name, layout):
         fb = bool(run.mask[bh])
         p = run.oracle_prep(bh, fallback=fb)
         if fb:
-            assert np.array_equal(g["q_rope"][bh], p["q_rope"].view(np.uint16))
-            assert np.array_equal(g["k_rope"][bh], p["k_rope"].view(np.uint16))
+            N = run.cfg.N
+            for t in ("q", "k"):
+                assert np.array_equal(g[f"{t}_rope"][bh][:N], p[f"{t}_rope"].view(np.uint16))
+                assert not g[f"{t}_rope"][bh][N:].any()
+            v = run.host[2].reshape(run.cfg.BH, N, run.cfg.D)[bh]
+            assert np.array_equal(g["v_t"][bh], fp16_vt_tiles(v, run.N_pad)), (name, bh, "v_t")
             continue
         f8 = layout == "fp8"
         for t in ("q", "k"):
@@ -198,11 +203,8 @@ def test_fp16_fallback_within_tolerance(name):
     run.prepare(mask=all_fb)
     o = run.empty_out()
     from video_diffusion_transformers_amd import rotattn as R
-    p = run.prep.struct
     BH, N, D = run.cfg.BH, run.cfg.N, run.cfg.D
-    qr = run.prep.view("q_rope", torch.float16, BH * N * D)
-    kr = run.prep.view("k_rope", torch.float16, BH * N * D)
-    R.fp16_fwd(run.shape, qr, kr, run.v, o, head_select=all_fb)
+    R.fp16_fwd(run.shape, run.prep, o, head_select=all_fb)
     torch.cuda.synchronize()
     og = o.reshape(BH, N, D).cpu().numpy()
     for bh in HEADS[name]:

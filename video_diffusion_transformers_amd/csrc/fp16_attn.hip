@@ -1,15 +1,18 @@
 // K3: FP16 FlashAttention forward on gfx950 -- RotateAttention's selective
 // FP16 fallback (RotateAttention page, Abstract: accuracy-sensitive attention
-// runs in FP16 instead of INT4).  Inputs are the RoPE'd fp16 Q', K' (no
-// rotation, no quantization) and fp16 V; O = softmax(Q'K'^T/sqrt(D)) V.
+// runs in FP16 instead of INT4).  Inputs are the prologue's fallback buffers:
+// RoPE'd fp16 Q', K' (no rotation, no quantization; rows padded to N_pad with
+// zeros) and V^T per 64-key tile in the operand order of the P.V product.
+// O = softmax(Q'K'^T/sqrt(D)) V.
 //
-// One work-group = 4 waves x 32 queries; 64-key tiles staged through LDS
-// (double buffered, one barrier per tile).  S^T = K Q'^T on
-// v_mfma_f32_32x32x16_f16, fp32 online softmax in the log2 domain (kappa =
-// log2(e)/sqrt(D)), P rounded to fp16 in registers and used directly as the
-// P^T operand of O^T = V^T P^T (same orientation trick as the INT4 kernel).
-// V is transposed into LDS while staging, with the key order of each 32-key
-// subtile permuted to match the P^T operand layout.
+// One work-group = 4 waves x 32 queries, two work-groups per CU.  Per 64-key
+// tile: S^T = K Q'^T on v_mfma_f32_32x32x16_f16 (each lane then holds one
+// query's scores in the layout of the P^T operand), fp32 online softmax in the
+// log2 domain (kappa = log2(e)/sqrt(D)), P rounded to fp16 in registers,
+// O^T += V^T P^T.  K and V^T tiles go straight from HBM into XOR-swizzled LDS
+// (global_load_lds, 64-bank layout), double buffered; the next tile is
+// requested after the softmax, while P.V runs; MFMA blocks run at raised wave
+// priority.
 #include <math.h>
 
 #include "rotattn_internal.h"
@@ -17,42 +20,71 @@
 namespace rotattn {
 
 constexpr int kFThreads = 256;
-constexpr int kKT = 64;                   // keys per tile
-constexpr int kFVStride = 2 * kKT + 16;   // V^T row in LDS: 64 keys fp16 + 16 bytes
+constexpr int kKT = 64;   // keys per tile
 
 template <int D>
 struct Fp16Kernel {
-  static constexpr int KS = D / 16;         // k-steps of 16 channels
-  static constexpr int DB = D / 32;
-  static constexpr int KStride = 2 * D + 16;
-  static constexpr int KPT = D / 2;         // K tile bytes per thread (64 keys x 2D bytes / 256)
-  static constexpr int VITEMS = 16 * (D / 8);   // (4-key chunk, 8-channel chunk) items per tile
+  static constexpr int KS = D / 16;              // k-steps of 16 channels for QK^T
+  static constexpr int DB = D / 32;              // 32-channel blocks of O^T
+  static constexpr int NW = kFThreads / 64;
+  static constexpr int KRB = 2 * D;              // bytes per K row
+  static constexpr int KCPR = KRB / 16;          // 16-byte chunks per K row
+  static constexpr int KRPB = 256 / KRB;         // K rows per 256 bytes (one bank row)
+  static constexpr int TCH = kKT * KRB / 16;     // chunks per tile (K and V^T alike)
+  static constexpr int LOADS = TCH / kFThreads;  // loads per thread per tile and tensor
+  static_assert(TCH % kFThreads == 0 && D * 128 / 16 == TCH, "whole waves per tile");
 
-  template <bool TAIL>
-  __device__ __forceinline__ static void tile(const Fp16Args& a, int t, const uint8_t* sk,
-                                              const uint8_t* sv, const v8h (&qf)[KS], float& m,
-                                              float& l, v16f (&O)[DB]) {
+  // XOR swizzle of the 16-byte chunks of a row: the 16 rows read together by
+  // a ds_read_b128 land on 16 different chunk columns of the 64 banks
+  __device__ __forceinline__ static int kswz(int row) { return (row / KRPB) & (KCPR - 1); }
+  __device__ __forceinline__ static int vswz(int row) { return (row >> 1) & 7; }   // 128-byte rows
+
+  __device__ __forceinline__ static v8h ld16(const uint8_t* p) { return *(const v8h*)p; }
+
+  __device__ __forceinline__ static void qk(const uint8_t* sk, const v8h (&qf)[KS], v16f (&S)[2]) {
     const int lane = threadIdx.x & 63;
     const int col = lane & 31, hh = lane >> 5;
-    v16f S[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
+      const int row = 32 * sub + col;
       S[sub] = v16f{0.0f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const v8h kf = *(const v8h*)(sk + (32 * sub + col) * KStride + 2 * (16 * ks + 8 * hh));
-        S[sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], S[sub], 0, 0, 0);
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        S[sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            ld16(sk + row * KRB + 16 * ((2 * ks + hh) ^ kswz(row))), qf[ks], S[sub], 0, 0, 0);
     }
-    if (TAIL) {
-      const int nv = a.N - t * kKT;
+  }
+
+  __device__ __forceinline__ static void pv(const uint8_t* sv, const v8h (&P)[2][2],
+                                            v16f (&O)[DB]) {
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int row = 32 * db + col;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * sub + 8 * (r >> 2) + 4 * hh + (r & 3) >= nv) S[sub][r] = -INFINITY;
+        for (int s = 0; s < 2; ++s)
+          O[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              ld16(sv + row * 128 + 16 * ((4 * sub + 2 * s + hh) ^ vswz(row))), P[sub][s], O[db],
+              0, 0, 0);
     }
-    float mx = -INFINITY;
+  }
+
+  // Keys >= nv (last tile only) get S = -inf.
+  __device__ __forceinline__ static void mask_tail(v16f (&S)[2], int nv) {
+    const int hh = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (32 * sub + 8 * (r >> 2) + 4 * hh + (r & 3) >= nv) S[sub][r] = -INFINITY;
+  }
+
+  __device__ __forceinline__ static void softmax(const Fp16Args& a, v16f (&S)[2], float& m,
+                                                 float& l, v16f (&O)[DB], v8h (&P)[2][2]) {
+    float mx = S[0][0];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -67,8 +99,7 @@ struct Fp16Kernel {
 #pragma unroll
         for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
     }
-    v8h P[2][2];
-    float ls = 0.0f;   // tile sum first, then into the running l (see the INT4 kernel)
+    float ls = 0.0f;   // tile sum first, then into the running l
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -78,93 +109,45 @@ struct Fp16Kernel {
         P[sub][r >> 3][r & 7] = (_Float16)p;
       }
     l = fmaf(l, alpha, ls);
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const v8h vf =
-              *(const v8h*)(sv + (32 * db + col) * kFVStride + 2 * (32 * sub + 16 * s + 8 * hh));
-          O[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, P[sub][s], O[db], 0, 0, 0);
-        }
   }
 
   __device__ static void run(const Fp16Args& a) {
-    __shared__ __align__(16) uint8_t sk[2][kKT * KStride];
-    __shared__ __align__(16) uint8_t sv[2][D * kFVStride];
+    __shared__ __align__(16) uint8_t sk[2][kKT * KRB];
+    __shared__ __align__(16) uint8_t sv[2][D * 128];
     const int qb = blockIdx.x, bh = blockIdx.y;
     if (!a.run.test(bh)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int col = lane & 31, hh = lane >> 5;
-    const int N = a.N;
-    const size_t head = (size_t)bh * N;   // first token row of this head
+    const int N = a.N, NT = (N + kKT - 1) / kKT;
+    const size_t head_pad = (size_t)bh * a.NB * kBlock;   // first padded row of this head
 
     v8h qf[KS];
     {
-      const int query = qb * kBlock + 32 * w + col;
-      const uint16_t* qrow = a.q + (head + (query < N ? query : 0)) * D;
+      const uint16_t* qrow = a.q + (head_pad + (size_t)qb * kBlock + 32 * w + col) * D;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        uint4 p = query < N ? *(const uint4*)(qrow + 16 * ks + 8 * hh) : uint4{0, 0, 0, 0};
-        qf[ks] = __builtin_bit_cast(v8h, p);
-      }
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const v8h*)(qrow + 16 * ks + 8 * hh);
     }
 
-    uint4 kreg[KPT / 16];
-    uint4 vreg[4 * ((VITEMS + kFThreads - 1) / kFThreads)];
-    auto gload = [&](int t) {
-      {
-        const int key = t * kKT + (tid >> 2);
-        const uint8_t* src = (const uint8_t*)(a.k + (head + (key < N ? key : 0)) * D) + (tid & 3) * KPT;
+    // per-lane byte offsets of the tile loads (fixed), the tile base moves
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    uint32_t koff[LOADS], voff[LOADS];
 #pragma unroll
-        for (int i = 0; i < KPT / 16; ++i)
-          kreg[i] = key < N ? *(const uint4*)(src + 16 * i) : uint4{0, 0, 0, 0};
-      }
+    for (int i = 0; i < LOADS; ++i) {
+      const int pc = (NW * i + w) * 64 + lane;   // physical chunk
+      const int krow = pc / KCPR, vrow = pc / 8;
+      koff[i] = krow * KRB + 16 * ((pc % KCPR) ^ kswz(krow));
+      voff[i] = vrow * 128 + 16 * ((pc % 8) ^ vswz(vrow));
+    }
+    auto gload = [&](int t, int buf) {
+      const uint8_t* kb = (const uint8_t*)(a.k + (head_pad + (size_t)t * kKT) * D);
+      const uint8_t* vb = (const uint8_t*)(a.v_t + (head_pad + (size_t)t * kKT) * D);
 #pragma unroll
-      for (int it = 0; it < (VITEMS + kFThreads - 1) / kFThreads; ++it) {
-        const int item = tid + it * kFThreads;
-        if (item < VITEMS) {
-          const int dc = item % (D / 8), qc = item / (D / 8);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = t * kKT + 4 * qc + i;
-            vreg[4 * it + i] = key < N ? *(const uint4*)(a.v + (head + key) * D + 8 * dc)
-                                       : uint4{0, 0, 0, 0};
-          }
-        }
-      }
-    };
-    auto lstore = [&](int buf) {
-      {
-        uint8_t* dst = sk[buf] + (tid >> 2) * KStride + (tid & 3) * KPT;
-#pragma unroll
-        for (int i = 0; i < KPT / 16; ++i) *(uint4*)(dst + 16 * i) = kreg[i];
-      }
-#pragma unroll
-      for (int it = 0; it < (VITEMS + kFThreads - 1) / kFThreads; ++it) {
-        const int item = tid + it * kFThreads;
-        if (item < VITEMS) {
-          const int dc = item % (D / 8), qc = item / (D / 8);
-          // 4-key chunk c of a 32-key subtile goes to chunk position with its
-          // two low bits swapped: the P^T operand of k-step s, lane half hh
-          // holds keys 16s + 8(j/4) + 4hh + j%4, j = 0..7.
-          const int c = qc & 7;
-          const int pos = (qc & ~7) | (c & 4) | ((c & 1) << 1) | ((c >> 1) & 1);
-          const uint32_t* r0 = (const uint32_t*)&vreg[4 * it];
-          const uint32_t* r1 = (const uint32_t*)&vreg[4 * it + 1];
-          const uint32_t* r2 = (const uint32_t*)&vreg[4 * it + 2];
-          const uint32_t* r3 = (const uint32_t*)&vreg[4 * it + 3];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint2 even{__builtin_amdgcn_perm(r1[e], r0[e], 0x05040100u),
-                             __builtin_amdgcn_perm(r3[e], r2[e], 0x05040100u)};
-            const uint2 odd{__builtin_amdgcn_perm(r1[e], r0[e], 0x07060302u),
-                            __builtin_amdgcn_perm(r3[e], r2[e], 0x07060302u)};
-            *(uint2*)(sv[buf] + (8 * dc + 2 * e) * kFVStride + 8 * pos) = even;
-            *(uint2*)(sv[buf] + (8 * dc + 2 * e + 1) * kFVStride + 8 * pos) = odd;
-          }
-        }
+      for (int i = 0; i < LOADS; ++i) {
+        __builtin_amdgcn_global_load_lds((const void*)(kb + koff[i]),
+                                         (lds_ptr)(sk[buf] + (NW * i + wu) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vb + voff[i]),
+                                         (lds_ptr)(sv[buf] + (NW * i + wu) * 1024), 16, 0, 0);
       }
     };
 
@@ -172,31 +155,42 @@ struct Fp16Kernel {
     v16f O[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) O[db] = v16f{0.0f};
-    const int NT = (N + kKT - 1) / kKT;
-    gload(0);
-    lstore(0);
+    const int nv_last = N - (NT - 1) * kKT;
+
+    gload(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    // full tiles in the loop, the last (possibly ragged) tile peeled off
 #pragma unroll 1
-    for (int t = 0; t < NT - 1; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const int buf = t & 1;
-      gload(t + 1);
-      tile<false>(a, t, sk[buf], sv[buf], qf, m, l, O);
-      lstore(buf ^ 1);
+      v16f S[2];
+      v8h P[2][2];
+      __builtin_amdgcn_s_setprio(1);
+      qk(sk[buf], qf, S);
+      __builtin_amdgcn_s_setprio(0);
+      if (t == NT - 1 && nv_last < kKT) {
+        // opaque: nv_last is loop-invariant, and the comparisons would be
+        // hoisted out of the loop and kept live as SGPR masks
+        int nv = nv_last;
+        asm volatile("" : "+v"(nv));
+        mask_tail(S, nv);
+      }
+      softmax(a, S, m, l, O, P);
+      // tile t+1 -> the other buffers, last read in tile t-1 (before the barrier)
+      if (t + 1 < NT) gload(t + 1, buf ^ 1);
+      __builtin_amdgcn_s_setprio(1);
+      pv(sv[buf], P, O);
+      __builtin_amdgcn_s_setprio(0);
+      // this thread's tile loads have landed in LDS before anyone passes the barrier
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
-    {
-      const int t = NT - 1, buf = t & 1;
-      if ((N % kKT) != 0)
-        tile<true>(a, t, sk[buf], sv[buf], qf, m, l, O);
-      else
-        tile<false>(a, t, sk[buf], sv[buf], qf, m, l, O);
-    }
+
     l += __shfl_xor(l, 32, 64);
     const int query = qb * kBlock + 32 * w + col;
     if (query < N) {
       const float il = 1.0f / l;
-      uint16_t* orow = a.o + (head + query) * D;
+      uint16_t* orow = a.o + ((size_t)bh * N + query) * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -218,7 +212,7 @@ __global__ __launch_bounds__(kFThreads, 2) void k_fp16_attn(Fp16Args a) {
 }
 
 hipError_t launch_fp16(int D, int BH, const Fp16Args& a, hipStream_t st) {
-  dim3 grid((a.N + kBlock - 1) / kBlock, BH);
+  dim3 grid(a.NB, BH);
   if (D == 128)
     hipLaunchKernelGGL(k_fp16_attn<128>, grid, dim3(kFThreads), 0, st, a);
   else

@@ -278,16 +278,42 @@ __device__ __forceinline__ void load_tile(const uint16_t* src, int n0, int N, ui
   }
 }
 
-// Coalesced store of the staged fp16 rows of the valid tokens.
+// Coalesced store of all 128 staged fp16 rows (rows past N are zero) into a
+// padded [N_pad][D] buffer.
 template <int D>
-__device__ __forceinline__ void store_tile(uint16_t* dst, int n0, int N, const uint32_t* xs) {
+__device__ __forceinline__ void store_tile_all(uint16_t* dst, int n0, const uint32_t* xs) {
   constexpr int kChunks = D / 8;
   constexpr int kRS = D / 2 + 1;
   for (int i = threadIdx.x; i < kBlock * kChunks; i += kThreads) {
     const int r = i / kChunks, c = i % kChunks;
-    if (n0 + r >= N) continue;
     const uint32_t* s_ = xs + r * kRS + 4 * c;
     *(uint4*)(dst + (size_t)(n0 + r) * D + 8 * c) = uint4{s_[0], s_[1], s_[2], s_[3]};
+  }
+}
+
+// The block's staged fp16 V rows (rows past N zero) -> its two 64-key V^T
+// tiles, [D][64] each, in the operand order of the fp16 P.V product: position
+// 32s + 4c + i holds key 32s + 4c' + i, c' = c with bits 0 and 1 swapped.
+template <int D>
+__device__ __forceinline__ void store_vt_tiles(const uint32_t* xs, uint16_t* dst) {
+  constexpr int kRS = D / 2 + 1;
+  for (int item = threadIdx.x; item < 2 * D * 8; item += kThreads) {
+    const int tl = item / (D * 8), d = (item / 8) % D, j = item % 8;   // 8 positions per item
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      uint32_t hv[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int pos = 8 * j + e + f;                   // 0..63
+        const int s = pos >> 5, pc = (pos >> 2) & 7, i = pos & 3;
+        const int c = (pc & 4) | ((pc & 1) << 1) | ((pc >> 1) & 1);
+        const int key = 64 * tl + 32 * s + 4 * c + i;    // token within the block
+        hv[f] = (xs[key * kRS + (d >> 1)] >> (16 * (d & 1))) & 0xffffu;
+      }
+      w[e / 2] = hv[0] | (hv[1] << 16);
+    }
+    *(uint4*)(dst + ((size_t)tl * D + d) * 64 + 8 * j) = uint4{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -402,8 +428,9 @@ __device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* sta
   if (threadIdx.x == 0) a.v_scale[(size_t)bh * a.NB + blk] = scale;
 }
 
-// Fallback head: RoPE'd fp16 Q and K only, one token per lane, wave pair a on
-// partition a.
+// Fallback head: RoPE'd fp16 Q and K into the padded q_rope/k_rope rows, one
+// token per lane, wave pair a on partition a; then V^T tiles for the fp16
+// attention.
 template <int D, int D0, int D1>
 __device__ __forceinline__ void prologue_fallback(const PrologueArgs& a, uint32_t* stage, int blk,
                                                   int bh) {
@@ -419,6 +446,7 @@ __device__ __forceinline__ void prologue_fallback(const PrologueArgs& a, uint32_
   const float* cos_a = part == 0 ? a.cos_t : (part == 1 ? a.cos_h : a.cos_w);
   const float* sin_a = part == 0 ? a.sin_t : (part == 1 ? a.sin_h : a.sin_w);
   const size_t head_tok = (size_t)bh * a.N;
+  const size_t head_pad = (size_t)bh * a.NB * kBlock;
   uint32_t* xrow = stage + nl * kRS;
   // tables are read for every lane; clamp the position of a padding token
   const int pos_c = n < a.N ? pos : 0;
@@ -431,9 +459,12 @@ __device__ __forceinline__ void prologue_fallback(const PrologueArgs& a, uint32_
     else
       rope_only_part<D1>(xrow, cos_a, sin_a, pos_c, off);
     __syncthreads();
-    store_tile<D>((s == 0 ? a.q_rope : a.k_rope) + head_tok * D, n0, a.N, stage);
+    store_tile_all<D>((s == 0 ? a.q_rope : a.k_rope) + head_pad * D, n0, stage);
     __syncthreads();
   }
+  load_tile<D>(a.v + head_tok * D, n0, a.N, stage);
+  __syncthreads();
+  store_vt_tiles<D>(stage, a.v_t + (head_pad + n0) * D);
 }
 
 // 3 waves per SIMD: two 6-wave work-groups per CU, so that one group's MFMA

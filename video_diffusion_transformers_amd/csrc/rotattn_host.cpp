@@ -119,8 +119,9 @@ size_t rotattn_prepared_bytes(const rotattn_shape* s, int with_rope, int layout)
   const size_t per_code = layout == ROTATTN_LAYOUT_FP8 ? 2 : 1;   // half-bytes per code
   const size_t packed = align_up(BH * NB * kBlock * D * per_code / 2);
   const size_t scales = align_up(BH * NB * sizeof(float));
-  const size_t rope = with_rope ? align_up(BH * (size_t)s->N * D * 2) : 0;
-  return 3 * packed + 3 * scales + kRotBytes + 2 * rope;
+  // fallback buffers: q_rope, k_rope, v_t, each [B*H][N_pad][D] fp16
+  const size_t rope = with_rope ? align_up(BH * NB * kBlock * D * 2) : 0;
+  return 3 * packed + 3 * scales + kRotBytes + 3 * rope;
 }
 
 int rotattn_prepared_carve(const rotattn_shape* s, void* base, size_t bytes, int with_rope,
@@ -135,7 +136,7 @@ int rotattn_prepared_carve(const rotattn_shape* s, void* base, size_t bytes, int
   const size_t per_code = layout == ROTATTN_LAYOUT_FP8 ? 2 : 1;
   const size_t packed = align_up(BH * NB * kBlock * D * per_code / 2);
   const size_t scales = align_up(BH * NB * sizeof(float));
-  const size_t rope = align_up(BH * (size_t)s->N * D * 2);
+  const size_t rope = align_up(BH * NB * kBlock * D * 2);
   uint8_t* p = (uint8_t*)base;
   out->layout = layout;
   out->q4 = p; p += packed;
@@ -148,9 +149,11 @@ int rotattn_prepared_carve(const rotattn_shape* s, void* base, size_t bytes, int
   if (with_rope) {
     out->q_rope = (uint16_t*)p; p += rope;
     out->k_rope = (uint16_t*)p; p += rope;
+    out->v_t = (uint16_t*)p; p += rope;
   } else {
     out->q_rope = nullptr;
     out->k_rope = nullptr;
+    out->v_t = nullptr;
   }
   return ROTATTN_OK;
 }
@@ -176,8 +179,9 @@ int rotattn_prepare_qkv(const rotattn_shape* s, const uint16_t* q, const uint16_
     if (!aligned16(out->q4) || !aligned16(out->k4) || !aligned16(out->v4)) return ROTATTN_E_ALIGN;
   }
   if (n_fb > 0) {
-    if (!out->q_rope || !out->k_rope) return ROTATTN_E_NULL;
-    if (!aligned16(out->q_rope) || !aligned16(out->k_rope)) return ROTATTN_E_ALIGN;
+    if (!out->q_rope || !out->k_rope || !out->v_t) return ROTATTN_E_NULL;
+    if (!aligned16(out->q_rope) || !aligned16(out->k_rope) || !aligned16(out->v_t))
+      return ROTATTN_E_ALIGN;
   }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return ROTATTN_E_ALIGN;
 
@@ -192,7 +196,7 @@ int rotattn_prepare_qkv(const rotattn_shape* s, const uint16_t* q, const uint16_
   a.rot64 = out->rot64;
   a.q4 = out->q4; a.k4 = out->k4; a.v4 = out->v4;
   a.q_scale_l2 = out->q_scale_l2; a.k_scale = out->k_scale; a.v_scale = out->v_scale;
-  a.q_rope = out->q_rope; a.k_rope = out->k_rope;
+  a.q_rope = out->q_rope; a.k_rope = out->k_rope; a.v_t = out->v_t;
   a.N = s->N;
   a.NB = nblocks(s);
   a.grid_h = s->grid_h;
@@ -248,20 +252,21 @@ int rotattn_int4_fwd(const rotattn_shape* s, const rotattn_prepared* p,
   return ROTATTN_OK;
 }
 
-int rotattn_fp16_fwd(const rotattn_shape* s, const uint16_t* q_rope, const uint16_t* k_rope,
-                     const uint16_t* v, const uint8_t* head_select_host, uint16_t* o,
-                     hipStream_t stream) {
+int rotattn_fp16_fwd(const rotattn_shape* s, const rotattn_prepared* p,
+                     const uint8_t* head_select_host, uint16_t* o, hipStream_t stream) {
   const int st = rotattn_validate(s);
   if (st != ROTATTN_OK) return st;
-  if (!q_rope || !k_rope || !v || !o) return ROTATTN_E_NULL;
-  if (!aligned16(q_rope) || !aligned16(k_rope) || !aligned16(v) || !aligned16(o))
+  if (!p || !o) return ROTATTN_E_NULL;
+  if (!p->q_rope || !p->k_rope || !p->v_t) return ROTATTN_E_NULL;
+  if (!aligned16(p->q_rope) || !aligned16(p->k_rope) || !aligned16(p->v_t) || !aligned16(o))
     return ROTATTN_E_ALIGN;
   const int BH = s->B * s->H;
   int n_run = 0;
   Fp16Args a;
   a.run = make_bits(head_select_host, BH, true, true, &n_run);
-  a.q = q_rope; a.k = k_rope; a.v = v; a.o = o;
+  a.q = p->q_rope; a.k = p->k_rope; a.v_t = p->v_t; a.o = o;
   a.N = s->N;
+  a.NB = nblocks(s);
   a.kappa = rotattn_kappa_host(s->D);
   if (n_run == 0) return ROTATTN_OK;
   return launch_fp16(s->D, BH, a, stream) == hipSuccess ? ROTATTN_OK : ROTATTN_E_HIP;
@@ -288,7 +293,7 @@ int rotattn_mixed_fwd(const rotattn_shape* s, const uint16_t* q, const uint16_t*
   if (fallback_mask_host) {
     int n_fb = 0;
     make_bits(fallback_mask_host, s->B * s->H, true, false, &n_fb);
-    if (n_fb > 0) r = rotattn_fp16_fwd(s, p.q_rope, p.k_rope, v, fallback_mask_host, o, stream);
+    if (n_fb > 0) r = rotattn_fp16_fwd(s, &p, fallback_mask_host, o, stream);
   }
   return r;
 }

@@ -43,7 +43,7 @@ struct PrologueArgs {
   const double* rot64;          // rotation in fp64, [k][r] per partition (t at 0, h at d_t^2, w next)
   uint8_t *q4, *k4, *v4;
   float *q_scale_l2, *k_scale, *v_scale;
-  uint16_t *q_rope, *k_rope;
+  uint16_t *q_rope, *k_rope, *v_t;   // fallback heads: [BH][N_pad][D], V^T tiles
   int N, NB, grid_h, grid_w;
   float kappa;
   HeadBits fallback;            // bit set: RoPE'd fp16 only
@@ -68,9 +68,10 @@ struct Int4Debug {
 };
 
 struct Fp16Args {
-  const uint16_t *q, *k, *v;
+  const uint16_t *q, *k;   // RoPE'd Q', K': [BH][N_pad][D], rows >= N zero
+  const uint16_t* v_t;     // V^T per 64-key tile: [BH][N_pad/64][D][64], operand order
   uint16_t* o;
-  int N;
+  int N, NB;
   float kappa;
   HeadBits run;
 };

@@ -48,7 +48,7 @@ class RopeRot(C.Structure):
 class Prepared(C.Structure):
     _fields_ = [("layout", C.c_int32)] + [
         (n, C.c_void_p) for n in ("q4", "k4", "v4", "q_scale_l2", "k_scale", "v_scale", "q_rope",
-                                  "k_rope", "rot64")]
+                                  "k_rope", "v_t", "rot64")]
 
 
 class Debug(C.Structure):
@@ -86,7 +86,7 @@ def lib() -> C.CDLL:
             "rotattn_prepare_qkv": (C.c_int, [S, P, P, P, C.POINTER(RopeRot), P,
                                               C.POINTER(Prepared), P]),
             "rotattn_int4_fwd": (C.c_int, [S, C.POINTER(Prepared), P, P, C.POINTER(Debug), P]),
-            "rotattn_fp16_fwd": (C.c_int, [S, P, P, P, P, P, P]),
+            "rotattn_fp16_fwd": (C.c_int, [S, P, P, P, P]),
             "rotattn_workspace_bytes": (C.c_size_t, [S]),
             "rotattn_mixed_fwd": (C.c_int, [S, P, P, P, C.POINTER(RopeRot), P, P, C.c_size_t, P, P]),
             "rotattn_pcode_sweep": (C.c_int, [C.c_int, C.c_uint32, C.c_uint32, P, C.c_uint32, P, P]),
@@ -224,9 +224,11 @@ def int4_fwd(shape: Shape, prep: PreparedDevice, o, mask=None, debug: Debug | No
                                  _stream(stream)), "int4_fwd")
 
 
-def fp16_fwd(shape: Shape, q_rope, k_rope, v, o, head_select=None, stream=None) -> None:
+def fp16_fwd(shape: Shape, prep: PreparedDevice, o, head_select=None, stream=None) -> None:
+    """FP16 attention of the selected heads from the prologue's fallback
+    buffers (q_rope, k_rope, v_t of `prep`)."""
     keep, m = _mask_arg(head_select)
-    check(lib().rotattn_fp16_fwd(C.byref(shape), _ptr(q_rope), _ptr(k_rope), _ptr(v), m, _ptr(o),
+    check(lib().rotattn_fp16_fwd(C.byref(shape), C.byref(prep.struct), m, _ptr(o),
                                  _stream(stream)), "fp16_fwd")
 
 
