@@ -22,6 +22,9 @@ namespace rotattn {
 constexpr int kFThreads = 256;
 constexpr int kKT = 64;   // keys per tile
 
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
 template <int D>
 struct Fp16Kernel {
   static constexpr int KS = D / 16;              // k-steps of 16 channels for QK^T
@@ -103,10 +106,19 @@ struct Fp16Kernel {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(S[sub][r], a.kappa, -mnew));
-        ls += p;
-        P[sub][r >> 3][r & 7] = (_Float16)p;
+      for (int s = 0; s < 2; ++s) {
+        uint32_t wpk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 8 * s + 2 * i;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(S[sub][r], a.kappa, -mnew));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(S[sub][r + 1], a.kappa, -mnew));
+          ls += p0;
+          ls += p1;
+          // one v_cvt_pk_f16_f32 per pair (round to nearest even), packed in place
+          wpk[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){p0, p1}, v2h));
+        }
+        P[sub][s] = __builtin_bit_cast(v8h, uint4{wpk[0], wpk[1], wpk[2], wpk[3]});
       }
     l = fmaf(l, alpha, ls);
   }
