@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="time the step only: skip the packed-layout, mixed_fwd and all-FP16 "
                          "side figures (used for counter collection)")
-    ap.add_argument("--mixed-steps", type=int, default=1,
+    ap.add_argument("--mixed-steps", type=int, default=2,
                     help="denoising steps of the mixed workload to time as a side figure (0: skip)")
     return ap.parse_args()
 
@@ -186,6 +186,11 @@ def main():
         kernels["mixed_fwd_call_ms"] = round(e0.elapsed_time(e1) / 3, 4)
         del ws
 
+        # INT4 output of every head, kept for the per-head error report below
+        R.prepare_qkv(shape, qd, kd, vd, rr, prep, None)
+        R.int4_fwd(shape, prep, o, mask=None)
+        o_int4 = o.clone()
+
         # FP16 FlashAttention on every head of the same shape (kernel-level analogue
         # of the full-precision baseline) -- context figure
         all_fb = np.ones(BH, np.uint8)
@@ -203,6 +208,11 @@ def main():
         kernels["fp16_attn_f16_peak_frac"] = round(ops / (f16_ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4)
         kernels["int4_vs_fp16_kernel_speedup"] = round(f16_ms / k2_ms, 3) if n_int4 == BH else None
         print(f"[bench] fp16 all heads {f16_ms:.3f} ms", file=sys.stderr, flush=True)
+        from video_diffusion_transformers_amd import fallback
+        kernels["int4_vs_fp16_head_error"] = dict(
+            reference="FP16 attention kernel, same inputs",
+            **fallback.report(fallback.head_rel_error(o_int4, o)))
+        del o_int4
     del qd, kd, vd, prep, o
     torch.cuda.empty_cache()
 
@@ -245,8 +255,9 @@ def main():
 
 
 def bench_mixed(steps: int):
-    """The mixed workload: 720p shape, a seeded quarter of the heads FP16, one
-    rotattn_mixed_fwd per denoising step with fresh inputs (side figure)."""
+    """The mixed workload: 720p shape, one rotattn_mixed_fwd per denoising step
+    with fresh inputs and a per-step fallback mask (step 0: every head FP16;
+    later steps: a seeded quarter of the heads FP16).  Side figure."""
     import torch
     from video_diffusion_transformers_amd import rotattn as R
     from video_diffusion_transformers_amd import synth
@@ -254,26 +265,30 @@ def bench_mixed(steps: int):
     shape = R.shape_of(cfg)
     _, r32 = synth.rotation_matrices(cfg.split)
     rr = R.RopeRotDevice(shape, r32)
-    mask = synth.fallback_mask(cfg)
+    sched = synth.fallback_schedule(cfg, steps, early_fp16_steps=1)[:, 0]
     ws = torch.empty(R.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
     o = torch.empty((cfg.B, cfg.H, cfg.N, cfg.D), dtype=torch.float16, device="cuda")
-    times = []
+    per_step = []
     for s in range(steps):
         q, k, v = synth.all_heads_qkv(cfg, s)
         qd, kd, vd = (torch.from_numpy(x).cuda() for x in (q, k, v))
-        R.mixed_fwd(shape, qd, kd, vd, rr, mask, ws, o)      # warm
+        R.mixed_fwd(shape, qd, kd, vd, rr, sched[s], ws, o)      # warm
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        R.mixed_fwd(shape, qd, kd, vd, rr, mask, ws, o)
+        R.mixed_fwd(shape, qd, kd, vd, rr, sched[s], ws, o)
         e1.record()
         torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
+        per_step.append({"step": s, "fp16_heads": int(sched[s].sum()),
+                         "ms": round(e0.elapsed_time(e1), 4)})
         del qd, kd, vd
-    ms = float(np.mean(times))
+    ms = float(np.mean([p["ms"] for p in per_step]))
     ops = 4.0 * cfg.B * cfg.H * cfg.N ** 2 * cfg.D
-    print(f"[bench] mixed {steps} step(s): {ms:.3f} ms/step", file=sys.stderr, flush=True)
-    return {"workload": "720p shape, 30 INT4 + 10 FP16 heads (seeded mask), fresh inputs per step",
-            "steps": steps, "ms_per_step": round(ms, 4),
+    print(f"[bench] mixed {steps} step(s): " +
+          ", ".join(f"step {p['step']} ({p['fp16_heads']} FP16 heads) {p['ms']:.3f} ms"
+                    for p in per_step), file=sys.stderr, flush=True)
+    return {"workload": "720p shape, per-step fallback mask (step 0 all heads FP16, then 10 of "
+                        "40 heads FP16, seeded), fresh inputs per step",
+            "steps": steps, "per_step": per_step, "ms_per_step": round(ms, 4),
             "effective_tops": round(ops / (ms * 1e-3) / 1e12, 2)}
 
 

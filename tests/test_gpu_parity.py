@@ -249,6 +249,74 @@ def test_mixed_720p_denoising_steps(step):
         check_out(og[bh][rows], ref, f"mixed step {step} head {bh}")
 
 
+def test_mixed_schedule_steps_and_layers():
+    """A per-(step, layer) schedule through mixed_fwd: step 0 all heads FP16,
+    step 1 the fixed quarter mask; each layer call writes its own output."""
+    torch = torch_cuda()
+    from video_diffusion_transformers_amd import rotattn as R
+    cfg = synth.CONFIGS["mixed"]
+    sched = synth.fallback_schedule(cfg, 2, n_layers=2, early_fp16_steps=1, fp16_layers=(1,))
+    for step in (0, 1):
+        run = get_run("mixed", step)
+        ws = torch.empty(R.workspace_bytes(run.shape), dtype=torch.uint8, device="cuda")
+        for layer in (0, 1):
+            mask = sched[step, layer]
+            o = run.empty_out()
+            R.mixed_fwd(run.shape, run.q, run.k, run.v, run.rr, mask, ws, o)
+            torch.cuda.synchronize()
+            og = o.reshape(run.cfg.BH, run.cfg.N, run.cfg.D).cpu().numpy()
+            bhs = [3 + 11 * layer + 5 * step]
+            if not mask.all():
+                bhs.append(int(np.nonzero(mask == 0)[0][layer]))
+            for bh in bhs:
+                rows = synth.sampled_rows(run.cfg, bh, 32)
+                ref = run.oracle_fp16(bh, rows)[0] if mask[bh] else run.oracle_int4(bh, rows)[0]
+                check_out(og[bh][rows], ref, f"schedule step {step} layer {layer} head {bh}")
+        del ws
+
+
+def test_head_error_proxy_tracks_fp64_reference():
+    """The per-head INT4 error measured against the FP16 kernel (what the
+    benchmark reports to guide the fallback mask) agrees with the INT4 error
+    against exact float64 attention of the unquantized RoPE'd inputs, within
+    10% on every head, because the FP16 kernel's own error is far smaller."""
+    torch = torch_cuda()
+    from video_diffusion_transformers_amd import fallback
+    from video_diffusion_transformers_amd import rotattn as R
+    run = get_run("mixed", 0)
+    cfg = run.cfg
+    BH, N, D = cfg.BH, cfg.N, cfg.D
+    run.prepare(mask=None)
+    o4 = run.empty_out()
+    R.int4_fwd(run.shape, run.prep, o4, mask=None)
+    all_fb = np.ones(BH, np.uint8)
+    run.prepare(mask=all_fb)
+    o16 = run.empty_out()
+    R.fp16_fwd(run.shape, run.prep, o16, head_select=all_fb)
+    torch.cuda.synchronize()
+    whole = fallback.head_rel_error(o4, o16)
+    g4 = o4.reshape(BH, N, D).cpu().numpy().astype(np.float64)
+    g16 = o16.reshape(BH, N, D).cpu().numpy().astype(np.float64)
+    del o4, o16
+    tab64 = O.all_rope_tables(cfg.grid, cfg.split, dtype=np.float64)
+    q, k, v = (x.reshape(BH, N, D) for x in run.host)
+
+    def rel(a, b):
+        return np.linalg.norm(a - b) / np.linalg.norm(b)
+
+    for bh in range(BH):
+        rows = synth.sampled_rows(cfg, bh, 16)
+        qr = O.apply_rope(q[bh].astype(np.float64), tab64, cfg.grid, cfg.split)
+        kr = O.apply_rope(k[bh].astype(np.float64), tab64, cfg.grid, cfg.split)
+        ref = O.softmax_attention(qr, kr, v[bh], rows, 1.0 / np.sqrt(D))
+        e4, e16 = rel(g4[bh][rows], ref), rel(g16[bh][rows], ref)
+        proxy = rel(g4[bh][rows], g16[bh][rows])
+        assert e16 <= 0.1 * e4, f"head {bh}: fp16 {e16:.3g} vs int4 {e4:.3g}"
+        assert abs(proxy - e4) <= 0.1 * e4, f"head {bh}: proxy {proxy:.3g} vs fp64 {e4:.3g}"
+        # the whole-head figure and the sampled-row figure describe one head
+        assert proxy / 3 <= whole[bh] <= 3 * proxy, f"head {bh}: {whole[bh]:.3g} vs {proxy:.3g}"
+
+
 RAGGED = [((1, 3, (3, 5, 7)), 64, (24, 20, 20)),      # N = 105 < 128
           ((2, 2, (2, 9, 17)), 128, (44, 42, 42)),    # N = 306: tail 50
           ((1, 4, (5, 7, 11)), 128, (44, 42, 42)),    # N = 385: tail 1

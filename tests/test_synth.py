@@ -53,3 +53,26 @@ def test_masks_and_rows():
     r = synth.sampled_rows(synth.CONFIGS["720p"], 5)
     assert r.size == 256 and np.all(np.diff(r) > 0) and r.max() < 75600
     assert np.array_equal(synth.sampled_rows(synth.CONFIGS["small"], 0), np.arange(1024))
+
+
+def test_fallback_schedule_steps_and_layers():
+    cfg = synth.CONFIGS["mixed"]
+    base = synth.fallback_mask(cfg)
+    sched = synth.fallback_schedule(cfg, 4, n_layers=3, early_fp16_steps=1, fp16_layers=(2,))
+    assert sched.shape == (4, 3, cfg.BH) and sched.dtype == np.uint8
+    assert np.all(sched[0] == 1)                      # early step: every head FP16
+    assert np.all(sched[:, 2] == 1)                   # FP16 layer at every step
+    for s in range(1, 4):
+        for layer in range(2):
+            assert np.array_equal(sched[s, layer], base)
+    assert synth.fallback_schedule(cfg, 2, early_fp16_steps=5).min() == 1
+    assert synth.fallback_schedule(cfg, 0).shape == (0, 1, cfg.BH)
+    none = synth.fallback_schedule(synth.CONFIGS["720p"], 3, early_fp16_steps=0)
+    assert none.sum() == 0
+    for bad in (dict(n_layers=0), dict(fp16_layers=(1,))):
+        try:
+            synth.fallback_schedule(cfg, 2, **bad)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError(bad)

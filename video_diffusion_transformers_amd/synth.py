@@ -12,14 +12,18 @@ activations exist here, so Q/K/V are drawn from distributions that carry the
 structure the pages describe:
 
 * Q/K outliers sit in a few channels whose placement follows how 3D RoPE
-  partitions the head dimension (RotateAttention page, Abstract) -- here a
-  few heavy channels inside one partition;
+  partitions the head dimension (RotateAttention page, Abstract) -- here four
+  heavy channels inside the temporal partition, the same in Q and K, with the
+  logit spread held at LOGIT_STD nats so that each query row spreads its
+  weight over hundreds to thousands of the 75,600 keys at 720p instead of
+  collapsing onto one;
 * V outliers are not tied to channels or positions (MXAttention page,
   VC-Attention abstract) -- here sparse whole-token rows scaled up.
 
 Every tensor of every head has its own stream,
 ``SeedSequence([cfg_seed, step, tensor, b, h])`` with tensor Q=0, K=1, V=2, so a
-single head can be regenerated without the others.  Values are drawn in
+single head can be regenerated without the others; a head's Q/K channel scales
+come from ``SeedSequence([cfg_seed, STRUCTURE_SALT, b, h])``.  Values are drawn in
 float64, rounded to float32 and then to float16 (round to nearest even).
 """
 from __future__ import annotations
@@ -33,6 +37,8 @@ TENSOR_Q, TENSOR_K, TENSOR_V = 0, 1, 2
 ROTATION_SEED = 7          # SeedSequence([7, partition]) for the default rotation
 ROW_SAMPLE_SALT = 555      # SeedSequence([cfg_seed, 555, h]) for sampled query rows
 MASK_SALT = 999            # SeedSequence([cfg_seed, 999]) for the fallback mask
+STRUCTURE_SALT = 333       # SeedSequence([cfg_seed, 333, b, h]) for a head's Q/K channel scales
+LOGIT_STD = 2.5            # nats: spread of q.k/sqrt(D) over independent rows ("video")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -96,13 +102,28 @@ def _qk_tiny(rng, N, D, split):
     return x
 
 
-def _qk_video(rng, N, D, split):
-    z = rng.standard_normal(D)
-    x = rng.standard_normal((N, D)) * np.exp(0.5 * z)[None, :]
+def _video_channel_scales(cfg: Config, b: int, h: int):
+    """Per-channel standard deviations of one head's Q and K.
+
+    They stand for the head's projection weights, so they come from a stream
+    of their own, SeedSequence([cfg_seed, STRUCTURE_SALT, b, h]), and stay the
+    same across denoising steps.  Each channel has a log-normal scale
+    exp(0.5 z); four channels inside the temporal RoPE partition, the same four
+    in Q and K, are raised by independent factors in [10, 30].  Q and K are then
+    scaled by one common factor so that the scaled logits q.k/sqrt(D) of
+    independent rows have a standard deviation of LOGIT_STD nats:
+    Var(q.k/sqrt(D)) = sum_c sq_c^2 sk_c^2 / D for independent zero-mean rows.
+    """
+    D, split = cfg.D, cfg.split
+    rng = _rng(cfg.cfg_seed, STRUCTURE_SALT, b, h)
+    sq = np.exp(0.5 * rng.standard_normal(D))
+    sk = np.exp(0.5 * rng.standard_normal(D))
     ch = rng.choice(split[0], size=4, replace=False)      # temporal partition
-    mult = rng.uniform(10.0, 30.0, size=4)
-    x[:, ch] *= mult[None, :]
-    return x
+    sq[ch] *= rng.uniform(10.0, 30.0, size=4)
+    sk[ch] *= rng.uniform(10.0, 30.0, size=4)
+    logit_sd = np.sqrt(np.sum(sq ** 2 * sk ** 2) / D)
+    c = np.sqrt(LOGIT_STD / logit_sd)
+    return sq * c, sk * c
 
 
 def _v_video(rng, N, D):
@@ -122,7 +143,11 @@ def head_qkv(cfg: Config, step: int, b: int, h: int):
         if cfg.dist == "tiny":
             x = _qk_tiny(rng, N, D, cfg.split) if tensor != TENSOR_V else rng.standard_normal((N, D))
         elif cfg.dist == "video":
-            x = _qk_video(rng, N, D, cfg.split) if tensor != TENSOR_V else _v_video(rng, N, D)
+            if tensor == TENSOR_V:
+                x = _v_video(rng, N, D)
+            else:
+                scales = _video_channel_scales(cfg, b, h)[0 if tensor == TENSOR_Q else 1]
+                x = rng.standard_normal((N, D)) * scales[None, :]
         elif cfg.dist == "diffuse":
             # no outliers; scaled logits have a standard deviation of about
             # one nat, so rows are spread and every P code occurs
@@ -174,6 +199,26 @@ def fallback_mask(cfg: Config) -> np.ndarray:
     elif cfg.fallback != "none":
         raise ValueError(cfg.fallback)
     return mask
+
+
+def fallback_schedule(cfg: Config, n_steps: int, n_layers: int = 1, early_fp16_steps: int = 1,
+                      fp16_layers=()) -> np.ndarray:
+    """uint8 [n_steps, n_layers, B*H]: the fallback mask of every (denoising
+    step, attention layer).  Full-precision fallback may be given to whole
+    attention blocks and to whole denoising steps (RotateAttention page,
+    Abstract); the plainest schedule of that kind is used here: the first
+    early_fp16_steps steps and the layers listed in fp16_layers run every head
+    in FP16, every other (step, layer) uses the config's fixed head mask."""
+    if n_steps < 0 or n_layers < 1:
+        raise ValueError("n_steps must be >= 0 and n_layers >= 1")
+    sched = np.repeat(fallback_mask(cfg)[None, None, :], n_steps, axis=0)
+    sched = np.repeat(sched, n_layers, axis=1)
+    sched[:min(early_fp16_steps, n_steps)] = 1
+    for layer in fp16_layers:
+        if not 0 <= layer < n_layers:
+            raise ValueError(f"layer {layer} out of range")
+        sched[:, layer] = 1
+    return sched
 
 
 def sampled_rows(cfg: Config, h: int, count: int | None = None) -> np.ndarray:
