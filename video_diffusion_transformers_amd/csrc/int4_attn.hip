@@ -45,7 +45,6 @@ struct CodeCtx {
   float ct;      // c_t
   float mnew;    // m'
   float delta;   // half-width of the band around each half-integer that takes the exact path
-  float tz;      // exponent-domain bound: a group whose largest argument is below it has only code 0
 };
 
 __device__ __forceinline__ float ulp_pos(float v) {   // ulp of a positive normal float
@@ -68,13 +67,9 @@ __device__ __forceinline__ CodeCtx make_ctx(float ct, float mnew, float log2_15,
   const float e = 0x1p-21f + ulp_pos(fabsf(mnew) + 8.0f);
   // 15.5 * ln 2 < 10.75; v_exp_f32 error < 1 ulp; 12x and +4e-6 are margin.
   c.delta = 12.0f * e + 4e-6f;
-  // The fused argument t is within e of x + log2(15).  If t < -1 - 2e then
-  // 15*2^x < 1/2, so x < tau_1 and the code is 0; -1 - 4e leaves a factor 2.
-  c.tz = -1.0f - 4.0f * e;
   // c_t so small that c_t * iscale may be subnormal: never trust the fast path.
   if (ct != 0.0f && ct < 0x1p-100f) {
     c.delta = 1.0f;
-    c.tz = -INFINITY;
   }
   return c;
 }
@@ -158,19 +153,18 @@ __device__ __forceinline__ int signbit01(float v) { return (int)(__float_as_uint
 
 // The P code of the fp8 kernel for one lane's 16 scores of a 32-key group
 // (exact float I), as E4M3 bytes (byte r = code of score r; exact for the
-// integers 0..15).  rr receives the codes as floats; lp[] accumulates the
-// unquantized 15*2^x in four partial sums.
+// integers 0..15).  rr receives the codes as floats; lsum accumulates the
+// unquantized 15*2^x.
 //
 // y = v_exp_f32(t), t = fma(I, c_t, log2(15) - m'), is within delta of
-// 15*2^x.  If no lane's largest t reaches tz, every code of the group is 0.
-// Otherwise code = rne(y) unless some |y - rne(y)| exceeds 1/2 - delta in the
+// 15*2^x.  code = rne(y) unless some |y - rne(y)| exceeds 1/2 - delta in the
 // wave; then every score of the group is fixed exactly: the true value lies
 // within delta of y, so the code is j - 1 or j for the half-integer boundary
 // j - 1/2 nearest y (j = rne(y) + [y > rne(y)]), and it is j iff x >= tau_j
 // with x = fl(fl(I c_t) - m') -- one comparison against the staged table.
 // Masked keys (last tile) arrive as I = -inf: t = -inf, y = 0, code 0 on both
 // paths (the exact one sees x = -inf or NaN against tau_0 = -inf with j = 0).
-__device__ __forceinline__ v4i pcode16_f8(const float (&f)[16], float fmax, const CodeCtx& cx,
+__device__ __forceinline__ v4i pcode16_f8(const float (&f)[16], const CodeCtx& cx,
                                           const float* tau_lds, float& lsum,
                                           float (&rr)[16]) {
   float y[16];
@@ -178,11 +172,6 @@ __device__ __forceinline__ v4i pcode16_f8(const float (&f)[16], float fmax, cons
   for (int r = 0; r < 16; ++r) {
     y[r] = __builtin_amdgcn_exp2f(fmaf(f[r], cx.cq, cx.m15n));
     lsum += y[r];
-  }
-  if (!wave_any(fmaf(fmax, cx.cq, cx.m15n) >= cx.tz)) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) rr[r] = 0.0f;
-    return v4i{0, 0, 0, 0};
   }
   float g = 0.0f;
 #pragma unroll
@@ -515,18 +504,30 @@ struct Int4F8Kernel {
     const uint4 b = *(const uint4*)(row + 16 * ((c0 + 1) ^ key));
     return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
   }
+  // The same for the operand reads of the MFMA loops: logical chunk
+  // 4k + 2hh + j of row r (j = 0, 1) sits at byte 16 ((2hh ^ key(r)) ^ (4k + j))
+  // of the row (the three index parts use disjoint bits), so one per-lane
+  // offset x = row * width + 16 (2hh ^ key) serves every k and j by an XOR.
+  // x is made opaque once per tile so that the four XORed offsets are
+  // recomputed (3 VALU) instead of being held in registers across the loop.
+  __device__ __forceinline__ static v8i ld32x(const uint8_t* tile, uint32_t x, int k) {
+    const uint4 a = *(const uint4*)(tile + (x ^ (64u * k)));
+    const uint4 b = *(const uint4*)(tile + (x ^ (64u * k + 16u)));
+    return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+  }
 
   // S^T = K_t Q^T
   __device__ __forceinline__ static void qk(const uint8_t* sk, const v8i (&qf)[KS], v16f (&S)[4]) {
     const int lane = threadIdx.x & 63;
     const int col = lane & 31, hh = lane >> 5;
+    uint32_t x = col * D + 16 * ((2 * hh) ^ kswz(col));
+    asm volatile("" : "+v"(x));
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
-      const int row = 32 * sub + col;
       S[sub] = v16f{0.0f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        S[sub] = mfma_f8(ld32s(sk + row * D, 4 * ks + 2 * hh, kswz(row)), qf[ks], S[sub]);
+        S[sub] = mfma_f8(ld32x(sk + 32 * sub * D, x, ks), qf[ks], S[sub]);
     }
   }
 
@@ -535,6 +536,8 @@ struct Int4F8Kernel {
                                             const v8i (&P)[2], v16f (&O)[DB]) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int col = lane & 31, hh = lane >> 5;
+    uint32_t xv = col * kBlock + 16 * ((2 * hh) ^ vswz(col));
+    if (!DBG) asm volatile("" : "+v"(xv));
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int row = 32 * db + col;
@@ -553,7 +556,7 @@ struct Int4F8Kernel {
       } else {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          O[db] = mfma_f8(ld32s(sv + row * kBlock, 4 * c + 2 * hh, vswz(row)), P[c], O[db]);
+          O[db] = mfma_f8(ld32x(sv + 32 * db * kBlock, xv, c), P[c], O[db]);
       }
     }
   }
@@ -618,7 +621,7 @@ struct Int4F8Kernel {
       float f[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) f[r] = S[sub][r];
-      const v4i pk = pcode16_f8(f, smx[sub], cx, tau_lds, ls, rr[sub]);
+      const v4i pk = pcode16_f8(f, cx, tau_lds, ls, rr[sub]);
       // 64-key chunk c = sub/2 holds subtile 2c in bytes 0-15, 2c+1 in 16-31
 #pragma unroll
       for (int i = 0; i < 4; ++i) P[sub >> 1][4 * (sub & 1) + i] = pk[i];
@@ -666,22 +669,34 @@ struct Int4F8Kernel {
     // within a tile are fixed; only the tile base (uniform) moves.
     typedef __attribute__((address_space(3))) void* lds_ptr;
     const int wu = __builtin_amdgcn_readfirstlane(w);   // wave index in an SGPR (LDS window base)
-    uint32_t koff[LOADS], voff[LOADS];
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int pc = (NW * i + w) * 64 + lane;             // physical chunk
+    // Instruction i of a wave fills rows 32i (D = 128; 64i for D = 64) further
+    // down than instruction 0, and the swizzle keys repeat with that period,
+    // so its per-lane offset is instruction 0's plus 4096 i: the uniform part
+    // goes to the scalar base, and one offset register per tensor remains.
+    static_assert(NW * 64 * 16 == 4096, "4 KiB per load instruction of the work-group");
+    uint32_t koff0, voff0;
+    {
+      const int pc = w * 64 + lane;                        // physical chunk of instruction 0
       const int krow = pc / KCPR, vrow = pc / 8;
-      koff[i] = krow * D + 16 * ((pc % KCPR) ^ kswz(krow));
-      voff[i] = vrow * kBlock + 16 * ((pc % 8) ^ vswz(vrow));
+      koff0 = krow * D + 16 * ((pc % KCPR) ^ kswz(krow));
+      voff0 = vrow * kBlock + 16 * ((pc % 8) ^ vswz(vrow));
     }
     auto gload = [&](int t, int buf) {
       const uint8_t* kb = a.k4 + (rows0 + (size_t)t * kBlock) * D;
       const uint8_t* vb = a.v4 + ((size_t)bh * NB + t) * D * kBlock;
+      // opaque per tile: keeps the loop from turning base + offset into
+      // per-lane 64-bit pointers held in registers
+      uint32_t ko = koff0, vo = voff0;
+      asm volatile("" : "+v"(ko), "+v"(vo));
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        __builtin_amdgcn_global_load_lds((const void*)(kb + koff[i]),
+        // uniform base in an SGPR pair + 32-bit lane offset: the saddr form
+        const uint8_t* kbi = kb + 4096 * i;
+        const uint8_t* vbi = vb + 4096 * i;
+        asm volatile("" : "+s"(kbi), "+s"(vbi));
+        __builtin_amdgcn_global_load_lds((const void*)(kbi + ko),
                                          (lds_ptr)(sk[buf] + (NW * i + wu) * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vb + voff[i]),
+        __builtin_amdgcn_global_load_lds((const void*)(vbi + vo),
                                          (lds_ptr)(sv[buf] + (NW * i + wu) * 1024), 16, 0, 0);
       }
     };
@@ -792,7 +807,7 @@ __device__ __forceinline__ v4i codes_of(const float (&I)[16], float c, float m, 
   if (F8) {
     const CodeCtx cx = make_ctx(c, m, a.log2_15, 1.0f);
     float rr[16], lsum = 0.0f;
-    pcode16_f8(f, fm, cx, tau_lds, lsum, rr);
+    pcode16_f8(f, cx, tau_lds, lsum, rr);
     uint32_t pk[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
