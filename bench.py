@@ -212,7 +212,24 @@ def main():
         kernels["int4_vs_fp16_head_error"] = dict(
             reference="FP16 attention kernel, same inputs",
             **fallback.report(fallback.head_rel_error(o_int4, o)))
-        del o_int4
+
+        # the rotation merged into RoPE (seeded pair phases in the tables, no
+        # dense rotation): prologue time and the same error report
+        rr_m = R.RopeRotDevice(shape, None, phases=synth.mergeable_phases(cfg.split))
+        R.prepare_qkv(shape, qd, kd, vd, rr_m, prep, None)
+        e0.record()
+        for _ in range(3):
+            R.prepare_qkv(shape, qd, kd, vd, rr_m, prep, None)
+        e1.record()
+        torch.cuda.synchronize()
+        kernels["prologue_merged_rotation_ms"] = round(e0.elapsed_time(e1) / 3, 4)
+        R.int4_fwd(shape, prep, o_int4, mask=None)
+        kernels["int4_merged_rotation_vs_fp16_head_error"] = dict(
+            reference="FP16 attention kernel, same inputs",
+            **fallback.report(fallback.head_rel_error(o_int4, o)))
+        print(f"[bench] prologue with the rotation merged into RoPE "
+              f"{kernels['prologue_merged_rotation_ms']:.3f} ms", file=sys.stderr, flush=True)
+        del o_int4, rr_m
     del qd, kd, vd, prep, o
     torch.cuda.empty_cache()
 

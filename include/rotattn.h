@@ -73,11 +73,15 @@ typedef struct rotattn_shape {
 
 /*
  * RoPE tables and rotation matrices (device, fp32, caller-owned).
- * cos_a/sin_a: [extent_a][d_a/2] with entry [p][j] = cos/sin(p * theta_{a,j}),
- * theta_{a,j} = base^(-2j/d_a); rotattn_rope_tables_host() fills them.
+ * cos_a/sin_a: [extent_a][d_a/2] with entry [p][j] = cos/sin(p * theta_{a,j}
+ * + phi_{a,j}), theta_{a,j} = base^(-2j/d_a); rotattn_rope_tables_host()
+ * fills them with phi = 0, rotattn_rope_tables_phase_host() with phases.
  * rot_a: [d_a][d_a] row-major orthogonal matrix, row = output channel; the
  * same matrices apply to Q and K of every head (RoPE-aware rotation inside
- * each RoPE partition, applied after RoPE).
+ * each RoPE partition, applied after RoPE; RotateAttention page, Abstract).
+ * rot_t, rot_h and rot_w may all be NULL: then no dense rotation is applied
+ * (z = the RoPE'd values), which is the form of a rotation merged into RoPE
+ * (phase tables).  Only some of them NULL is ROTATTN_E_NULL.
  */
 typedef struct rotattn_rope_rot {
   const float *cos_t, *sin_t, *cos_h, *sin_h, *cos_w, *sin_w;
@@ -170,6 +174,22 @@ int rotattn_rope_tables_host(const rotattn_shape* s, double base,
                              float* sin_h, float* cos_w, float* sin_w);
 
 /*
+ * Host: RoPE tables with a rotation merged in (the RotateAttention page,
+ * Abstract, offers rotation matrices that can be fused into RoPE).  A
+ * block-diagonal rotation made of one 2x2 rotation by phi_{a,j} per RoPE pair
+ * commutes with RoPE, so applying it after RoPE at position p equals RoPE with
+ * angle p * theta_{a,j} + phi_{a,j}.  phase_a: host array of d_a/2 doubles
+ * (NULL: all zero); entries are cos/sin of that angle computed in long double
+ * and rounded once to fp32.  Use with rot_t = rot_h = rot_w = NULL.
+ * Returns ROTATTN_E_ARG for a non-finite phase or base <= 1.
+ */
+int rotattn_rope_tables_phase_host(const rotattn_shape* s, double base,
+                                   const double* phase_t, const double* phase_h,
+                                   const double* phase_w, float* cos_t,
+                                   float* sin_t, float* cos_h, float* sin_h,
+                                   float* cos_w, float* sin_w);
+
+/*
  * Host: the 15 P-code thresholds tau_k (smallest fp32 with 15*2^tau_k >=
  * k - 1/2), so code(x) = #{k : x >= tau_k} = rne(15 * 2^x) for x <= 0.
  */
@@ -189,7 +209,8 @@ int rotattn_prepared_carve(const rotattn_shape* s, void* base, size_t bytes,
 /*
  * Prologue.  For every head with fallback_mask_host[b*H+h] == 0 (or all heads
  * when the mask is NULL): 3D RoPE on Q and K in fp32, the partition-wise
- * rotation (fp64 accumulation, one rounding to fp32), per-block symmetric
+ * rotation (fp64 accumulation, one rounding to fp32; skipped when the
+ * rotation pointers are NULL), per-block symmetric
  * INT4 quantization of Q, K, V, stored in out->layout.  For a fallback head:
  * RoPE'd fp16 Q'/K' into out->q_rope / out->k_rope and V^T tiles into
  * out->v_t only.

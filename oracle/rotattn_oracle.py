@@ -120,19 +120,24 @@ def token_coords(grid):
     return n // (Hg * Wg), (n // Wg) % Hg, n % Wg
 
 
-def rope_tables(extent: int, width: int, base: float = ROPE_BASE, dtype=np.float32):
-    """cos/sin of p * theta_j for p < extent, j < width/2 (R2).
+def rope_tables(extent: int, width: int, base: float = ROPE_BASE, dtype=np.float32,
+                phase=None):
+    """cos/sin of p * theta_j + phi_j for p < extent, j < width/2 (R2).
 
     theta_j = base^(-2j/width) taken as a real number; each entry is the exact
     cosine/sine rounded once to float32 (or float64 for the invariance pins).
+    phase (float64 per pair, default 0) is a 2x2 rotation of each RoPE pair
+    merged into RoPE (RotateAttention, Abstract: rotation matrices that can be
+    fused into RoPE; see pair_rotation).
     """
     half = width // 2
     cos = np.empty((extent, half), dtype)
     sin = np.empty((extent, half), dtype)
     for j in range(half):
         theta = mpmath.power(mpmath.mpf(base), -mpmath.mpf(2 * j) / width)
+        phi = mpmath.mpf(0) if phase is None else mpmath.mpf(float(phase[j]))
         for p in range(extent):
-            ang = p * theta
+            ang = p * theta + phi
             if dtype == np.float32:
                 cos[p, j] = nearest_f32(mpmath.cos(ang))
                 sin[p, j] = nearest_f32(mpmath.sin(ang))
@@ -142,9 +147,33 @@ def rope_tables(extent: int, width: int, base: float = ROPE_BASE, dtype=np.float
     return cos, sin
 
 
-def all_rope_tables(grid, split, base: float = ROPE_BASE, dtype=np.float32):
-    """[(cos_t, sin_t), (cos_h, sin_h), (cos_w, sin_w)]."""
-    return [rope_tables(extent, width, base, dtype) for extent, width in zip(grid, split)]
+def all_rope_tables(grid, split, base: float = ROPE_BASE, dtype=np.float32, phases=None):
+    """[(cos_t, sin_t), (cos_h, sin_h), (cos_w, sin_w)]; phases: one per-pair
+    array per partition (a merged rotation) or None."""
+    if phases is None:
+        phases = [None, None, None]
+    return [rope_tables(extent, width, base, dtype, ph)
+            for extent, width, ph in zip(grid, split, phases)]
+
+
+def pair_rotation(split, phases) -> list:
+    """The rotation that phase tables merge into RoPE, as explicit matrices.
+
+    One float64 [d_a, d_a] matrix per partition, block diagonal with the 2x2
+    rotation [[cos phi_j, -sin phi_j], [sin phi_j, cos phi_j]] on pair
+    (2j, 2j+1).  It commutes with RoPE at every position (both rotate the same
+    planes), so applying it after RoPE equals RoPE with angle p*theta_j + phi_j
+    (RotateAttention, Abstract: mergeable rotation fused into RoPE).
+    """
+    mats = []
+    for width, ph in zip(split, phases):
+        r = np.zeros((width, width))
+        for j in range(width // 2):
+            c, s = math.cos(float(ph[j])), math.sin(float(ph[j]))
+            r[2 * j, 2 * j], r[2 * j, 2 * j + 1] = c, -s
+            r[2 * j + 1, 2 * j], r[2 * j + 1, 2 * j + 1] = s, c
+        mats.append(r)
+    return mats
 
 
 def apply_rope(x: np.ndarray, tables, grid, split) -> np.ndarray:
@@ -362,15 +391,17 @@ def fp16_attention(q_rope16, k_rope16, v16, rows):
 def prepare_head(q16, k16, v16, tables, mats32, grid, split, fallback: bool = False):
     """Prologue of one head: RoPE, rotation, INT4 quantization (R2-R4).
 
-    A fallback head only gets RoPE'd fp16 Q'/K' (R7).
+    mats32 None: no dense rotation, z = the RoPE'd values (the form of a
+    rotation merged into the RoPE tables).  A fallback head only gets RoPE'd
+    fp16 Q'/K' (R7).
     """
     D = q16.shape[1]
     yq = apply_rope(q16.astype(np.float32), tables, grid, split)
     yk = apply_rope(k16.astype(np.float32), tables, grid, split)
     if fallback:
         return {"q_rope": yq.astype(np.float16), "k_rope": yk.astype(np.float16)}
-    zq = rotate(yq, mats32, split)
-    zk = rotate(yk, mats32, split)
+    zq = yq if mats32 is None else rotate(yq, mats32, split)
+    zk = yk if mats32 is None else rotate(yk, mats32, split)
     qc, qs, _ = quantize_blocks(zq)
     kc, ks, _ = quantize_blocks(zk)
     vc, vs, _ = quantize_blocks(v16.astype(np.float32))

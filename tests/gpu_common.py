@@ -88,7 +88,9 @@ def pack_vt_blocks(codes: np.ndarray, N_pad: int) -> np.ndarray:
 class Run:
     """One config on the device: inputs, RoPE/rotation, prepared buffers."""
 
-    def __init__(self, cfg: synth.Config, step: int = 0, layout: int = 1):
+    def __init__(self, cfg: synth.Config, step: int = 0, layout: int = 1, merged: bool = False):
+        """merged: the rotation is merged into the RoPE tables (seeded pair
+        phases, no dense rotation matrices)."""
         torch = torch_cuda()
         from video_diffusion_transformers_amd import rotattn as R
         self.R = R
@@ -100,8 +102,13 @@ class Run:
         q, k, v = synth.all_heads_qkv(cfg, step)
         self.host = (q, k, v)
         self.q, self.k, self.v = (torch.from_numpy(x).cuda() for x in (q, k, v))
-        self.r64, self.r32 = synth.rotation_matrices(cfg.split)
-        self.rr = R.RopeRotDevice(self.shape, self.r32)
+        self.merged = merged
+        self.phases = synth.mergeable_phases(cfg.split) if merged else None
+        if merged:
+            self.r64 = self.r32 = None
+        else:
+            self.r64, self.r32 = synth.rotation_matrices(cfg.split)
+        self.rr = R.RopeRotDevice(self.shape, self.r32, phases=self.phases)
         self.mask = synth.fallback_mask(cfg)
         self.layout = layout
         self.prep = R.PreparedDevice(self.shape, with_rope=True, layout=layout)
@@ -139,7 +146,7 @@ class Run:
 
     @functools.cached_property
     def tables(self):
-        return O.all_rope_tables(self.cfg.grid, self.cfg.split)
+        return O.all_rope_tables(self.cfg.grid, self.cfg.split, phases=self.phases)
 
     @functools.lru_cache(maxsize=64)
     def oracle_prep(self, bh: int, fallback: bool = False):

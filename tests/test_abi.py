@@ -109,3 +109,27 @@ def test_host_thresholds_and_kappa_equal_oracle():
     assert np.array_equal(R.pcode_thresholds().view(np.uint32), O.pcode_thresholds().view(np.uint32))
     for D in (64, 128):
         assert R.kappa(D) == O.kappa(D)
+
+
+@pytest.mark.parametrize("name", ["small", "720p"])
+def test_host_phase_tables_equal_oracle(name):
+    cfg = synth.CONFIGS[name]
+    phases = synth.mergeable_phases(cfg.split)
+    lib_tabs = R.rope_tables(R.shape_of(cfg), phases=phases)
+    ora_tabs = O.all_rope_tables(cfg.grid, cfg.split, phases=phases)
+    for (lc, ls), (oc, os_) in zip(lib_tabs, ora_tabs):
+        assert np.array_equal(lc.view(np.uint32), oc.view(np.uint32))
+        assert np.array_equal(ls.view(np.uint32), os_.view(np.uint32))
+    bad = [np.full(w // 2, np.nan) for w in cfg.split]
+    with pytest.raises(R.RotAttnError):
+        R.rope_tables(R.shape_of(cfg), phases=bad)
+
+
+def test_prepare_rejects_partial_rotation_pointers():
+    L = R.lib()
+    s = R.make_shape(1, 2, (2, 4, 4), 64, (24, 20, 20))
+    fake = C.c_void_p(1 << 20)
+    rr = R.RopeRot(*([fake] * 6 + [fake, C.c_void_p(0), fake]))
+    p = R.Prepared()
+    assert L.rotattn_prepare_qkv(C.byref(s), fake, fake, fake, C.byref(rr), None, C.byref(p),
+                                 C.c_void_p(0)) == -1

@@ -24,14 +24,15 @@ _RUNS = {}
 LAYOUTS = {"packed": 0, "fp8": 1}
 
 
-def get_run(name, step=0, layout="fp8"):
+def get_run(name, step=0, layout="fp8", merged=False):
     """Workloads stay resident for the whole module (tens of GB at most); the
-    denoising steps of the mixed workload replace one another."""
-    key = (name, step, layout)
+    denoising steps of the mixed workload, and the merged-rotation variant of
+    a workload, replace one another."""
+    key = (name, step, layout, merged)
     if key not in _RUNS:
         for old in [k for k in _RUNS if k[0] == name and k[2] == layout]:
             del _RUNS[old]
-        _RUNS[key] = Run(synth.CONFIGS[name], step, LAYOUTS[layout])
+        _RUNS[key] = Run(synth.CONFIGS[name], step, LAYOUTS[layout], merged=merged)
     return _RUNS[key]
 
 
@@ -190,6 +191,43 @@ def test_int4_output_within_tolerance(name, layout):
         rows = synth.sampled_rows(run.cfg, bh)
         o16, _ = run.oracle_int4(bh, rows)
         check_out(og[bh][rows], o16, f"{name} head {bh}")
+
+
+# ------------------------------------------------------------------ rotation merged into RoPE
+
+@pytest.mark.parametrize("layout", ["packed", "fp8"])
+@pytest.mark.parametrize("name", ["tiny", "small", "720p"])
+def test_merged_rotation_prologue_and_output(name, layout):
+    """Phase tables and no dense rotation (the prologue's RoPE-only path):
+    codes and scale bits equal the oracle's, fallback heads' Q'/K' too, and the
+    INT4 output is within tolerance."""
+    torch = torch_cuda()
+    run = get_run(name, layout=layout, merged=True)
+    run.prepare()
+    g = run.gpu_prepared()
+    f8 = layout == "fp8"
+    N = run.cfg.N
+    for bh in HEADS[name]:
+        fb = bool(run.mask[bh])
+        p = run.oracle_prep(bh, fallback=fb)
+        if fb:
+            for t in ("q", "k"):
+                assert np.array_equal(g[f"{t}_rope"][bh][:N], p[f"{t}_rope"].view(np.uint16))
+            continue
+        for t in ("q", "k"):
+            want = np.zeros((run.N_pad, run.cfg.D if f8 else run.cfg.D // 2), np.uint8)
+            want[:N] = fp8_bytes(p[f"{t}_codes"]) if f8 else pack_rows(p[f"{t}_codes"])
+            assert np.array_equal(g[f"{t}4"][bh], want), (name, bh, t)
+        for f in ("q_scale_l2", "k_scale", "v_scale"):
+            assert np.array_equal(g[f][bh].view(np.uint32), p[f].view(np.uint32)), (name, bh, f)
+    from video_diffusion_transformers_amd import rotattn as R
+    o = run.empty_out()
+    R.int4_fwd(run.shape, run.prep, o, mask=run.mask)
+    torch.cuda.synchronize()
+    og = o.reshape(run.cfg.BH, N, run.cfg.D).cpu().numpy()
+    bh = [h for h in HEADS[name] if not run.mask[h]][-1]
+    rows = synth.sampled_rows(run.cfg, bh, 64 if N > 4096 else None)
+    check_out(og[bh][rows], run.oracle_int4(bh, rows)[0], f"{name} merged head {bh}")
 
 
 # ------------------------------------------------------------------ FP16 fallback

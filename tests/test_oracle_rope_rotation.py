@@ -170,3 +170,78 @@ def test_rotation_float32_is_correctly_summed():
         ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
         assert np.all(np.abs(got - ref) <= ulp)
         assert np.mean(got == ref.astype(np.float32)) > 0.999
+
+
+# ------------------------------------------------------------------ rotation merged into RoPE
+# RotateAttention page, Abstract: rotation matrices that can be fused into
+# RoPE.  Pins: the phase tables equal the explicit 2x2 pair rotation applied
+# after plain RoPE (an independent construction), scores are unchanged, zero
+# phases give the plain tables, and the float32 entries are correctly rounded.
+
+@pytest.mark.parametrize("grid,split", SPLITS)
+def test_phase_rope_equals_pair_rotation_after_rope(grid, split):
+    rng = np.random.default_rng(5)
+    D = sum(split)
+    N = grid[0] * grid[1] * grid[2]
+    phases = [rng.uniform(0, 2 * np.pi, w // 2) for w in split]
+    x = rng.standard_normal((N, D))
+    merged = O.apply_rope(x, O.all_rope_tables(grid, split, dtype=np.float64, phases=phases),
+                          grid, split)
+    plain = O.apply_rope(x, O.all_rope_tables(grid, split, dtype=np.float64), grid, split)
+    after = np.empty_like(plain)
+    for off, w, r in zip(O.partition_offsets(split), split, O.pair_rotation(split, phases)):
+        after[:, off:off + w] = plain[:, off:off + w] @ r.T
+    assert np.allclose(merged, after, rtol=0, atol=1e-12)
+    # and a block-diagonal pair rotation commutes with RoPE: before == after
+    before_x = np.empty_like(x)
+    for off, w, r in zip(O.partition_offsets(split), split, O.pair_rotation(split, phases)):
+        before_x[:, off:off + w] = x[:, off:off + w] @ r.T
+    before = O.apply_rope(before_x, O.all_rope_tables(grid, split, dtype=np.float64), grid, split)
+    assert np.allclose(before, after, rtol=0, atol=1e-12)
+
+
+def test_phase_rope_leaves_scores_unchanged():
+    grid, split = SPLITS[1]
+    rng = np.random.default_rng(6)
+    N, D = grid[0] * grid[1] * grid[2], sum(split)
+    phases = synth.mergeable_phases(split)
+    q, k = rng.standard_normal((N, D)), rng.standard_normal((N, D))
+    t64 = O.all_rope_tables(grid, split, dtype=np.float64)
+    p64 = O.all_rope_tables(grid, split, dtype=np.float64, phases=phases)
+    s0 = O.apply_rope(q, t64, grid, split) @ O.apply_rope(k, t64, grid, split).T
+    s1 = O.apply_rope(q, p64, grid, split) @ O.apply_rope(k, p64, grid, split).T
+    assert np.allclose(s0, s1, rtol=0, atol=1e-10 * np.abs(s0).max())
+    # a phase applied to K only is not a rotation of both: scores change
+    s2 = O.apply_rope(q, t64, grid, split) @ O.apply_rope(k, p64, grid, split).T
+    assert np.abs(s2 - s0).max() > 1e-3 * np.abs(s0).max()
+
+
+def test_zero_phases_give_plain_tables_and_float32_is_correctly_rounded():
+    grid, split = (6, 7, 9), (44, 42, 42)
+    zero = [np.zeros(w // 2) for w in split]
+    for (a, b), (c, d) in zip(O.all_rope_tables(grid, split, phases=zero),
+                              O.all_rope_tables(grid, split)):
+        assert np.array_equal(a, c) and np.array_equal(b, d)
+    phases = synth.mergeable_phases(split)
+    for e, w, ph, (cs, sn) in zip(grid, split, phases,
+                                  O.all_rope_tables(grid, split, phases=phases)):
+        j = np.arange(w // 2)
+        ang = np.arange(e)[:, None] * (10000.0 ** (-2.0 * j / w))[None, :] + ph[None, :]
+        for tab, ref in ((cs, np.cos(ang)), (sn, np.sin(ang))):
+            # numpy's float64 cos/sin (an independent evaluation) within half an
+            # ulp of the float32 entry, plus float64 rounding slack
+            ulp = np.spacing(np.abs(tab).astype(np.float32)).astype(np.float64)
+            assert np.all(np.abs(tab.astype(np.float64) - ref) <= 0.5 * ulp + 1e-12)
+
+
+def test_prepare_without_rotation_equals_identity_rotation():
+    """mats32 None (merged) and identity matrices through the fp64 rotation
+    give the same codes: rotation by I is exact."""
+    cfg = synth.CONFIGS["small"]
+    q, k, v = synth.head_qkv(cfg, 0, 0, 3)
+    tab = O.all_rope_tables(cfg.grid, cfg.split, phases=synth.mergeable_phases(cfg.split))
+    eye = [np.eye(w, dtype=np.float32) for w in cfg.split]
+    a = O.prepare_head(q, k, v, tab, None, cfg.grid, cfg.split)
+    b = O.prepare_head(q, k, v, tab, eye, cfg.grid, cfg.split)
+    for key in ("q_codes", "k_codes", "v_codes", "q_scale_l2", "k_scale", "v_scale"):
+        assert np.array_equal(a[key], b[key]), key

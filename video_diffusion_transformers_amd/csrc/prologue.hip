@@ -208,6 +208,61 @@ __device__ __forceinline__ float rotate_tensor(const uint32_t* xs, const float* 
   return amax;
 }
 
+// RoPE only, for rotations merged into the RoPE tables (per-pair 2x2
+// rotations commute with RoPE, so R RoPE(p) = RoPE with phase offsets):
+// z = y = RoPE(x) exactly as the rotating path computes its A fragments, kept
+// in that layout (token tok0 + 16 tb + l%16, channel 4 ks + l/16).  Returns
+// the lane's max |z|.
+template <int DA, int kRS>
+__device__ __forceinline__ float rope_tensor(const uint32_t* xs, const float* cos_a,
+                                             const float* sin_a, int off, int tok0, int n0, int N,
+                                             int axis, int HW, int gh, int gw,
+                                             float (&z)[4][Part<DA>::KS]) {
+  constexpr int KS = Part<DA>::KS;
+  const int l = threadIdx.x & 63;
+  float amax = 0.0f;
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const int i = tok0 + 16 * tb + (l & 15);
+    const int n = n0 + i;
+    const int pos = n < N ? (axis == 0 ? n / HW : (axis == 1 ? (n / gw) % gh : n % gw)) : 0;
+    const uint32_t* xrow = xs + i * kRS + off / 2;
+    const float* crow = cos_a + pos * (DA / 2);
+    const float* srow = sin_a + pos * (DA / 2);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = 4 * ks + (l >> 4);
+      const int jp = (c >> 1) < DA / 2 ? (c >> 1) : DA / 2 - 1;
+      const uint32_t pr = xrow[jp];
+      const float x0 = h2f((uint16_t)(pr & 0xffffu));
+      const float x1 = h2f((uint16_t)(pr >> 16));
+      const float cs = crow[jp], sn = srow[jp];
+      const bool odd = (c & 1) != 0;
+      const float p0 = x0 * (odd ? sn : cs);
+      const float p1 = x1 * (odd ? cs : sn);
+      const float y = p0 + (odd ? p1 : -p1);
+      z[tb][ks] = c < DA ? y : 0.0f;
+      amax = fmaxf(amax, fabsf(z[tb][ks]));
+    }
+  }
+  return amax;
+}
+
+// Codes of rope_tensor's z (A layout) into the LDS code buffer.
+template <int DA, bool F8>
+__device__ __forceinline__ void quant_tensor_a(const float (&z)[4][Part<DA>::KS], float inv,
+                                               int off, int tok0, int8_t* codes) {
+  const int l = threadIdx.x & 63;
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int ks = 0; ks < Part<DA>::KS; ++ks) {
+      const int c = 4 * ks + (l >> 4);
+      if (c < DA)
+        codes[(tok0 + 16 * tb + (l & 15)) * kCodeStride + off + c] = code_byte<F8>(quant(z[tb][ks], inv));
+    }
+}
+
 // Codes of one tensor's z (MFMA output layout) into the LDS code buffer
 // ([token][channel], kCodeStride bytes per row).
 template <int DA, bool F8>
@@ -368,7 +423,7 @@ __device__ __forceinline__ void store_v_codes(const int8_t* codesT, uint8_t* dst
 // the MFMA, block amax, codes into the LDS buffer that held the tensor's rows,
 // coalesced store; then V: block amax and codes, stored transposed.  Every
 // wave runs the same sequence of barriers whatever its partition.
-template <int D, int DA, bool F8>
+template <int D, int DA, bool F8, bool ROT>
 __device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* stage_q,
                                             uint32_t* stage_k, float* red, int blk, int bh,
                                             int off, int axis, const float* cos_a,
@@ -384,21 +439,29 @@ __device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* sta
   load_tile<D>(a.q + head_tok * D, n0, a.N, stage_q);
   load_tile<D>(a.k + head_tok * D, n0, a.N, stage_k);
   float b[Part<DA>::KS][Part<DA>::JB];   // R_a^T of this wave's partition
-  load_rot_frags<DA>(rot, b);
+  if (ROT) load_rot_frags<DA>(rot, b);
   __syncthreads();
 
 #pragma unroll 1
   for (int s = 0; s < 2; ++s) {
     uint32_t* xs = s == 0 ? stage_q : stage_k;
-    float z[4][Part<DA>::JB][4];
-    const float amax = rotate_tensor<DA, kRS>(xs, cos_a, sin_a, b, off, tok0, n0, a.N, axis, HW,
-                                              a.grid_h, a.grid_w, z);
+    int8_t* codes = (int8_t*)xs;
     float inv, scale;
     // every wave is past its last read of xs once the reduction's barriers are
     // passed: the buffer takes the codes next
-    block_scale(amax, red, inv, scale);
-    int8_t* codes = (int8_t*)xs;
-    quant_tensor<DA, F8>(z, inv, off, tok0, codes);
+    if (ROT) {
+      float z[4][Part<DA>::JB][4];
+      const float amax = rotate_tensor<DA, kRS>(xs, cos_a, sin_a, b, off, tok0, n0, a.N, axis, HW,
+                                                a.grid_h, a.grid_w, z);
+      block_scale(amax, red, inv, scale);
+      quant_tensor<DA, F8>(z, inv, off, tok0, codes);
+    } else {
+      float z[4][Part<DA>::KS];
+      const float amax = rope_tensor<DA, kRS>(xs, cos_a, sin_a, off, tok0, n0, a.N, axis, HW,
+                                              a.grid_h, a.grid_w, z);
+      block_scale(amax, red, inv, scale);
+      quant_tensor_a<DA, F8>(z, inv, off, tok0, codes);
+    }
     __syncthreads();
     if (F8)
       store_qk_codes_f8<D>(codes, (s == 0 ? a.q4 : a.k4) + pad_row * D);
@@ -469,7 +532,7 @@ __device__ __forceinline__ void prologue_fallback(const PrologueArgs& a, uint32_
 
 // 3 waves per SIMD: two 6-wave work-groups per CU, so that one group's MFMA
 // phase overlaps the other's memory phases.
-template <int D, int D0, int D1, bool F8>
+template <int D, int D0, int D1, bool F8, bool ROT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void k_prologue(PrologueArgs a) {
   static_assert(D0 + 2 * D1 == D, "split must be (D0, D1, D1)");
@@ -489,30 +552,39 @@ void k_prologue(PrologueArgs a) {
   // t at 0, h at D0^2, w at D0^2 + D1^2
   const int part = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) >> 1);
   if (part == 0)
-    prologue_qk<D, D0, F8>(a, stage_q, stage_k, red, blk, bh, 0, 0, a.cos_t, a.sin_t, a.rot64);
+    prologue_qk<D, D0, F8, ROT>(a, stage_q, stage_k, red, blk, bh, 0, 0, a.cos_t, a.sin_t, a.rot64);
   else if (part == 1)
-    prologue_qk<D, D1, F8>(a, stage_q, stage_k, red, blk, bh, D0, 1, a.cos_h, a.sin_h,
-                           a.rot64 + D0 * D0);
+    prologue_qk<D, D1, F8, ROT>(a, stage_q, stage_k, red, blk, bh, D0, 1, a.cos_h, a.sin_h,
+                                a.rot64 + D0 * D0);
   else
-    prologue_qk<D, D1, F8>(a, stage_q, stage_k, red, blk, bh, D0 + D1, 2, a.cos_w, a.sin_w,
-                           a.rot64 + D0 * D0 + D1 * D1);
+    prologue_qk<D, D1, F8, ROT>(a, stage_q, stage_k, red, blk, bh, D0 + D1, 2, a.cos_w, a.sin_w,
+                                a.rot64 + D0 * D0 + D1 * D1);
 }
 
-hipError_t launch_prologue(int D, int dt, int BH, bool f8, const PrologueArgs& a, hipStream_t st) {
-  dim3 grid(a.NB, BH);
-  if (D == 128 && dt == 44) {
-    if (f8)
-      hipLaunchKernelGGL((k_prologue<128, 44, 42, true>), grid, dim3(kThreads), 0, st, a);
+template <int D, int D0, int D1>
+static void launch_prologue_t(bool f8, bool rot, dim3 grid, const PrologueArgs& a, hipStream_t st) {
+  if (f8) {
+    if (rot)
+      hipLaunchKernelGGL((k_prologue<D, D0, D1, true, true>), grid, dim3(kThreads), 0, st, a);
     else
-      hipLaunchKernelGGL((k_prologue<128, 44, 42, false>), grid, dim3(kThreads), 0, st, a);
-  } else if (D == 64 && dt == 24) {
-    if (f8)
-      hipLaunchKernelGGL((k_prologue<64, 24, 20, true>), grid, dim3(kThreads), 0, st, a);
-    else
-      hipLaunchKernelGGL((k_prologue<64, 24, 20, false>), grid, dim3(kThreads), 0, st, a);
+      hipLaunchKernelGGL((k_prologue<D, D0, D1, true, false>), grid, dim3(kThreads), 0, st, a);
   } else {
-    return hipErrorInvalidValue;
+    if (rot)
+      hipLaunchKernelGGL((k_prologue<D, D0, D1, false, true>), grid, dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_prologue<D, D0, D1, false, false>), grid, dim3(kThreads), 0, st, a);
   }
+}
+
+hipError_t launch_prologue(int D, int dt, int BH, bool f8, bool rot, const PrologueArgs& a,
+                           hipStream_t st) {
+  dim3 grid(a.NB, BH);
+  if (D == 128 && dt == 44)
+    launch_prologue_t<128, 44, 42>(f8, rot, grid, a, st);
+  else if (D == 64 && dt == 24)
+    launch_prologue_t<64, 24, 20>(f8, rot, grid, a, st);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -71,28 +71,39 @@ const char* rotattn_strerror(int status) {
   }
 }
 
-int rotattn_rope_tables_host(const rotattn_shape* s, double base, float* cos_t, float* sin_t,
-                             float* cos_h, float* sin_h, float* cos_w, float* sin_w) {
+int rotattn_rope_tables_phase_host(const rotattn_shape* s, double base, const double* phase_t,
+                                   const double* phase_h, const double* phase_w, float* cos_t,
+                                   float* sin_t, float* cos_h, float* sin_h, float* cos_w,
+                                   float* sin_w) {
   const int st = rotattn_validate(s);
   if (st != ROTATTN_OK) return st;
   if (!cos_t || !sin_t || !cos_h || !sin_h || !cos_w || !sin_w) return ROTATTN_E_NULL;
   if (!(base > 1.0)) return ROTATTN_E_ARG;
   const int ext[3] = {s->grid_t, s->grid_h, s->grid_w};
   const int wid[3] = {s->d_t, s->d_h, s->d_w};
+  const double* ph[3] = {phase_t, phase_h, phase_w};
   float* cs[3] = {cos_t, cos_h, cos_w};
   float* sn[3] = {sin_t, sin_h, sin_w};
   for (int a = 0; a < 3; ++a) {
     const int half = wid[a] / 2;
     for (int j = 0; j < half; ++j) {
       const long double theta = powl((long double)base, -2.0L * j / (long double)wid[a]);
+      const long double phi = ph[a] ? (long double)ph[a][j] : 0.0L;
+      if (ph[a] && !isfinite(ph[a][j])) return ROTATTN_E_ARG;
       for (int p = 0; p < ext[a]; ++p) {
-        const long double ang = (long double)p * theta;
+        const long double ang = (long double)p * theta + phi;
         cs[a][p * half + j] = (float)cosl(ang);
         sn[a][p * half + j] = (float)sinl(ang);
       }
     }
   }
   return ROTATTN_OK;
+}
+
+int rotattn_rope_tables_host(const rotattn_shape* s, double base, float* cos_t, float* sin_t,
+                             float* cos_h, float* sin_h, float* cos_w, float* sin_w) {
+  return rotattn_rope_tables_phase_host(s, base, nullptr, nullptr, nullptr, cos_t, sin_t, cos_h,
+                                        sin_h, cos_w, sin_w);
 }
 
 int rotattn_pcode_thresholds_host(float tau[15]) {
@@ -165,16 +176,19 @@ int rotattn_prepare_qkv(const rotattn_shape* s, const uint16_t* q, const uint16_
   const int st = rotattn_validate(s);
   if (st != ROTATTN_OK) return st;
   if (!q || !k || !v || !rr || !out) return ROTATTN_E_NULL;
-  if (!rr->cos_t || !rr->sin_t || !rr->cos_h || !rr->sin_h || !rr->cos_w || !rr->sin_w ||
-      !rr->rot_t || !rr->rot_h || !rr->rot_w)
+  if (!rr->cos_t || !rr->sin_t || !rr->cos_h || !rr->sin_h || !rr->cos_w || !rr->sin_w)
     return ROTATTN_E_NULL;
+  // all three rotation matrices, or none (rotation merged into the tables)
+  const int n_rot = (rr->rot_t != nullptr) + (rr->rot_h != nullptr) + (rr->rot_w != nullptr);
+  if (n_rot != 0 && n_rot != 3) return ROTATTN_E_NULL;
+  const bool rot = n_rot == 3;
   const int BH = s->B * s->H;
   if (out->layout != ROTATTN_LAYOUT_PACKED && out->layout != ROTATTN_LAYOUT_FP8) return ROTATTN_E_ARG;
   int n_fb = 0;
   const HeadBits fb = make_bits(fallback_mask_host, BH, true, false, &n_fb);
   if (n_fb < BH) {
     if (!out->q4 || !out->k4 || !out->v4 || !out->q_scale_l2 || !out->k_scale || !out->v_scale ||
-        !out->rot64)
+        (rot && !out->rot64))
       return ROTATTN_E_NULL;
     if (!aligned16(out->q4) || !aligned16(out->k4) || !aligned16(out->v4)) return ROTATTN_E_ALIGN;
   }
@@ -185,7 +199,7 @@ int rotattn_prepare_qkv(const rotattn_shape* s, const uint16_t* q, const uint16_
   }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return ROTATTN_E_ALIGN;
 
-  if (n_fb < BH && launch_rot_to_f64(rr->rot_t, rr->rot_h, rr->rot_w, s->d_t, s->d_h, out->rot64,
+  if (rot && n_fb < BH && launch_rot_to_f64(rr->rot_t, rr->rot_h, rr->rot_w, s->d_t, s->d_h, out->rot64,
                                      stream) != hipSuccess)
     return ROTATTN_E_HIP;
   PrologueArgs a;
@@ -203,7 +217,8 @@ int rotattn_prepare_qkv(const rotattn_shape* s, const uint16_t* q, const uint16_
   a.grid_w = s->grid_w;
   a.kappa = rotattn_kappa_host(s->D);
   a.fallback = fb;
-  return launch_prologue(s->D, s->d_t, BH, out->layout == ROTATTN_LAYOUT_FP8, a, stream) == hipSuccess
+  return launch_prologue(s->D, s->d_t, BH, out->layout == ROTATTN_LAYOUT_FP8, rot, a, stream) ==
+                 hipSuccess
              ? ROTATTN_OK
              : ROTATTN_E_HIP;
 }

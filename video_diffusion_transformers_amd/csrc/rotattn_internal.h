@@ -40,7 +40,8 @@ __device__ __forceinline__ uint32_t pack_nibbles(uint32_t lo4, uint32_t hi4) {
 struct PrologueArgs {
   const uint16_t *q, *k, *v;
   const float *cos_t, *sin_t, *cos_h, *sin_h, *cos_w, *sin_w;
-  const double* rot64;          // rotation in fp64, [k][r] per partition (t at 0, h at d_t^2, w next)
+  const double* rot64;          // rotation in fp64, [k][r] per partition (t at 0, h at d_t^2, w next);
+                                // unused by the kernels without a dense rotation
   uint8_t *q4, *k4, *v4;
   float *q_scale_l2, *k_scale, *v_scale;
   uint16_t *q_rope, *k_rope, *v_t;   // fallback heads: [BH][N_pad][D], V^T tiles
@@ -79,7 +80,8 @@ struct Fp16Args {
 // Launchers (each defined next to its kernel).  Return a hipError_t.
 hipError_t launch_rot_to_f64(const float* rt, const float* rh, const float* rw, int dt, int dh,
                              double* out, hipStream_t st);
-hipError_t launch_prologue(int D, int dt, int BH, bool f8, const PrologueArgs& a, hipStream_t st);
+hipError_t launch_prologue(int D, int dt, int BH, bool f8, bool rot, const PrologueArgs& a,
+                           hipStream_t st);
 hipError_t launch_int4(int D, int BH, const Int4Args& a, const Int4Debug* dbg, hipStream_t st);
 hipError_t launch_int4_f8(int D, int BH, const Int4Args& a, const Int4Debug* dbg, hipStream_t st);
 hipError_t launch_fp16(int D, int BH, const Fp16Args& a, hipStream_t st);

@@ -29,6 +29,7 @@ STATUS = {0: "ok", -1: "null pointer argument", -2: "inconsistent shape",
           -7: "argument out of range"}
 
 EXPORTS = ["rotattn_validate", "rotattn_strerror", "rotattn_rope_tables_host",
+           "rotattn_rope_tables_phase_host",
            "rotattn_pcode_thresholds_host", "rotattn_kappa_host", "rotattn_prepared_bytes",
            "rotattn_prepared_carve", "rotattn_prepare_qkv", "rotattn_int4_fwd", "rotattn_fp16_fwd",
            "rotattn_workspace_bytes", "rotattn_mixed_fwd", "rotattn_pcode_sweep",
@@ -78,6 +79,7 @@ def lib() -> C.CDLL:
             "rotattn_validate": (C.c_int, [S]),
             "rotattn_strerror": (C.c_char_p, [C.c_int]),
             "rotattn_rope_tables_host": (C.c_int, [S, C.c_double] + [P] * 6),
+            "rotattn_rope_tables_phase_host": (C.c_int, [S, C.c_double] + [P] * 9),
             "rotattn_pcode_thresholds_host": (C.c_int, [P]),
             "rotattn_kappa_host": (C.c_float, [C.c_int32]),
             "rotattn_prepared_bytes": (C.c_size_t, [S, C.c_int, C.c_int]),
@@ -125,13 +127,24 @@ def n_blocks(shape: Shape) -> int:
 
 # ------------------------------------------------------------------ host constants
 
-def rope_tables(shape: Shape, base: float = 10000.0):
-    """Host float32 RoPE tables [(cos_t, sin_t), (cos_h, sin_h), (cos_w, sin_w)]."""
+def rope_tables(shape: Shape, base: float = 10000.0, phases=None):
+    """Host float32 RoPE tables [(cos_t, sin_t), (cos_h, sin_h), (cos_w, sin_w)];
+    phases: three float64 arrays of d_a/2 pair phase offsets (a merged
+    rotation), or None."""
     ext = (shape.grid_t, shape.grid_h, shape.grid_w)
     wid = (shape.d_t, shape.d_h, shape.d_w)
     arrs = [np.zeros((e, w // 2), np.float32) for e, w in zip(ext, wid) for _ in range(2)]
     ptrs = [a.ctypes.data_as(C.c_void_p) for a in arrs]
-    check(lib().rotattn_rope_tables_host(C.byref(shape), C.c_double(base), *ptrs), "rope_tables")
+    if phases is None:
+        check(lib().rotattn_rope_tables_host(C.byref(shape), C.c_double(base), *ptrs), "rope_tables")
+    else:
+        ph = [np.ascontiguousarray(x, np.float64) for x in phases]
+        for x, w in zip(ph, wid):
+            if x.shape != (w // 2,):
+                raise ValueError(f"phase array of shape {x.shape}, expected ({w // 2},)")
+        pp = [x.ctypes.data_as(C.c_void_p) for x in ph]
+        check(lib().rotattn_rope_tables_phase_host(C.byref(shape), C.c_double(base), *pp, *ptrs),
+              "rope_tables_phase")
     return [(arrs[0], arrs[1]), (arrs[2], arrs[3]), (arrs[4], arrs[5])]
 
 
@@ -170,16 +183,22 @@ def _mask_arg(mask):
 
 
 class RopeRotDevice:
-    """Device copies of the RoPE tables and rotation matrices (fp32)."""
+    """Device copies of the RoPE tables and rotation matrices (fp32).
+    rot32=None: no dense rotation (with phases: the rotation merged into RoPE)."""
 
-    def __init__(self, shape: Shape, rot32, base: float = 10000.0, device="cuda"):
+    def __init__(self, shape: Shape, rot32, base: float = 10000.0, device="cuda", phases=None):
         torch = _torch()
-        tabs = rope_tables(shape, base)
+        tabs = rope_tables(shape, base, phases)
         self.tensors = [torch.from_numpy(np.ascontiguousarray(x)).to(device)
                         for pair in tabs for x in pair]
-        self.tensors += [torch.from_numpy(np.ascontiguousarray(r, np.float32)).to(device)
-                         for r in rot32]
-        self.struct = RopeRot(*[t.data_ptr() for t in self.tensors])
+        ptrs = [t.data_ptr() for t in self.tensors]
+        if rot32 is not None:
+            rots = [torch.from_numpy(np.ascontiguousarray(r, np.float32)).to(device) for r in rot32]
+            self.tensors += rots
+            ptrs += [t.data_ptr() for t in rots]
+        else:
+            ptrs += [0, 0, 0]
+        self.struct = RopeRot(*ptrs)
 
 
 class PreparedDevice:

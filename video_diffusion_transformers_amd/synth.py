@@ -37,6 +37,7 @@ TENSOR_Q, TENSOR_K, TENSOR_V = 0, 1, 2
 ROTATION_SEED = 7          # SeedSequence([7, partition]) for the default rotation
 ROW_SAMPLE_SALT = 555      # SeedSequence([cfg_seed, 555, h]) for sampled query rows
 MASK_SALT = 999            # SeedSequence([cfg_seed, 999]) for the fallback mask
+PHASE_SALT = 444           # SeedSequence([seed, 444, partition]) for merged-rotation phases
 STRUCTURE_SALT = 333       # SeedSequence([cfg_seed, 333, b, h]) for a head's Q/K channel scales
 LOGIT_STD = 2.5            # nats: spread of q.k/sqrt(D) over independent rows ("video")
 
@@ -186,6 +187,14 @@ def rotation_matrices(split, seed: int = ROTATION_SEED):
         r64.append(np.ascontiguousarray(qm))
         r32.append(np.ascontiguousarray(qm.astype(np.float32)))
     return r64, r32
+
+
+def mergeable_phases(split, seed: int = ROTATION_SEED):
+    """Seeded per-pair angles, uniform in [0, 2 pi), one float64 array of d_a/2
+    per RoPE partition: the default rotation to merge into the RoPE tables.
+    Stream: SeedSequence([seed, PHASE_SALT, partition])."""
+    return [_rng(seed, PHASE_SALT, a).uniform(0.0, 2.0 * np.pi, size=width // 2)
+            for a, width in enumerate(split)]
 
 
 def fallback_mask(cfg: Config) -> np.ndarray:
