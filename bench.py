@@ -233,6 +233,9 @@ def main():
     del qd, kd, vd, prep, o
     torch.cuda.empty_cache()
 
+    dit = None
+    if not args.no_extras and args.workload == "720p":
+        dit = bench_dit_block(cfg)
     mixed = None
     if args.mixed_steps and args.workload == "720p":
         mixed = bench_mixed(args.mixed_steps)
@@ -266,9 +269,53 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "mixed": mixed,
+        "dit_block": dit,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_dit_block(cfg, width: int = 5120, reps: int = 2):
+    """Side figure: a synthetic DiT self-attention block at the 720p shape with
+    model width 5120 (40 heads x 128): QKV projection GEMM, attention, output
+    projection GEMM (fp16 GEMMs on hipBLASLt, seeded random weights).  INT4
+    attention with the prologue reading the projection's token-major output in
+    place and O written token-major, against the same block with contiguous
+    copies around the attention, and against FP16 attention on every head."""
+    import torch
+    from video_diffusion_transformers_amd import dit_block, rotattn as R, synth
+    shape = R.shape_of(cfg)
+    _, r32 = synth.rotation_matrices(cfg.split)
+    blk = dit_block.DiTAttentionBlock(shape, width, R.RopeRotDevice(shape, r32), seed=5)
+    g = torch.Generator(device="cpu").manual_seed(6)
+    x = torch.randn(cfg.B, cfg.N, width, generator=g).half().cuda()
+    res = {}
+    for key, kw in (("int4_fused_ms", dict(fp16=False, fused=True)),
+                    ("int4_unfused_ms", dict(fp16=False, fused=False)),
+                    ("fp16_fused_ms", dict(fp16=True, fused=True))):
+        blk.forward(x, **kw)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            blk.forward(x, **kw)
+        e1.record()
+        torch.cuda.synchronize()
+        res[key] = round(e0.elapsed_time(e1) / reps, 3)
+    # the projections alone
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(x, blk.w_qkv, out=blk.qkv)
+        torch.matmul(blk.o_tok.view(cfg.B, cfg.N, -1), blk.w_o)
+    e1.record()
+    torch.cuda.synchronize()
+    res["projections_ms"] = round(e0.elapsed_time(e1) / reps, 3)
+    res["int4_vs_fp16_block_speedup"] = round(res["fp16_fused_ms"] / res["int4_fused_ms"], 3)
+    print(f"[bench] DiT block: {res}", file=sys.stderr, flush=True)
+    del blk, x
+    torch.cuda.empty_cache()
+    return dict(workload=f"720p shape, width {width}, QKV projection + attention + output "
+                         f"projection, random weights (timing only)", **res)
 
 
 def bench_mixed(steps: int):

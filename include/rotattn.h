@@ -89,6 +89,21 @@ typedef struct rotattn_rope_rot {
 } rotattn_rope_rot;
 
 /*
+ * Element strides of an fp16 [B][H][N][D] tensor whose channel stride is 1:
+ * element (b, h, n, d) sits at b*batch + h*head + n*token + d.  A NULL
+ * rotattn_strides* means contiguous [B][H][N][D] ({H*N*D, N*D, D}).  The
+ * token-major output of a fused QKV projection, [B][N][3][H][D] with Q, K and
+ * V starting at element 0, H*D and 2*H*D, is {N*3*H*D, D, 3*H*D}; an output
+ * written as [B][N][H][D] for the output projection is {N*H*D, D, H*D}.
+ * Every stride must be a multiple of 8 (16-byte rows, ROTATTN_E_ALIGN) and
+ * token >= D (ROTATTN_E_ARG).  Outputs whose rows overlap are the caller's
+ * error (not detected).
+ */
+typedef struct rotattn_strides {
+  int64_t batch, head, token;
+} rotattn_strides;
+
+/*
  * Layout of the INT4 codes in a rotattn_prepared.
  *  ROTATTN_LAYOUT_PACKED: two codes per byte (4-bit two's complement); the
  *      attention kernel multiplies them on i8 MFMA.
@@ -221,6 +236,17 @@ int rotattn_prepare_qkv(const rotattn_shape* s, const uint16_t* q,
                         const uint8_t* fallback_mask_host,
                         const rotattn_prepared* out, hipStream_t stream);
 
+/* rotattn_prepare_qkv on q, k, v laid out with qkv_strides (shared by the
+ * three; NULL = contiguous), e.g. read straight from a fused QKV projection's
+ * token-major output with no transposition pass. */
+int rotattn_prepare_qkv_strided(const rotattn_shape* s, const uint16_t* q,
+                                const uint16_t* k, const uint16_t* v,
+                                const rotattn_strides* qkv_strides,
+                                const rotattn_rope_rot* rr,
+                                const uint8_t* fallback_mask_host,
+                                const rotattn_prepared* out,
+                                hipStream_t stream);
+
 /*
  * INT4 attention over the heads with fallback_mask_host[...] == 0 (all heads
  * when NULL): I = q4.k4^T (i8 MFMA for the PACKED layout, f8f6f4 MFMA for
@@ -234,6 +260,13 @@ int rotattn_int4_fwd(const rotattn_shape* s, const rotattn_prepared* p,
                      const uint8_t* fallback_mask_host, uint16_t* o,
                      const rotattn_debug* dbg, hipStream_t stream);
 
+/* rotattn_int4_fwd writing o with o_strides (NULL = contiguous), e.g. as the
+ * token-major [B][N][H][D] input of the output projection. */
+int rotattn_int4_fwd_strided(const rotattn_shape* s, const rotattn_prepared* p,
+                             const uint8_t* fallback_mask_host, uint16_t* o,
+                             const rotattn_strides* o_strides,
+                             const rotattn_debug* dbg, hipStream_t stream);
+
 /*
  * FP16 FlashAttention: O = softmax(Q'K'^T / sqrt(D)) V on fp16 MFMA with fp32
  * softmax and accumulation, for the heads with head_select_host[...] != 0
@@ -243,6 +276,12 @@ int rotattn_int4_fwd(const rotattn_shape* s, const rotattn_prepared* p,
 int rotattn_fp16_fwd(const rotattn_shape* s, const rotattn_prepared* p,
                      const uint8_t* head_select_host, uint16_t* o,
                      hipStream_t stream);
+
+/* rotattn_fp16_fwd writing o with o_strides (NULL = contiguous). */
+int rotattn_fp16_fwd_strided(const rotattn_shape* s, const rotattn_prepared* p,
+                             const uint8_t* head_select_host, uint16_t* o,
+                             const rotattn_strides* o_strides,
+                             hipStream_t stream);
 
 /* Workspace bytes for rotattn_mixed_fwd (a FP8-layout rotattn_prepared with
  * the fp16 fallback buffers). */
@@ -257,6 +296,18 @@ int rotattn_mixed_fwd(const rotattn_shape* s, const uint16_t* q,
                       const rotattn_rope_rot* rr,
                       const uint8_t* fallback_mask_host, void* workspace,
                       size_t workspace_bytes, uint16_t* o, hipStream_t stream);
+
+/* rotattn_mixed_fwd with input strides (shared by q, k, v) and output strides
+ * (NULL = contiguous): one call between a fused QKV projection and the output
+ * projection with no layout passes. */
+int rotattn_mixed_fwd_strided(const rotattn_shape* s, const uint16_t* q,
+                              const uint16_t* k, const uint16_t* v,
+                              const rotattn_strides* qkv_strides,
+                              const rotattn_rope_rot* rr,
+                              const uint8_t* fallback_mask_host,
+                              void* workspace, size_t workspace_bytes,
+                              uint16_t* o, const rotattn_strides* o_strides,
+                              hipStream_t stream);
 
 /*
  * Self-test of the P-code device function (the exact code the attention

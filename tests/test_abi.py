@@ -133,3 +133,27 @@ def test_prepare_rejects_partial_rotation_pointers():
     p = R.Prepared()
     assert L.rotattn_prepare_qkv(C.byref(s), fake, fake, fake, C.byref(rr), None, C.byref(p),
                                  C.c_void_p(0)) == -1
+
+
+def test_strided_entry_points_validate_strides():
+    """Bad strides are refused before anything is launched."""
+    L = R.lib()
+    s = R.make_shape(1, 2, (2, 4, 4), 64, (24, 20, 20))
+    fake = C.c_void_p(1 << 20)
+    p = R.Prepared()
+    short = R.Strides(2 * 32 * 64, 32 * 64, 32)        # token stride < D
+    odd = R.Strides(2 * 32 * 64, 32 * 64 + 4, 64)       # not a multiple of 8
+    for st, code in ((short, -7), (odd, -5)):
+        assert L.rotattn_int4_fwd_strided(C.byref(s), C.byref(p), None, fake, C.byref(st), None,
+                                          C.c_void_p(0)) in (-1, code)
+        assert L.rotattn_fp16_fwd_strided(C.byref(s), C.byref(p), None, fake, C.byref(st),
+                                          C.c_void_p(0)) in (-1, code)
+        assert L.rotattn_mixed_fwd_strided(C.byref(s), fake, fake, fake, None, None, None, fake,
+                                           1 << 30, fake, C.byref(st), C.c_void_p(0)) == -1
+    # with valid everything else, a bad output stride is reported as such
+    ws = R.lib().rotattn_workspace_bytes(C.byref(s))
+    rr = R.RopeRot(*([fake] * 9))
+    for st, code in ((short, -7), (odd, -5)):
+        assert L.rotattn_mixed_fwd_strided(C.byref(s), fake, fake, fake, None, C.byref(rr), None,
+                                           C.c_void_p(1 << 24), ws, fake, C.byref(st),
+                                           C.c_void_p(0)) == code

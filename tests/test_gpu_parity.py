@@ -230,6 +230,55 @@ def test_merged_rotation_prologue_and_output(name, layout):
     check_out(og[bh][rows], run.oracle_int4(bh, rows)[0], f"{name} merged head {bh}")
 
 
+# ------------------------------------------------------------------ strided layouts (DiT block)
+
+@pytest.mark.parametrize("name", ["tiny", "small", "rag306"])
+def test_token_major_layouts_equal_contiguous(name):
+    """Q, K, V read in place from a fused projection's token-major output and O
+    written token-major give the same bits as the contiguous layout, for INT4
+    and FP16 heads (one call of mixed_fwd each)."""
+    torch = torch_cuda()
+    from video_diffusion_transformers_amd import rotattn as R
+    cfg = (synth.custom_config("rag306", 2, 2, (2, 9, 17), 128, (44, 42, 42), cfg_seed=33)
+           if name == "rag306" else synth.CONFIGS[name])
+    run = Run(cfg)
+    B, H, N, D = cfg.B, cfg.H, cfg.N, cfg.D
+    mask = np.zeros(cfg.BH, np.uint8)
+    mask[1] = 1
+    ws = torch.empty(R.workspace_bytes(run.shape), dtype=torch.uint8, device="cuda")
+    o_ref = run.empty_out()
+    R.mixed_fwd(run.shape, run.q, run.k, run.v, run.rr, mask, ws, o_ref)
+    qkv = torch.empty((B, N, 3, H, D), dtype=torch.float16, device="cuda")
+    for i, x in enumerate((run.q, run.k, run.v)):
+        qkv[:, :, i] = x.permute(0, 2, 1, 3)
+    q, k, v = qkv.permute(2, 0, 3, 1, 4)
+    assert R.strides_of(q).token == 3 * H * D
+    o_tok = torch.full((B, N, H, D), float("nan"), dtype=torch.float16, device="cuda")
+    R.mixed_fwd(run.shape, q, k, v, run.rr, mask, ws, o_tok.permute(0, 2, 1, 3))
+    torch.cuda.synchronize()
+    got = o_tok.permute(0, 2, 1, 3).cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), o_ref.cpu().numpy().view(np.uint16))
+
+
+def test_dit_block_fused_equals_unfused():
+    """The synthetic DiT block: strided (no layout passes) and contiguous-copy
+    forms give the same bits, for the INT4 and the FP16 attention."""
+    torch = torch_cuda()
+    from video_diffusion_transformers_amd import dit_block, rotattn as R
+    cfg = synth.CONFIGS["small"]
+    shape = R.shape_of(cfg)
+    _, r32 = synth.rotation_matrices(cfg.split)
+    blk = dit_block.DiTAttentionBlock(shape, 512, R.RopeRotDevice(shape, r32), seed=3)
+    g = torch.Generator(device="cpu").manual_seed(4)
+    x = torch.randn(cfg.B, cfg.N, 512, generator=g).half().cuda()
+    for fp16 in (False, True):
+        a = blk.forward(x, fp16=fp16, fused=True).clone()
+        b = blk.forward(x, fp16=fp16, fused=False)
+        torch.cuda.synchronize()
+        assert torch.isfinite(a).all()
+        assert torch.equal(a, b), fp16
+
+
 # ------------------------------------------------------------------ FP16 fallback
 
 @pytest.mark.parametrize("name", ["tiny", "small", "720p"])

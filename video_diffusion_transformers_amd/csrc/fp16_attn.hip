@@ -202,7 +202,7 @@ struct Fp16Kernel {
     const int query = qb * kBlock + 32 * w + col;
     if (query < N) {
       const float il = 1.0f / l;
-      uint16_t* orow = a.o + ((size_t)bh * N + query) * D;
+      uint16_t* orow = a.o + a.os.head_offset(bh, a.H) + (int64_t)query * a.os.token;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll

@@ -420,7 +420,7 @@ struct Int4Kernel {
     }
     if (query < a.N) {
       const float il = 1.0f / l;
-      uint16_t* orow = a.o + ((size_t)bh * a.N + query) * D;
+      uint16_t* orow = a.o + a.os.head_offset(bh, a.H) + (int64_t)query * a.os.token;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -745,7 +745,7 @@ struct Int4F8Kernel {
     }
     if (query < a.N) {
       const float il = u / l;
-      uint16_t* orow = a.o + ((size_t)bh * a.N + query) * D;
+      uint16_t* orow = a.o + a.os.head_offset(bh, a.H) + (int64_t)query * a.os.token;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll

@@ -321,13 +321,14 @@ __device__ __forceinline__ void v_part(const uint32_t* xrow, int off, float* red
 // dwords (the odd stride keeps the per-token reads conflict-free); rows past
 // N are zero.
 template <int D>
-__device__ __forceinline__ void load_tile(const uint16_t* src, int n0, int N, uint32_t* xs) {
+__device__ __forceinline__ void load_tile(const uint16_t* src, int64_t row_stride, int n0, int N,
+                                          uint32_t* xs) {
   constexpr int kChunks = D / 8;           // 16-byte chunks per row
   constexpr int kRS = D / 2 + 1;
   for (int i = threadIdx.x; i < kBlock * kChunks; i += kThreads) {
     const int r = i / kChunks, c = i % kChunks;
     uint4 v = uint4{0, 0, 0, 0};
-    if (n0 + r < N) v = *(const uint4*)(src + (size_t)(n0 + r) * D + 8 * c);
+    if (n0 + r < N) v = *(const uint4*)(src + (int64_t)(n0 + r) * row_stride + 8 * c);
     uint32_t* d = xs + r * kRS + 4 * c;
     d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
   }
@@ -433,11 +434,11 @@ __device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* sta
   const int tok0 = (w & 1) * 64;
   const int n0 = blk * kBlock;
   const int HW = a.grid_h * a.grid_w;
-  const size_t head_tok = (size_t)bh * a.N;
+  const int64_t head_in = a.in.head_offset(bh, a.H);
   const size_t pad_row = ((size_t)bh * a.NB + blk) * kBlock;   // first code row of this block
 
-  load_tile<D>(a.q + head_tok * D, n0, a.N, stage_q);
-  load_tile<D>(a.k + head_tok * D, n0, a.N, stage_k);
+  load_tile<D>(a.q + head_in, a.in.token, n0, a.N, stage_q);
+  load_tile<D>(a.k + head_in, a.in.token, n0, a.N, stage_k);
   float b[Part<DA>::KS][Part<DA>::JB];   // R_a^T of this wave's partition
   if (ROT) load_rot_frags<DA>(rot, b);
   __syncthreads();
@@ -478,7 +479,7 @@ __device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* sta
 
   // V: staged in the Q buffer, codes (channel rows) in the K buffer
   const int nl = tok0 + (threadIdx.x & 63);
-  load_tile<D>(a.v + head_tok * D, n0, a.N, stage_q);
+  load_tile<D>(a.v + head_in, a.in.token, n0, a.N, stage_q);
   __syncthreads();
   int8_t* codes = (int8_t*)stage_k;
   float scale;
@@ -508,14 +509,14 @@ __device__ __forceinline__ void prologue_fallback(const PrologueArgs& a, uint32_
   const int off = part == 0 ? 0 : (part == 1 ? D0 : D0 + D1);
   const float* cos_a = part == 0 ? a.cos_t : (part == 1 ? a.cos_h : a.cos_w);
   const float* sin_a = part == 0 ? a.sin_t : (part == 1 ? a.sin_h : a.sin_w);
-  const size_t head_tok = (size_t)bh * a.N;
+  const int64_t head_in = a.in.head_offset(bh, a.H);
   const size_t head_pad = (size_t)bh * a.NB * kBlock;
   uint32_t* xrow = stage + nl * kRS;
   // tables are read for every lane; clamp the position of a padding token
   const int pos_c = n < a.N ? pos : 0;
 #pragma unroll 1
   for (int s = 0; s < 2; ++s) {
-    load_tile<D>((s == 0 ? a.q : a.k) + head_tok * D, n0, a.N, stage);
+    load_tile<D>((s == 0 ? a.q : a.k) + head_in, a.in.token, n0, a.N, stage);
     __syncthreads();
     if (part == 0)
       rope_only_part<D0>(xrow, cos_a, sin_a, pos_c, off);
@@ -525,7 +526,7 @@ __device__ __forceinline__ void prologue_fallback(const PrologueArgs& a, uint32_
     store_tile_all<D>((s == 0 ? a.q_rope : a.k_rope) + head_pad * D, n0, stage);
     __syncthreads();
   }
-  load_tile<D>(a.v + head_tok * D, n0, a.N, stage);
+  load_tile<D>(a.v + head_in, a.in.token, n0, a.N, stage);
   __syncthreads();
   store_vt_tiles<D>(stage, a.v_t + (head_pad + n0) * D);
 }

@@ -169,10 +169,35 @@ int rotattn_prepared_carve(const rotattn_shape* s, void* base, size_t bytes, int
   return ROTATTN_OK;
 }
 
+// Strides of a tensor, contiguous [B][H][N][D] when st is NULL.  Every stride
+// must keep 16-byte rows (a multiple of 8 elements), and rows of one head must
+// not overlap (token >= D).
+static int resolve_strides(const rotattn_shape* s, const rotattn_strides* st, Strides* out) {
+  if (!st) {
+    out->batch = (int64_t)s->H * s->N * s->D;
+    out->head = (int64_t)s->N * s->D;
+    out->token = s->D;
+    return ROTATTN_OK;
+  }
+  if (st->batch < 0 || st->head < 0 || st->token < s->D) return ROTATTN_E_ARG;
+  if (st->batch % 8 || st->head % 8 || st->token % 8) return ROTATTN_E_ALIGN;
+  out->batch = st->batch;
+  out->head = st->head;
+  out->token = st->token;
+  return ROTATTN_OK;
+}
+
 int rotattn_prepare_qkv(const rotattn_shape* s, const uint16_t* q, const uint16_t* k,
                         const uint16_t* v, const rotattn_rope_rot* rr,
                         const uint8_t* fallback_mask_host, const rotattn_prepared* out,
                         hipStream_t stream) {
+  return rotattn_prepare_qkv_strided(s, q, k, v, nullptr, rr, fallback_mask_host, out, stream);
+}
+
+int rotattn_prepare_qkv_strided(const rotattn_shape* s, const uint16_t* q, const uint16_t* k,
+                                const uint16_t* v, const rotattn_strides* qkv_strides,
+                                const rotattn_rope_rot* rr, const uint8_t* fallback_mask_host,
+                                const rotattn_prepared* out, hipStream_t stream) {
   const int st = rotattn_validate(s);
   if (st != ROTATTN_OK) return st;
   if (!q || !k || !v || !rr || !out) return ROTATTN_E_NULL;
@@ -198,12 +223,17 @@ int rotattn_prepare_qkv(const rotattn_shape* s, const uint16_t* q, const uint16_
       return ROTATTN_E_ALIGN;
   }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return ROTATTN_E_ALIGN;
+  Strides in;
+  const int sr = resolve_strides(s, qkv_strides, &in);
+  if (sr != ROTATTN_OK) return sr;
 
   if (rot && n_fb < BH && launch_rot_to_f64(rr->rot_t, rr->rot_h, rr->rot_w, s->d_t, s->d_h, out->rot64,
                                      stream) != hipSuccess)
     return ROTATTN_E_HIP;
   PrologueArgs a;
   a.q = q; a.k = k; a.v = v;
+  a.in = in;
+  a.H = s->H;
   a.cos_t = rr->cos_t; a.sin_t = rr->sin_t;
   a.cos_h = rr->cos_h; a.sin_h = rr->sin_h;
   a.cos_w = rr->cos_w; a.sin_w = rr->sin_w;
@@ -226,9 +256,19 @@ int rotattn_prepare_qkv(const rotattn_shape* s, const uint16_t* q, const uint16_
 int rotattn_int4_fwd(const rotattn_shape* s, const rotattn_prepared* p,
                      const uint8_t* fallback_mask_host, uint16_t* o, const rotattn_debug* dbg,
                      hipStream_t stream) {
+  return rotattn_int4_fwd_strided(s, p, fallback_mask_host, o, nullptr, dbg, stream);
+}
+
+int rotattn_int4_fwd_strided(const rotattn_shape* s, const rotattn_prepared* p,
+                             const uint8_t* fallback_mask_host, uint16_t* o,
+                             const rotattn_strides* o_strides, const rotattn_debug* dbg,
+                             hipStream_t stream) {
   const int st = rotattn_validate(s);
   if (st != ROTATTN_OK) return st;
   if (!p || !o) return ROTATTN_E_NULL;
+  Strides os;
+  const int sr = resolve_strides(s, o_strides, &os);
+  if (sr != ROTATTN_OK) return sr;
   if (!p->q4 || !p->k4 || !p->v4 || !p->q_scale_l2 || !p->k_scale || !p->v_scale)
     return ROTATTN_E_NULL;
   if (!aligned16(p->q4) || !aligned16(p->k4) || !aligned16(p->v4) || !aligned16(o))
@@ -257,6 +297,8 @@ int rotattn_int4_fwd(const rotattn_shape* s, const rotattn_prepared* p,
   a.q4 = p->q4; a.k4 = p->k4; a.v4 = p->v4;
   a.q_scale_l2 = p->q_scale_l2; a.k_scale = p->k_scale; a.v_scale = p->v_scale;
   a.o = o;
+  a.os = os;
+  a.H = s->H;
   a.N = s->N;
   a.NB = nblocks(s);
   a.log2_15 = log2_15_f();
@@ -269,9 +311,18 @@ int rotattn_int4_fwd(const rotattn_shape* s, const rotattn_prepared* p,
 
 int rotattn_fp16_fwd(const rotattn_shape* s, const rotattn_prepared* p,
                      const uint8_t* head_select_host, uint16_t* o, hipStream_t stream) {
+  return rotattn_fp16_fwd_strided(s, p, head_select_host, o, nullptr, stream);
+}
+
+int rotattn_fp16_fwd_strided(const rotattn_shape* s, const rotattn_prepared* p,
+                             const uint8_t* head_select_host, uint16_t* o,
+                             const rotattn_strides* o_strides, hipStream_t stream) {
   const int st = rotattn_validate(s);
   if (st != ROTATTN_OK) return st;
   if (!p || !o) return ROTATTN_E_NULL;
+  Strides os;
+  const int sr = resolve_strides(s, o_strides, &os);
+  if (sr != ROTATTN_OK) return sr;
   if (!p->q_rope || !p->k_rope || !p->v_t) return ROTATTN_E_NULL;
   if (!aligned16(p->q_rope) || !aligned16(p->k_rope) || !aligned16(p->v_t) || !aligned16(o))
     return ROTATTN_E_ALIGN;
@@ -280,6 +331,8 @@ int rotattn_fp16_fwd(const rotattn_shape* s, const rotattn_prepared* p,
   Fp16Args a;
   a.run = make_bits(head_select_host, BH, true, true, &n_run);
   a.q = p->q_rope; a.k = p->k_rope; a.v_t = p->v_t; a.o = o;
+  a.os = os;
+  a.H = s->H;
   a.N = s->N;
   a.NB = nblocks(s);
   a.kappa = rotattn_kappa_host(s->D);
@@ -295,20 +348,32 @@ int rotattn_mixed_fwd(const rotattn_shape* s, const uint16_t* q, const uint16_t*
                       const uint16_t* v, const rotattn_rope_rot* rr,
                       const uint8_t* fallback_mask_host, void* workspace, size_t workspace_bytes,
                       uint16_t* o, hipStream_t stream) {
+  return rotattn_mixed_fwd_strided(s, q, k, v, nullptr, rr, fallback_mask_host, workspace,
+                                   workspace_bytes, o, nullptr, stream);
+}
+
+int rotattn_mixed_fwd_strided(const rotattn_shape* s, const uint16_t* q, const uint16_t* k,
+                              const uint16_t* v, const rotattn_strides* qkv_strides,
+                              const rotattn_rope_rot* rr, const uint8_t* fallback_mask_host,
+                              void* workspace, size_t workspace_bytes, uint16_t* o,
+                              const rotattn_strides* o_strides, hipStream_t stream) {
   const int st = rotattn_validate(s);
   if (st != ROTATTN_OK) return st;
   if (!q || !k || !v || !rr || !workspace || !o) return ROTATTN_E_NULL;
   rotattn_prepared p;
   const int cs = rotattn_prepared_carve(s, workspace, workspace_bytes, 1, ROTATTN_LAYOUT_FP8, &p);
   if (cs != ROTATTN_OK) return cs;
-  int r = rotattn_prepare_qkv(s, q, k, v, rr, fallback_mask_host, &p, stream);
+  Strides chk;
+  int r = resolve_strides(s, o_strides, &chk);
   if (r != ROTATTN_OK) return r;
-  r = rotattn_int4_fwd(s, &p, fallback_mask_host, o, nullptr, stream);
+  r = rotattn_prepare_qkv_strided(s, q, k, v, qkv_strides, rr, fallback_mask_host, &p, stream);
+  if (r != ROTATTN_OK) return r;
+  r = rotattn_int4_fwd_strided(s, &p, fallback_mask_host, o, o_strides, nullptr, stream);
   if (r != ROTATTN_OK) return r;
   if (fallback_mask_host) {
     int n_fb = 0;
     make_bits(fallback_mask_host, s->B * s->H, true, false, &n_fb);
-    if (n_fb > 0) r = rotattn_fp16_fwd(s, &p, fallback_mask_host, o, stream);
+    if (n_fb > 0) r = rotattn_fp16_fwd_strided(s, &p, fallback_mask_host, o, o_strides, stream);
   }
   return r;
 }

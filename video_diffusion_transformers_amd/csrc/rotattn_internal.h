@@ -37,8 +37,18 @@ __device__ __forceinline__ uint32_t pack_nibbles(uint32_t lo4, uint32_t hi4) {
   return (lo4 & 0x0F0F0F0Fu) | ((hi4 & 0x0F0F0F0Fu) << 4);
 }
 
+// Element strides of a [B][H][N][D] fp16 tensor with unit channel stride.
+struct Strides {
+  int64_t batch, head, token;
+  __host__ __device__ int64_t head_offset(int bh, int H) const {
+    return (int64_t)(bh / H) * batch + (int64_t)(bh % H) * head;
+  }
+};
+
 struct PrologueArgs {
   const uint16_t *q, *k, *v;
+  Strides in;                   // of q, k and v
+  int H;
   const float *cos_t, *sin_t, *cos_h, *sin_h, *cos_w, *sin_w;
   const double* rot64;          // rotation in fp64, [k][r] per partition (t at 0, h at d_t^2, w next);
                                 // unused by the kernels without a dense rotation
@@ -54,6 +64,8 @@ struct Int4Args {
   const uint8_t *q4, *k4, *v4;
   const float *q_scale_l2, *k_scale, *v_scale;
   uint16_t* o;
+  Strides os;                   // of o
+  int H;
   int N, NB;
   float log2_15;                // fl32(log2(15))
   float tau[15];                // P-code thresholds
@@ -72,6 +84,8 @@ struct Fp16Args {
   const uint16_t *q, *k;   // RoPE'd Q', K': [BH][N_pad][D], rows >= N zero
   const uint16_t* v_t;     // V^T per 64-key tile: [BH][N_pad/64][D][64], operand order
   uint16_t* o;
+  Strides os;              // of o
+  int H;
   int N, NB;
   float kappa;
   HeadBits run;

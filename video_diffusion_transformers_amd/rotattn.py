@@ -33,7 +33,8 @@ EXPORTS = ["rotattn_validate", "rotattn_strerror", "rotattn_rope_tables_host",
            "rotattn_pcode_thresholds_host", "rotattn_kappa_host", "rotattn_prepared_bytes",
            "rotattn_prepared_carve", "rotattn_prepare_qkv", "rotattn_int4_fwd", "rotattn_fp16_fwd",
            "rotattn_workspace_bytes", "rotattn_mixed_fwd", "rotattn_pcode_sweep",
-           "rotattn_pcode_eval"]
+           "rotattn_pcode_eval", "rotattn_prepare_qkv_strided", "rotattn_int4_fwd_strided",
+           "rotattn_fp16_fwd_strided", "rotattn_mixed_fwd_strided"]
 
 
 class Shape(C.Structure):
@@ -44,6 +45,10 @@ class Shape(C.Structure):
 class RopeRot(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("cos_t", "sin_t", "cos_h", "sin_h", "cos_w", "sin_w",
                                           "rot_t", "rot_h", "rot_w")]
+
+
+class Strides(C.Structure):
+    _fields_ = [("batch", C.c_int64), ("head", C.c_int64), ("token", C.c_int64)]
 
 
 class Prepared(C.Structure):
@@ -93,6 +98,14 @@ def lib() -> C.CDLL:
             "rotattn_mixed_fwd": (C.c_int, [S, P, P, P, C.POINTER(RopeRot), P, P, C.c_size_t, P, P]),
             "rotattn_pcode_sweep": (C.c_int, [C.c_int, C.c_uint32, C.c_uint32, P, C.c_uint32, P, P]),
             "rotattn_pcode_eval": (C.c_int, [C.c_int, P, C.c_uint32, C.c_float, C.c_float, P, P]),
+            "rotattn_prepare_qkv_strided": (C.c_int, [S, P, P, P, C.POINTER(Strides),
+                                                      C.POINTER(RopeRot), P, C.POINTER(Prepared), P]),
+            "rotattn_int4_fwd_strided": (C.c_int, [S, C.POINTER(Prepared), P, P,
+                                                   C.POINTER(Strides), C.POINTER(Debug), P]),
+            "rotattn_fp16_fwd_strided": (C.c_int, [S, P, P, P, C.POINTER(Strides), P]),
+            "rotattn_mixed_fwd_strided": (C.c_int, [S, P, P, P, C.POINTER(Strides),
+                                                    C.POINTER(RopeRot), P, P, C.c_size_t, P,
+                                                    C.POINTER(Strides), P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -175,6 +188,28 @@ def _stream(stream=None) -> C.c_void_p:
     return C.c_void_p(s.cuda_stream)
 
 
+def strides_of(t):
+    """Strides of a 4-D [B][H][N][D] torch view with unit channel stride, or
+    None for a contiguous tensor (the library's default layout)."""
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [B][H][N][D] view with unit channel stride")
+    if t.is_contiguous():
+        return None
+    return Strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _strides_arg(st):
+    return None if st is None else C.byref(st)
+
+
+def _shared_strides(q, k, v):
+    sq, sk, sv = (strides_of(x) for x in (q, k, v))
+    key = [None if x is None else (x.batch, x.head, x.token) for x in (sq, sk, sv)]
+    if not key[0] == key[1] == key[2]:
+        raise ValueError("q, k and v must share one layout")
+    return sq
+
+
 def _mask_arg(mask):
     if mask is None:
         return None, C.c_void_p(0)
@@ -230,25 +265,30 @@ class PreparedDevice:
 
 def prepare_qkv(shape: Shape, q, k, v, rr: RopeRotDevice, prep: PreparedDevice, mask=None,
                 stream=None) -> None:
+    """q, k, v: [B][H][N][D] fp16 tensors or views sharing one layout (e.g.
+    slices of a fused QKV projection's token-major output); no copies."""
     keep, m = _mask_arg(mask)
-    check(lib().rotattn_prepare_qkv(C.byref(shape), _ptr(q), _ptr(k), _ptr(v), C.byref(rr.struct),
-                                    m, C.byref(prep.struct), _stream(stream)), "prepare_qkv")
+    st = _shared_strides(q, k, v)
+    check(lib().rotattn_prepare_qkv_strided(C.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                            _strides_arg(st), C.byref(rr.struct), m,
+                                            C.byref(prep.struct), _stream(stream)), "prepare_qkv")
 
 
 def int4_fwd(shape: Shape, prep: PreparedDevice, o, mask=None, debug: Debug | None = None,
              stream=None) -> None:
     keep, m = _mask_arg(mask)
     dbg = C.byref(debug) if debug is not None else None
-    check(lib().rotattn_int4_fwd(C.byref(shape), C.byref(prep.struct), m, _ptr(o), dbg,
-                                 _stream(stream)), "int4_fwd")
+    check(lib().rotattn_int4_fwd_strided(C.byref(shape), C.byref(prep.struct), m, _ptr(o),
+                                         _strides_arg(strides_of(o)), dbg, _stream(stream)),
+          "int4_fwd")
 
 
 def fp16_fwd(shape: Shape, prep: PreparedDevice, o, head_select=None, stream=None) -> None:
     """FP16 attention of the selected heads from the prologue's fallback
     buffers (q_rope, k_rope, v_t of `prep`)."""
     keep, m = _mask_arg(head_select)
-    check(lib().rotattn_fp16_fwd(C.byref(shape), C.byref(prep.struct), m, _ptr(o),
-                                 _stream(stream)), "fp16_fwd")
+    check(lib().rotattn_fp16_fwd_strided(C.byref(shape), C.byref(prep.struct), m, _ptr(o),
+                                         _strides_arg(strides_of(o)), _stream(stream)), "fp16_fwd")
 
 
 def workspace_bytes(shape: Shape) -> int:
@@ -257,9 +297,13 @@ def workspace_bytes(shape: Shape) -> int:
 
 def mixed_fwd(shape: Shape, q, k, v, rr: RopeRotDevice, mask, workspace, o, stream=None) -> None:
     keep, m = _mask_arg(mask)
-    check(lib().rotattn_mixed_fwd(C.byref(shape), _ptr(q), _ptr(k), _ptr(v), C.byref(rr.struct), m,
-                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                  _ptr(o), _stream(stream)), "mixed_fwd")
+    st = _shared_strides(q, k, v)
+    check(lib().rotattn_mixed_fwd_strided(C.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                          _strides_arg(st), C.byref(rr.struct), m,
+                                          _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _ptr(o),
+                                          _strides_arg(strides_of(o)), _stream(stream)),
+          "mixed_fwd")
 
 
 def pcode_sweep(mag_lo: int, count: int, max_transitions: int = 4096, layout: int = LAYOUT_FP8,
