@@ -138,7 +138,9 @@ __device__ __forceinline__ void load_rot_frags(const double* rot,
 #pragma unroll
     for (int jb = 0; jb < Part<DA>::JB; ++jb) {
       const int k = 4 * ks + (l >> 4), j = 16 * jb + (l & 15);
-      b[ks][jb] = (k < DA && j < DA) ? (float)rot[k * DA + j] : 0.0f;
+      // unconditional (clamped) loads: all of them in flight at once
+      const float r = (float)rot[min(k, DA - 1) * DA + min(j, DA - 1)];
+      b[ks][jb] = (k < DA && j < DA) ? r : 0.0f;
     }
 }
 
@@ -320,19 +322,32 @@ __device__ __forceinline__ void v_part(const uint32_t* xrow, int off, float* red
 // Coalesced load of a block's fp16 rows [128][D] into LDS rows of D/2 + 1
 // dwords (the odd stride keeps the per-token reads conflict-free); rows past
 // N are zero.
+// Stage 128 fp16 rows (tokens n0..n0+127 of one head, row_stride elements
+// apart) into xs, kRS dwords per row, zero rows for tokens >= N.  Each wave
+// instruction moves one row straight from memory into LDS (global_load_lds,
+// lane L -> dword L of the row): no registers, no waits here.  The caller
+// waits with wait_tiles() before the barrier that publishes the rows.
 template <int D>
 __device__ __forceinline__ void load_tile(const uint16_t* src, int64_t row_stride, int n0, int N,
                                           uint32_t* xs) {
-  constexpr int kChunks = D / 8;           // 16-byte chunks per row
   constexpr int kRS = D / 2 + 1;
-  for (int i = threadIdx.x; i < kBlock * kChunks; i += kThreads) {
-    const int r = i / kChunks, c = i % kChunks;
-    uint4 v = uint4{0, 0, 0, 0};
-    if (n0 + r < N) v = *(const uint4*)(src + (int64_t)(n0 + r) * row_stride + 8 * c);
-    uint32_t* d = xs + r * kRS + 4 * c;
-    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+  constexpr int kW = kThreads / 64;
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll 1
+  for (int r = w; r < kBlock; r += kW) {
+    if (n0 + r < N) {
+      if (lane < D / 2)
+        __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)(n0 + r) * row_stride + 2 * lane),
+                                         (lds_ptr)(xs + r * kRS), 4, 0, 0);
+    } else if (lane < D / 2) {
+      xs[r * kRS + lane] = 0u;
+    }
   }
 }
+
+__device__ __forceinline__ void wait_tiles() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Coalesced store of all 128 staged fp16 rows (rows past N are zero) into a
 // padded [N_pad][D] buffer.
@@ -441,6 +456,7 @@ __device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* sta
   load_tile<D>(a.k + head_in, a.in.token, n0, a.N, stage_k);
   float b[Part<DA>::KS][Part<DA>::JB];   // R_a^T of this wave's partition
   if (ROT) load_rot_frags<DA>(rot, b);
+  wait_tiles();
   __syncthreads();
 
 #pragma unroll 1
@@ -480,6 +496,7 @@ __device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* sta
   // V: staged in the Q buffer, codes (channel rows) in the K buffer
   const int nl = tok0 + (threadIdx.x & 63);
   load_tile<D>(a.v + head_in, a.in.token, n0, a.N, stage_q);
+  wait_tiles();
   __syncthreads();
   int8_t* codes = (int8_t*)stage_k;
   float scale;
@@ -517,6 +534,7 @@ __device__ __forceinline__ void prologue_fallback(const PrologueArgs& a, uint32_
 #pragma unroll 1
   for (int s = 0; s < 2; ++s) {
     load_tile<D>((s == 0 ? a.q : a.k) + head_in, a.in.token, n0, a.N, stage);
+    wait_tiles();
     __syncthreads();
     if (part == 0)
       rope_only_part<D0>(xrow, cos_a, sin_a, pos_c, off);
@@ -527,6 +545,7 @@ __device__ __forceinline__ void prologue_fallback(const PrologueArgs& a, uint32_
     __syncthreads();
   }
   load_tile<D>(a.v + head_in, a.in.token, n0, a.N, stage);
+  wait_tiles();
   __syncthreads();
   store_vt_tiles<D>(stage, a.v_t + (head_pad + n0) * D);
 }
