@@ -103,6 +103,23 @@ struct Fp16Kernel {
         for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
     }
     float ls = 0.0f;   // tile sum first, then into the running l
+    // The fused S kappa - m' compares an exact product with the rounded one in
+    // m' = fl(max S kappa): past |m'| = 2^12 that difference could reach whole
+    // units and overflow the exponential, so such a wave (logits of thousands
+    // of nats) takes fl(fl(S kappa) - m') <= 0 instead.
+    const bool exact_arg = __ballot(fabsf(mnew) > 4096.0f) != 0;
+    float e[2][16];
+    if (!exact_arg) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[sub][r] = __builtin_amdgcn_exp2f(fmaf(S[sub][r], a.kappa, -mnew));
+    } else {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[sub][r] = __builtin_amdgcn_exp2f(S[sub][r] * a.kappa - mnew);
+    }
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -111,8 +128,8 @@ struct Fp16Kernel {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 8 * s + 2 * i;
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(S[sub][r], a.kappa, -mnew));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(S[sub][r + 1], a.kappa, -mnew));
+          const float p0 = e[sub][r];
+          const float p1 = e[sub][r + 1];
           ls += p0;
           ls += p1;
           // one v_cvt_pk_f16_f32 per pair (round to nearest even), packed in place

@@ -45,11 +45,15 @@ struct CodeCtx {
   float ct;      // c_t
   float mnew;    // m'
   float delta;   // half-width of the band around each half-integer that takes the exact path
+  float l2_15;   // fl(log2(15))
+  bool exact_arg;   // wave-uniform: the argument is x + log2(15) with x = fl(fl(I c_t) - m')
 };
 
 __device__ __forceinline__ float ulp_pos(float v) {   // ulp of a positive normal float
   return __uint_as_float(__float_as_uint(v) & 0x7F800000u) * 0x1p-23f;
 }
+
+__device__ __forceinline__ uint32_t wave_any(bool p) { return __ballot(p) != 0; }
 
 __device__ __forceinline__ CodeCtx make_ctx(float ct, float mnew, float log2_15,
                                             float iscale = 0x1p-8f) {
@@ -57,14 +61,22 @@ __device__ __forceinline__ CodeCtx make_ctx(float ct, float mnew, float log2_15,
   c.iscale = iscale;
   c.ct = ct;
   c.mnew = mnew;
+  c.l2_15 = log2_15;
   // cq >= 2^-126: a score of -inf (a masked key of the last tile) then gives
   // t = -inf and y = 0 even when c_t = 0; for |I| < 2^14 the clamp moves t by
   // less than 2^-112, far inside the error bound below
   c.cq = fmaxf(ct * iscale, 0x1p-126f);
   c.m15n = log2_15 - mnew;
   // error of the fused argument against x + log2(15) for scores that can
-  // round to a code in 1..15 (|x| < 8), in log2 units:
-  const float e = 0x1p-21f + ulp_pos(fabsf(mnew) + 8.0f);
+  // round to a code in 1..15 (|x| < 8), in log2 units.  The fused product
+  // I c_t is exact where m' = fl(max I c_t) is rounded, so the error grows
+  // with |m'|; past 2^12 (logits of thousands of nats) the wave computes the
+  // argument from x = fl(fl(I c_t) - m') <= 0 instead, whose only error is the
+  // rounding of x + log2(15): y then never exceeds 15 (no overflow) and the
+  // guard band stays narrow.
+  float e = 0x1p-21f + ulp_pos(fabsf(mnew) + 8.0f);
+  c.exact_arg = wave_any(e > 0x1p-12f);
+  if (c.exact_arg) e = 0x1p-20f;
   // 15.5 * ln 2 < 10.75; v_exp_f32 error < 1 ulp; 12x and +4e-6 are margin.
   c.delta = 12.0f * e + 4e-6f;
   // c_t so small that c_t * iscale may be subnormal: never trust the fast path.
@@ -74,7 +86,21 @@ __device__ __forceinline__ CodeCtx make_ctx(float ct, float mnew, float log2_15,
   return c;
 }
 
-__device__ __forceinline__ uint32_t wave_any(bool p) { return __ballot(p) != 0; }
+// y ~ 15 * 2^x of 16 scores (f = I / iscale exactly; a masked key arrives as
+// -inf and gives y = 0), the argument taken as make_ctx decided for the wave.
+template <int NS>
+__device__ __forceinline__ void exp_scores(const float (&f)[NS], const CodeCtx& cx,
+                                           float (&y)[NS]) {
+  if (!cx.exact_arg) {
+#pragma unroll
+    for (int r = 0; r < NS; ++r) y[r] = __builtin_amdgcn_exp2f(fmaf(f[r], cx.cq, cx.m15n));
+  } else {
+    const float ctc = fmaxf(cx.ct, 0x1p-126f);   // -inf * 0 would be NaN; see make_ctx
+#pragma unroll
+    for (int r = 0; r < NS; ++r)
+      y[r] = __builtin_amdgcn_exp2f((f[r] * cx.iscale * ctc - cx.mnew) + cx.l2_15);
+  }
+}
 
 // Exact P code of one score (float f = I / iscale exactly).
 __device__ __forceinline__ int exact_code(float f, const CodeCtx& cx, const float* tau) {
@@ -97,15 +123,18 @@ __device__ __forceinline__ int exact_code(float f, const CodeCtx& cx, const floa
 template <bool TAIL>
 __device__ __forceinline__ v4i pcode16(const float (&f)[16], float fmax, const CodeCtx& cx,
                                        const float* tau, float& lsum, uint32_t valid) {
-  float y[16];
+  float y[16], ym[1];
+  exp_scores<16>(f, cx, y);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    float t = fmaf(f[r], cx.cq, cx.m15n);
-    if (TAIL) t = ((valid >> r) & 1u) ? t : -INFINITY;
-    y[r] = __builtin_amdgcn_exp2f(t);
+    if (TAIL) y[r] = ((valid >> r) & 1u) ? y[r] : 0.0f;
     lsum += y[r];
   }
-  const float ymax = __builtin_amdgcn_exp2f(fmaf(fmax, cx.cq, cx.m15n));
+  {
+    const float fm[1] = {fmax};
+    exp_scores<1>(fm, cx, ym);
+  }
+  const float ymax = ym[0];
   if (!wave_any(ymax >= 0.5f - cx.delta)) return v4i{0, 0, 0, 0};
   float g = 1.0f;
 #pragma unroll
@@ -168,11 +197,9 @@ __device__ __forceinline__ v4i pcode16_f8(const float (&f)[16], const CodeCtx& c
                                           const float* tau_lds, float& lsum,
                                           float (&rr)[16]) {
   float y[16];
+  exp_scores<16>(f, cx, y);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    y[r] = __builtin_amdgcn_exp2f(fmaf(f[r], cx.cq, cx.m15n));
-    lsum += y[r];
-  }
+  for (int r = 0; r < 16; ++r) lsum += y[r];
   float g = 0.0f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
