@@ -260,11 +260,29 @@ int rotattn_int4_fwd(const rotattn_shape* s, const rotattn_prepared* p,
                      const uint8_t* fallback_mask_host, uint16_t* o,
                      const rotattn_debug* dbg, hipStream_t stream);
 
+/*
+ * Options of the INT4 attention.  normalizer: ROTATTN_NORM_EXP (default) takes
+ * l as the sum of the unquantized 2^x; ROTATTN_NORM_CODES as the sum of the
+ * P codes / 15, so that O is the quantized P's weighted mean of V (the other
+ * reading of the quantized FlashAttention on the RotateAttention page,
+ * Abstract; FP8 layout only, ROTATTN_E_UNSUPPORTED for PACKED).
+ */
+typedef enum rotattn_normalizer {
+  ROTATTN_NORM_EXP = 0,
+  ROTATTN_NORM_CODES = 1
+} rotattn_normalizer;
+
+typedef struct rotattn_int4_opts {
+  int32_t normalizer;
+} rotattn_int4_opts;
+
 /* rotattn_int4_fwd writing o with o_strides (NULL = contiguous), e.g. as the
- * token-major [B][N][H][D] input of the output projection. */
+ * token-major [B][N][H][D] input of the output projection; opts NULL = the
+ * defaults.  ROTATTN_E_ARG for an unknown normalizer. */
 int rotattn_int4_fwd_strided(const rotattn_shape* s, const rotattn_prepared* p,
                              const uint8_t* fallback_mask_host, uint16_t* o,
                              const rotattn_strides* o_strides,
+                             const rotattn_int4_opts* opts,
                              const rotattn_debug* dbg, hipStream_t stream);
 
 /*

@@ -287,7 +287,8 @@ def pcode(x: np.ndarray) -> np.ndarray:
 
 def int4_attention(q_codes, q_scale_l2, k_codes, k_scale, v_codes, v_scale, rows, *,
                    tile: int = L_BLOCK, quantize_p: bool = True, score_dtype=np.float32,
-                   record: dict | None = None, int64_check: bool = False):
+                   record: dict | None = None, int64_check: bool = False,
+                   normalizer: str = "exp"):
     """Output rows of one (batch, head), key tiles in ascending order.
 
     q_codes/k_codes/v_codes: [N, D] integer codes (or any float values for the
@@ -303,7 +304,13 @@ def int4_attention(q_codes, q_scale_l2, k_codes, k_scale, v_codes, v_scale, rows
       m      = m_new
     then O = fp16(acc / l).  Keys past N never enter (partial last tile).
     The float part (alpha, l, acc) is evaluated in float64.
+
+    normalizer "codes" takes l = alpha * l + sum_j code_j / 15 instead (R6's
+    alternative: the normalizer of the quantized P, so that O is the
+    code-weighted mean of the dequantized V rows).
     """
+    if normalizer not in ("exp", "codes") or (normalizer == "codes" and not quantize_p):
+        raise ValueError(normalizer)
     q_codes = np.asarray(q_codes)
     N, D = k_codes.shape
     rows = np.asarray(rows, np.int64)
@@ -339,10 +346,14 @@ def int4_attention(q_codes, q_scale_l2, k_codes, k_scale, v_codes, v_scale, rows
         x = (s - m_new[:, None]).astype(score_dtype)
         p = np.exp2(x.astype(np.float64))
         alpha = np.where(np.isneginf(m), 0.0, np.exp2(m.astype(np.float64) - m_new.astype(np.float64)))
-        l = alpha * l + p.sum(axis=1)
         vt = v_codes[k0:k1].astype(np.float64)
         if quantize_p:
             code = pcode(x)
+        if normalizer == "codes":
+            l = alpha * l + code.astype(np.float64).sum(axis=1) / P_LEVELS
+        else:
+            l = alpha * l + p.sum(axis=1)
+        if quantize_p:
             pv = code.astype(np.float64) @ vt
             assert np.all(pv == np.rint(pv))
             vs = np.float64(np.asarray(v_scale, np.float32)[k0 // L_BLOCK])

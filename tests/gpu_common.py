@@ -154,10 +154,11 @@ class Run:
         return O.prepare_head(q, k, v, self.tables, self.r32, self.cfg.grid, self.cfg.split,
                               fallback=fallback)
 
-    def oracle_int4(self, bh: int, rows, record=None):
+    def oracle_int4(self, bh: int, rows, record=None, normalizer="exp"):
         p = self.oracle_prep(bh)
         return O.int4_attention(p["q_codes"], p["q_scale_l2"], p["k_codes"], p["k_scale"],
-                                p["v_codes"], p["v_scale"], rows, record=record)
+                                p["v_codes"], p["v_scale"], rows, record=record,
+                                normalizer=normalizer)
 
     def oracle_fp16(self, bh: int, rows):
         p = self.oracle_prep(bh, fallback=True)

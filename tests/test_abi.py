@@ -145,7 +145,7 @@ def test_strided_entry_points_validate_strides():
     odd = R.Strides(2 * 32 * 64, 32 * 64 + 4, 64)       # not a multiple of 8
     for st, code in ((short, -7), (odd, -5)):
         assert L.rotattn_int4_fwd_strided(C.byref(s), C.byref(p), None, fake, C.byref(st), None,
-                                          C.c_void_p(0)) in (-1, code)
+                                          None, C.c_void_p(0)) in (-1, code)
         assert L.rotattn_fp16_fwd_strided(C.byref(s), C.byref(p), None, fake, C.byref(st),
                                           C.c_void_p(0)) in (-1, code)
         assert L.rotattn_mixed_fwd_strided(C.byref(s), fake, fake, fake, None, None, None, fake,

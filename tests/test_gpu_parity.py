@@ -573,3 +573,36 @@ def test_maximum_head_count():
     for bh in fb + [1, 62, 65, 2046, 2049, 4094]:
         ref = run.oracle_fp16(bh, rows)[0] if mask[bh] else run.oracle_int4(bh, rows)[0]
         check_out(og[bh], ref, f"maxheads head {bh}")
+
+
+@pytest.mark.parametrize("name", ["small", "720p"])
+def test_code_sum_normalizer(name):
+    """The code-sum normalizer option: output within tolerance of the oracle's
+    code-sum variant, codes and I unchanged (debug dump), l = sum of codes / 15;
+    the PACKED layout refuses it."""
+    torch = torch_cuda()
+    run = get_run(name)
+    run.prepare()
+    bufs, R = _debug_buffers(run)
+    bh, qb = (3, 5) if name == "small" else (17, 420)
+    H = run.cfg.H
+    dbg = R.Debug(bh // H, bh % H, qb, *(bufs[k].data_ptr() for k in
+                                         ("s_int", "p_code", "pv_int", "m_final", "l_final")))
+    o = run.empty_out()
+    R.int4_fwd(run.shape, run.prep, o, mask=run.mask, debug=dbg, normalizer="codes")
+    torch.cuda.synchronize()
+    N = run.cfg.N
+    rows_all = np.arange(qb * 128, min(N, qb * 128 + 128))
+    rec = {}
+    o16, _ = run.oracle_int4(bh, rows_all, record=rec, normalizer="codes")
+    nr = rows_all.size
+    assert np.array_equal(bufs["p_code"].cpu().numpy()[:nr, :N], np.concatenate(rec["code"], axis=1))
+    l_fin = bufs["l_final"].cpu().numpy()[:nr].astype(np.float64)
+    assert np.allclose(l_fin, rec["l_final"], rtol=1e-5, atol=0)
+    og = o.reshape(run.cfg.BH, N, run.cfg.D).cpu().numpy()
+    check_out(og[bh][rows_all], o16, f"{name} code-sum head {bh}")
+    rows = synth.sampled_rows(run.cfg, 5, 64 if N > 4096 else None)
+    check_out(og[5][rows], run.oracle_int4(5, rows, normalizer="codes")[0], f"{name} code-sum head 5")
+    packed = R.PreparedDevice(run.shape, with_rope=False, layout=R.LAYOUT_PACKED)
+    with pytest.raises(R.RotAttnError):
+        R.int4_fwd(run.shape, packed, o, normalizer="codes")

@@ -207,3 +207,27 @@ def test_keys_past_n_never_enter():
     o16, out = _run(prep, rows, record=rec)
     assert rec["I"][-1].shape == (3, 300 - 256)
     assert np.all(np.isfinite(out))
+
+
+def test_code_sum_normalizer_is_the_code_weighted_mean():
+    """The code-sum normalizer (R6's alternative): with V == 1 every output is
+    exactly 1 (the weights sum to one by construction), every output lies
+    inside the per-channel range of the dequantized V, and it differs from the
+    exp normalizer."""
+    cfg = synth.CONFIGS["small"]
+    _, _, _, prep = _prep(cfg)
+    rows = np.arange(0, cfg.N, 29)
+    one = dict(prep)
+    one["v_codes"] = np.full_like(prep["v_codes"], 7)
+    one["v_scale"] = np.full_like(prep["v_scale"], np.float32(1) / np.float32(7))
+    _, out1 = _run(one, rows, normalizer="codes")
+    vs = np.float64(np.float32(1) / np.float32(7)) * 7
+    assert np.allclose(out1, vs, rtol=1e-14, atol=0)
+    _, out_c = _run(prep, rows, normalizer="codes")
+    vq = prep["v_codes"].astype(np.float64) * np.repeat(prep["v_scale"].astype(np.float64),
+                                                         128)[:cfg.N, None]
+    assert np.all(out_c <= vq.max(axis=0) + 1e-12) and np.all(out_c >= vq.min(axis=0) - 1e-12)
+    _, out_e = _run(prep, rows)
+    assert np.abs(out_c - out_e).max() > 1e-4
+    with pytest.raises(ValueError):
+        _run(prep, rows, normalizer="sum")

@@ -193,13 +193,19 @@ __device__ __forceinline__ int signbit01(float v) { return (int)(__float_as_uint
 // with x = fl(fl(I c_t) - m') -- one comparison against the staged table.
 // Masked keys (last tile) arrive as I = -inf: t = -inf, y = 0, code 0 on both
 // paths (the exact one sees x = -inf or NaN against tau_0 = -inf with j = 0).
+//
+// CS adds the codes to lsum instead of 15*2^x: the normalizer of the
+// code-sum variant, l = sum of the quantized P.
+template <bool CS = false>
 __device__ __forceinline__ v4i pcode16_f8(const float (&f)[16], const CodeCtx& cx,
                                           const float* tau_lds, float& lsum,
                                           float (&rr)[16]) {
   float y[16];
   exp_scores<16>(f, cx, y);
+  if (!CS) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) lsum += y[r];
+    for (int r = 0; r < 16; ++r) lsum += y[r];
+  }
   float g = 0.0f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -215,6 +221,10 @@ __device__ __forceinline__ v4i pcode16_f8(const float (&f)[16], const CodeCtx& c
       const int code = j - signbit01(x - tau_lds[j]);       // j - 1 + [x >= tau_j]
       rr[r] = (float)(code < 0 ? 0 : code);
     }
+  }
+  if (CS) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lsum += rr[r];
   }
   uint32_t pk[4];
 #pragma unroll
@@ -501,7 +511,7 @@ hipError_t launch_int4(int D, int BH, const Int4Args& a, const Int4Debug* dbg, h
 // overlaps the other's MFMAs, which run at raised wave priority.  Per tile:
 // S, softmax, then the K/V tiles of t+1 are requested straight into the other
 // LDS buffers (global_load_lds) while P.V of tile t runs; one barrier per tile.
-template <int D, bool DBG>
+template <int D, bool DBG, bool CS>
 struct Int4F8Kernel {
   static constexpr int KS = D / 64;        // k-steps of 64 channels for QK^T
   static constexpr int DB = D / 32;        // 32-channel blocks of O^T
@@ -648,7 +658,7 @@ struct Int4F8Kernel {
       float f[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) f[r] = S[sub][r];
-      const v4i pk = pcode16_f8(f, cx, tau_lds, ls, rr[sub]);
+      const v4i pk = pcode16_f8<CS>(f, cx, tau_lds, ls, rr[sub]);
       // 64-key chunk c = sub/2 holds subtile 2c in bytes 0-15, 2c+1 in 16-31
 #pragma unroll
       for (int i = 0; i < 4; ++i) P[sub >> 1][4 * (sub & 1) + i] = pk[i];
@@ -788,25 +798,26 @@ struct Int4F8Kernel {
   }
 };
 
-template <int D, bool DBG>
+template <int D, bool DBG, bool CS>
 __global__ __launch_bounds__(256, 2) void k_int4_attn_f8(Int4Args a, Int4Debug dbg) {
-  Int4F8Kernel<D, DBG>::run(a, dbg);
+  Int4F8Kernel<D, DBG, CS>::run(a, dbg);
+}
+
+template <int D, bool CS>
+static void launch_int4_f8_t(int BH, const Int4Args& a, const Int4Debug* dbg, hipStream_t st) {
+  if (dbg == nullptr) {
+    Int4Debug none{};
+    hipLaunchKernelGGL((k_int4_attn_f8<D, false, CS>), dim3(a.NB, BH), dim3(256), 0, st, a, none);
+  } else {
+    hipLaunchKernelGGL((k_int4_attn_f8<D, true, CS>), dim3(1), dim3(256), 0, st, a, *dbg);
+  }
 }
 
 hipError_t launch_int4_f8(int D, int BH, const Int4Args& a, const Int4Debug* dbg, hipStream_t st) {
-  Int4Debug none{};
-  if (dbg == nullptr) {
-    dim3 grid(a.NB, BH);
-    if (D == 128)
-      hipLaunchKernelGGL((k_int4_attn_f8<128, false>), grid, dim3(256), 0, st, a, none);
-    else
-      hipLaunchKernelGGL((k_int4_attn_f8<64, false>), grid, dim3(256), 0, st, a, none);
-  } else {
-    if (D == 128)
-      hipLaunchKernelGGL((k_int4_attn_f8<128, true>), dim3(1), dim3(256), 0, st, a, *dbg);
-    else
-      hipLaunchKernelGGL((k_int4_attn_f8<64, true>), dim3(1), dim3(256), 0, st, a, *dbg);
-  }
+  if (D == 128)
+    a.code_sum ? launch_int4_f8_t<128, true>(BH, a, dbg, st) : launch_int4_f8_t<128, false>(BH, a, dbg, st);
+  else
+    a.code_sum ? launch_int4_f8_t<64, true>(BH, a, dbg, st) : launch_int4_f8_t<64, false>(BH, a, dbg, st);
   return hipGetLastError();
 }
 

@@ -256,13 +256,13 @@ int rotattn_prepare_qkv_strided(const rotattn_shape* s, const uint16_t* q, const
 int rotattn_int4_fwd(const rotattn_shape* s, const rotattn_prepared* p,
                      const uint8_t* fallback_mask_host, uint16_t* o, const rotattn_debug* dbg,
                      hipStream_t stream) {
-  return rotattn_int4_fwd_strided(s, p, fallback_mask_host, o, nullptr, dbg, stream);
+  return rotattn_int4_fwd_strided(s, p, fallback_mask_host, o, nullptr, nullptr, dbg, stream);
 }
 
 int rotattn_int4_fwd_strided(const rotattn_shape* s, const rotattn_prepared* p,
                              const uint8_t* fallback_mask_host, uint16_t* o,
-                             const rotattn_strides* o_strides, const rotattn_debug* dbg,
-                             hipStream_t stream) {
+                             const rotattn_strides* o_strides, const rotattn_int4_opts* opts,
+                             const rotattn_debug* dbg, hipStream_t stream) {
   const int st = rotattn_validate(s);
   if (st != ROTATTN_OK) return st;
   if (!p || !o) return ROTATTN_E_NULL;
@@ -275,6 +275,9 @@ int rotattn_int4_fwd_strided(const rotattn_shape* s, const rotattn_prepared* p,
     return ROTATTN_E_ALIGN;
   if (p->layout != ROTATTN_LAYOUT_PACKED && p->layout != ROTATTN_LAYOUT_FP8) return ROTATTN_E_ARG;
   const bool f8 = p->layout == ROTATTN_LAYOUT_FP8;
+  const int norm = opts ? opts->normalizer : ROTATTN_NORM_EXP;
+  if (norm != ROTATTN_NORM_EXP && norm != ROTATTN_NORM_CODES) return ROTATTN_E_ARG;
+  if (norm == ROTATTN_NORM_CODES && !f8) return ROTATTN_E_UNSUPPORTED;
   const int BH = s->B * s->H;
   Int4Debug d{};
   if (dbg) {
@@ -302,6 +305,7 @@ int rotattn_int4_fwd_strided(const rotattn_shape* s, const rotattn_prepared* p,
   a.N = s->N;
   a.NB = nblocks(s);
   a.log2_15 = log2_15_f();
+  a.code_sum = norm == ROTATTN_NORM_CODES;
   rotattn_pcode_thresholds_host(a.tau);
   auto launch = f8 ? launch_int4_f8 : launch_int4;
   if (n_run > 0 && launch(s->D, BH, a, nullptr, stream) != hipSuccess) return ROTATTN_E_HIP;
@@ -368,7 +372,7 @@ int rotattn_mixed_fwd_strided(const rotattn_shape* s, const uint16_t* q, const u
   if (r != ROTATTN_OK) return r;
   r = rotattn_prepare_qkv_strided(s, q, k, v, qkv_strides, rr, fallback_mask_host, &p, stream);
   if (r != ROTATTN_OK) return r;
-  r = rotattn_int4_fwd_strided(s, &p, fallback_mask_host, o, o_strides, nullptr, stream);
+  r = rotattn_int4_fwd_strided(s, &p, fallback_mask_host, o, o_strides, nullptr, nullptr, stream);
   if (r != ROTATTN_OK) return r;
   if (fallback_mask_host) {
     int n_fb = 0;

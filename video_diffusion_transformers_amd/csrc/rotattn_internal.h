@@ -69,6 +69,7 @@ struct Int4Args {
   int N, NB;
   float log2_15;                // fl32(log2(15))
   float tau[15];                // P-code thresholds
+  bool code_sum;                // normalizer: sum of the P codes (FP8 layout) instead of sum 2^x
   HeadBits run;                 // bit set: run this head
 };
 

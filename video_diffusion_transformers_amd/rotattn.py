@@ -51,6 +51,13 @@ class Strides(C.Structure):
     _fields_ = [("batch", C.c_int64), ("head", C.c_int64), ("token", C.c_int64)]
 
 
+class Int4Opts(C.Structure):
+    _fields_ = [("normalizer", C.c_int32)]
+
+
+NORMALIZERS = {"exp": 0, "codes": 1}
+
+
 class Prepared(C.Structure):
     _fields_ = [("layout", C.c_int32)] + [
         (n, C.c_void_p) for n in ("q4", "k4", "v4", "q_scale_l2", "k_scale", "v_scale", "q_rope",
@@ -101,7 +108,8 @@ def lib() -> C.CDLL:
             "rotattn_prepare_qkv_strided": (C.c_int, [S, P, P, P, C.POINTER(Strides),
                                                       C.POINTER(RopeRot), P, C.POINTER(Prepared), P]),
             "rotattn_int4_fwd_strided": (C.c_int, [S, C.POINTER(Prepared), P, P,
-                                                   C.POINTER(Strides), C.POINTER(Debug), P]),
+                                                   C.POINTER(Strides), C.POINTER(Int4Opts),
+                                                   C.POINTER(Debug), P]),
             "rotattn_fp16_fwd_strided": (C.c_int, [S, P, P, P, C.POINTER(Strides), P]),
             "rotattn_mixed_fwd_strided": (C.c_int, [S, P, P, P, C.POINTER(Strides),
                                                     C.POINTER(RopeRot), P, P, C.c_size_t, P,
@@ -275,12 +283,15 @@ def prepare_qkv(shape: Shape, q, k, v, rr: RopeRotDevice, prep: PreparedDevice, 
 
 
 def int4_fwd(shape: Shape, prep: PreparedDevice, o, mask=None, debug: Debug | None = None,
-             stream=None) -> None:
+             stream=None, normalizer: str = "exp") -> None:
+    """normalizer "exp": l = sum of the unquantized 2^x; "codes": the sum of
+    the P codes (FP8 layout)."""
     keep, m = _mask_arg(mask)
     dbg = C.byref(debug) if debug is not None else None
+    opts = Int4Opts(NORMALIZERS[normalizer])
     check(lib().rotattn_int4_fwd_strided(C.byref(shape), C.byref(prep.struct), m, _ptr(o),
-                                         _strides_arg(strides_of(o)), dbg, _stream(stream)),
-          "int4_fwd")
+                                         _strides_arg(strides_of(o)), C.byref(opts), dbg,
+                                         _stream(stream)), "int4_fwd")
 
 
 def fp16_fwd(shape: Shape, prep: PreparedDevice, o, head_select=None, stream=None) -> None:
