@@ -79,9 +79,9 @@ def traffic_from_profile(launch_ms: float):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: the INT4 attention shards by head with no "
-              f"exchange inside the kernel, and runs on more than one GPU are not part of this "
-              f"build (asked for --gpus {args.gpus}).", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the INT4 "
+              f"attention shards by head with no exchange inside the kernel, so a multi-GPU run "
+              f"is one GPU's run per shard; it is not provided.", file=sys.stderr)
         sys.exit(2)
 
     import torch

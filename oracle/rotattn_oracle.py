@@ -23,7 +23,7 @@ Sources (page titles; every function cites the passage it follows):
 
 The pages give an abstract only: no equations, block sizes or kernel details.
 Every step they leave open takes the plainest reading the rest supports; the
-readings are listed in the design doc and repeated next to the code that takes them:
+readings are these, repeated next to the code that takes them:
 
 R1  S = Q K^T / sqrt(D); the max is the row max.  Work in the log2 domain:
     kappa = fl32(log2(e)/sqrt(D)) is folded into Q's scale, so
