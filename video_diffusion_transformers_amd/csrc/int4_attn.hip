@@ -9,26 +9,35 @@
 // What one work-group computes (4 waves x 32 queries = one 128-query block of
 // one head; the block shares one Q scale):
 //   for each 128-key tile t (ascending):
-//     S^T  = K_t Q^T on v_mfma_i32_32x32x32_i8: operands are INT4 codes held
-//            as 16*code in int8 lanes, so the int32 result is 256*I exactly
+//     S^T  = K_t Q^T (exact integers I)
 //     m'   = max(m, fl(max_j I * c_t)),  c_t = fl(q_scale_l2 * k_scale_t)
 //     code = rne(15 * 2^(fl(fl(I*c_t) - m')))            (u4, exact, see below)
-//     l    = 2^(m-m') l + sum_j 15 * 2^(...)             (fp32, unquantized)
-//     O^T  = 2^(m-m') O^T + (v_scale_t/16) * (V_t^T P^T) (v_mfma_i32_32x32x32_i8)
+//     l    = 2^(m-m') l + sum_j 15 * 2^(...)             (fp32, unquantized;
+//            the code-sum variant adds the codes instead)
+//     O^T  = 2^(m-m') O^T + v_scale_t * (V_t^T P^T)      (exact integers V.P)
 //   O = O / l  -> fp16.
+// Two implementations with the same integers:
+//  * Int4F8Kernel (production, FP8 layout): codes are the FP8 E4M3 bytes of
+//    the integers, S^T and V^T P^T run on v_mfma_scale_f32_32x32x64_f8f6f4,
+//    whose fp32 accumulators hold the integer sums exactly; O is kept in units
+//    of the current V block scale.
+//  * Int4Kernel (PACKED layout): two codes per byte, unpacked to 16*code in
+//    int8 lanes for v_mfma_i32_32x32x32_i8 (the int32 result is 256*I).
 // Computing S^T (keys as MFMA rows) leaves every lane holding one query's
 // scores in exactly the operand layout the P.V MFMA needs for P^T, so the
 // requantized codes never leave registers; the running max, sum and O rows of
 // a query live in the same lane pair (lane, lane^32).
 //
-// P codes, exactly.  The fast path computes y = v_exp_f32(fma(256I, c_t/256,
-// log2(15) - m')) ~ 15*2^x and rounds it with v_cvt_pk_u8_f32 (round to
-// nearest even, checked on the device).  |y - 15*2^x| is bounded by the
-// rounding of the fused argument (at most ~ulp(|m'| + 8) + 2^-21 in x) and the
-// exp error (< 1 ulp); whenever some y of a 32-key subtile lies within delta
-// of a half-integer, that register is recomputed exactly as
-// #{k : fl(fl(I*c_t) - m') >= tau_k}.  The self-test entry points run this same
-// function over every float32 score and over random integer scores.
+// P codes, exactly.  The fast path computes y = v_exp_f32(fma(I, c_t,
+// log2(15) - m')) ~ 15*2^x and rounds it to nearest even.  |y - 15*2^x| is
+// bounded by the rounding of the fused argument (at most ~ulp(|m'| + 8) +
+// 2^-21 in x; a wave whose running max is too large for that bound to be
+// useful takes the argument from fl(fl(I*c_t) - m') instead) and the exp
+// error (< 1 ulp); whenever some y of a 32-key subtile lies within delta of a
+// half-integer, that register is recomputed exactly against the thresholds
+// tau_k (code = #{k : fl(fl(I*c_t) - m') >= tau_k}).  The self-test entry
+// points run the same device functions over every float32 score and over
+// random integer scores.
 #include <math.h>
 
 #include "rotattn_internal.h"
