@@ -157,3 +157,23 @@ def test_strided_entry_points_validate_strides():
         assert L.rotattn_mixed_fwd_strided(C.byref(s), fake, fake, fake, None, C.byref(rr), None,
                                            C.c_void_p(1 << 24), ws, fake, C.byref(st),
                                            C.c_void_p(0)) == code
+
+
+def test_binding_layout_helpers():
+    """strides_of / shared layouts on CPU tensors (host logic of the binding)."""
+    import torch
+    B, H, N, D = 1, 3, 10, 64
+    x = torch.zeros((B, H, N, D), dtype=torch.float16)
+    assert R.strides_of(x) is None                                    # contiguous
+    qkv = torch.zeros((B, N, 3, H, D), dtype=torch.float16)
+    q, k, v = qkv.permute(2, 0, 3, 1, 4)
+    st = R.strides_of(q)
+    assert (st.batch, st.head, st.token) == (N * 3 * H * D, D, 3 * H * D)
+    assert R._shared_strides(q, k, v).token == 3 * H * D
+    with pytest.raises(ValueError):
+        R._shared_strides(q, k, x)                                    # mixed layouts
+    with pytest.raises(ValueError):
+        R.strides_of(x.transpose(2, 3))                               # channel stride != 1
+    with pytest.raises(ValueError):
+        R.strides_of(x[0])                                            # not 4-D
+    assert set(R.NORMALIZERS) == {"exp", "codes"}
