@@ -8,7 +8,8 @@
 // symmetric INT4 quantization.  Heads routed to the FP16 fallback only get
 // RoPE'd fp16 Q/K.
 //
-// One work-group per (128-token block, head); 384 threads = 6 waves.
+// One work-group per (128-token block, head); 256 threads = 4 waves, one per
+// SIMD, so that two work-groups share a CU whatever their wave placement.
 // Arithmetic (bit-exact by construction; this file is built with
 // -ffp-contract=off):
 //   RoPE   y0 = fl(fl(x0*c) - fl(x1*s)), y1 = fl(fl(x0*s) + fl(x1*c))   fp32
@@ -20,14 +21,15 @@
 // runs on v_mfma_f64_16x16x4_f64, which accumulates D = C + a0 b0 + a1 b1 +
 // a2 b2 + a3 b3 as a chain of fused multiply-adds in ascending k (checked
 // bit for bit on the device against that chain), so 16x16x4 steps chained over
-// k reproduce the sequential fp64 sum exactly.  Wave 2a + h owns partition a
-// and tokens 64h..64h+63: R_a^T sits in its registers as B fragments, and the A
-// fragments are RoPE'd on the fly from the staged fp16 rows.
+// k reproduce the sequential fp64 sum exactly.  Wave w owns tokens
+// 32w..32w+31 in every partition: R_a^T is read (from cache) into registers
+// as B fragments partition by partition, and the A fragments are RoPE'd on
+// the fly from the staged fp16 rows.
 #include "rotattn_internal.h"
 
 namespace rotattn {
 
-constexpr int kThreads = 384;
+constexpr int kThreads = 256;
 constexpr int kCodeStride = 132;   // bytes per row of the int8 code buffers (33 dwords: no bank conflicts)
 
 __device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
@@ -99,22 +101,16 @@ __device__ __forceinline__ void block_scale(float local, float* red, float& inv,
   __syncthreads();   // red[] is reused by the next reduction
 }
 
-__device__ __forceinline__ int quant(float z, float inv) {
-  return (int)fminf(fmaxf(rintf(z * inv), -7.0f), 7.0f);
-}
-
-// FP8 E4M3 bits of an integer code in [-7, 7] (exact: 1 = 0x38, 2 = 0x40,
-// 3 = 0x44, ..., 7 = 0x4E; sign in bit 7).
-__device__ __forceinline__ uint32_t e4m3_of(int c) {
-  const uint64_t lut = 0x4E4C4A4844403800ull;
-  const uint32_t mag = (uint32_t)(c < 0 ? -c : c);
-  return (uint32_t)((lut >> (8 * mag)) & 0xFFu) | (c < 0 ? 0x80u : 0u);
-}
-
-// The byte stored for a code: int8 for the packed layout, E4M3 for FP8.
+// The code bytes of two values in bits 0-7 and 8-15: code =
+// clamp(rne(fl(z inv)), -7, 7) (the + 0 turns a -0 into +0), stored as E4M3
+// bytes for the FP8 layout (v_cvt_pk_fp8_f32 is exact on these integers:
+// 1 = 0x38, 2 = 0x40, ..., 7 = 0x4E, sign in bit 7) or as int8 bytes.
 template <bool F8>
-__device__ __forceinline__ int8_t code_byte(int c) {
-  return F8 ? (int8_t)e4m3_of(c) : (int8_t)c;
+__device__ __forceinline__ uint32_t code_pair(float z0, float z1, float inv) {
+  const float q0 = __builtin_amdgcn_fmed3f(__builtin_rintf(z0 * inv), -7.0f, 7.0f) + 0.0f;
+  const float q1 = __builtin_amdgcn_fmed3f(__builtin_rintf(z1 * inv), -7.0f, 7.0f) + 0.0f;
+  if (F8) return __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false) & 0xffffu;
+  return ((uint32_t)(int)q0 & 0xffu) | (((uint32_t)(int)q1 & 0xffu) << 8);
 }
 
 typedef double v4d __attribute__((ext_vector_type(4)));
@@ -144,21 +140,49 @@ __device__ __forceinline__ void load_rot_frags(const double* rot,
     }
 }
 
-// RoPE + rotation of one tensor over this wave's partition (width DA at channel
-// offset off) and 64 tokens (tok0..tok0+63 of the block): z in the MFMA output
-// layout (token row tok0 + 16 tb + l/16 + 4 r, channel 16 jb + l%16), returns
-// the lane's max |z|.  xs: staged fp16 rows of the tensor (kRS dwords per row).
-template <int DA, int kRS>
-__device__ __forceinline__ float rotate_tensor(const uint32_t* xs, const float* cos_a,
-                                               const float* sin_a,
-                                               float (&b)[Part<DA>::KS][Part<DA>::JB], int off,
-                                               int tok0, int n0, int N, int axis, int HW, int gh,
-                                               int gw, float (&z)[4][Part<DA>::JB][4]) {
+// Position of token n (< N) on RoPE axis `axis`: t = n / (Hg Wg),
+// h = (n / Wg) mod Hg, w = n mod Wg.  Padding tokens (n >= N) have zero rows;
+// any valid table row will do for them.
+__device__ __forceinline__ int axis_pos(int n, int N, int axis, int HW, int gh, int gw) {
+  return n < N ? (axis == 0 ? n / HW : (axis == 1 ? (n / gw) % gh : n % gw)) : 0;
+}
+
+// The RoPE'd value of channel c (< DA) of one partition for one token: the
+// token's staged fp16 row xrow (one dword per channel pair, partition start),
+// its table rows start at element trow of cos_a and sin_a.  Even channel:
+// fl(x0 c) - fl(x1 s); odd channel: fl(x0 s) + fl(x1 c).  Operands are
+// selected instead of branching (negation is exact).  Channels >= DA (MFMA
+// zero padding) read a clamped pair.
+template <int DA>
+__device__ __forceinline__ float rope_channel(const uint32_t* xrow, const float* cos_a,
+                                              const float* sin_a, int trow, int c) {
+  const int jp = (c >> 1) < DA / 2 ? (c >> 1) : DA / 2 - 1;
+  const uint32_t pr = xrow[jp];
+  const float x0 = h2f((uint16_t)(pr & 0xffffu));
+  const float x1 = h2f((uint16_t)(pr >> 16));
+  const float cs = cos_a[trow + jp], sn = sin_a[trow + jp];
+  const bool odd = (c & 1) != 0;
+  const float p0 = x0 * (odd ? sn : cs);
+  const float p1 = x1 * (odd ? cs : sn);
+  return p0 + (odd ? p1 : -p1);
+}
+
+// RoPE + rotation of one tensor over one partition (width DA at channel offset
+// off, RoPE axis `axis`) for TB groups of 16 tokens from tok0: z in the MFMA
+// output layout (token tok0 + 16 tb + l/16 + 4 r, channel 16 jb + l%16 of the
+// partition); returns the lane's max |z|.  xs: staged fp16 rows (kRS dwords
+// per row); b: R_a^T as B fragments.
+template <int DA, int TB, int kRS>
+__device__ __forceinline__ float rotate_part(const uint32_t* xs, const float* cos_a,
+                                             const float* sin_a,
+                                             float (&b)[Part<DA>::KS][Part<DA>::JB], int off,
+                                             int tok0, int n0, int N, int axis, int HW, int gh,
+                                             int gw, float (&z)[TB][Part<DA>::JB][4]) {
   constexpr int KS = Part<DA>::KS, JB = Part<DA>::JB;
   const int l = threadIdx.x & 63;
   float amax = 0.0f;
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
+  for (int tb = 0; tb < TB; ++tb) {
     // the fp32 fragments are marked as changing here so that their fp64
     // conversions stay next to the MFMAs instead of being hoisted into
     // 2 x KS x JB live registers
@@ -167,28 +191,15 @@ __device__ __forceinline__ float rotate_tensor(const uint32_t* xs, const float* 
 #pragma unroll
       for (int jb = 0; jb < JB; ++jb) asm volatile("" : "+v"(b[ks][jb]));
     const int i = tok0 + 16 * tb + (l & 15);   // this lane's A row (token in the block)
-    const int n = n0 + i;
-    // padding tokens have zero rows; any valid table row will do
-    const int pos = n < N ? (axis == 0 ? n / HW : (axis == 1 ? (n / gw) % gh : n % gw)) : 0;
+    const int pos = axis_pos(n0 + i, N, axis, HW, gh, gw);
     const uint32_t* xrow = xs + i * kRS + off / 2;
-    const float* crow = cos_a + pos * (DA / 2);
-    const float* srow = sin_a + pos * (DA / 2);
-    // RoPE'd A fragments of this token block, then the MFMA chain over k
+    const int trow = pos * (DA / 2);
+    // RoPE'd A fragments of this token group, then the MFMA chain over k
     double av[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int c = 4 * ks + (l >> 4);                      // channel in the partition
-      const int jp = (c >> 1) < DA / 2 ? (c >> 1) : DA / 2 - 1;   // pair (clamped on padding)
-      const uint32_t pr = xrow[jp];
-      const float x0 = h2f((uint16_t)(pr & 0xffffu));
-      const float x1 = h2f((uint16_t)(pr >> 16));
-      const float cs = crow[jp], sn = srow[jp];
-      // even channel: fl(x0 c) - fl(x1 s); odd: fl(x0 s) + fl(x1 c); operands
-      // are selected instead of branching (negation is exact)
-      const bool odd = (c & 1) != 0;
-      const float p0 = x0 * (odd ? sn : cs);
-      const float p1 = x1 * (odd ? cs : sn);
-      const float y = p0 + (odd ? p1 : -p1);
+      const float y = rope_channel<DA>(xrow, cos_a, sin_a, trow, c);
       av[ks] = c < DA ? (double)y : 0.0;
     }
     v4d acc[JB];
@@ -215,34 +226,24 @@ __device__ __forceinline__ float rotate_tensor(const uint32_t* xs, const float* 
 // z = y = RoPE(x) exactly as the rotating path computes its A fragments, kept
 // in that layout (token tok0 + 16 tb + l%16, channel 4 ks + l/16).  Returns
 // the lane's max |z|.
-template <int DA, int kRS>
-__device__ __forceinline__ float rope_tensor(const uint32_t* xs, const float* cos_a,
+template <int DA, int TB, int kRS>
+__device__ __forceinline__ float rope_part_a(const uint32_t* xs, const float* cos_a,
                                              const float* sin_a, int off, int tok0, int n0, int N,
                                              int axis, int HW, int gh, int gw,
-                                             float (&z)[4][Part<DA>::KS]) {
+                                             float (&z)[TB][Part<DA>::KS]) {
   constexpr int KS = Part<DA>::KS;
   const int l = threadIdx.x & 63;
   float amax = 0.0f;
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
+  for (int tb = 0; tb < TB; ++tb) {
     const int i = tok0 + 16 * tb + (l & 15);
-    const int n = n0 + i;
-    const int pos = n < N ? (axis == 0 ? n / HW : (axis == 1 ? (n / gw) % gh : n % gw)) : 0;
+    const int pos = axis_pos(n0 + i, N, axis, HW, gh, gw);
     const uint32_t* xrow = xs + i * kRS + off / 2;
-    const float* crow = cos_a + pos * (DA / 2);
-    const float* srow = sin_a + pos * (DA / 2);
+    const int trow = pos * (DA / 2);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int c = 4 * ks + (l >> 4);
-      const int jp = (c >> 1) < DA / 2 ? (c >> 1) : DA / 2 - 1;
-      const uint32_t pr = xrow[jp];
-      const float x0 = h2f((uint16_t)(pr & 0xffffu));
-      const float x1 = h2f((uint16_t)(pr >> 16));
-      const float cs = crow[jp], sn = srow[jp];
-      const bool odd = (c & 1) != 0;
-      const float p0 = x0 * (odd ? sn : cs);
-      const float p1 = x1 * (odd ? cs : sn);
-      const float y = p0 + (odd ? p1 : -p1);
+      const float y = rope_channel<DA>(xrow, cos_a, sin_a, trow, c);
       z[tb][ks] = c < DA ? y : 0.0f;
       amax = fmaxf(amax, fabsf(z[tb][ks]));
     }
@@ -250,83 +251,86 @@ __device__ __forceinline__ float rope_tensor(const uint32_t* xs, const float* co
   return amax;
 }
 
-// Codes of rope_tensor's z (A layout) into the LDS code buffer.
-template <int DA, bool F8>
-__device__ __forceinline__ void quant_tensor_a(const float (&z)[4][Part<DA>::KS], float inv,
-                                               int off, int tok0, int8_t* codes) {
+// Codes of rope_part_a's z (A layout) into the LDS code buffer.
+template <int DA, int TB, bool F8>
+__device__ __forceinline__ void quant_part_a(const float (&z)[TB][Part<DA>::KS], float inv, int off,
+                                             int tok0, int8_t* codes) {
   const int l = threadIdx.x & 63;
+  constexpr int KS = Part<DA>::KS;
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb)
+  for (int tb = 0; tb < TB; ++tb) {
+    int8_t* crow = codes + (tok0 + 16 * tb + (l & 15)) * kCodeStride + off;
 #pragma unroll
-    for (int ks = 0; ks < Part<DA>::KS; ++ks) {
+    for (int ks = 0; ks < KS; ks += 2) {
+      const uint32_t pr = code_pair<F8>(z[tb][ks], ks + 1 < KS ? z[tb][ks + 1] : 0.0f, inv);
       const int c = 4 * ks + (l >> 4);
-      if (c < DA)
-        codes[(tok0 + 16 * tb + (l & 15)) * kCodeStride + off + c] = code_byte<F8>(quant(z[tb][ks], inv));
+      if (c < DA) crow[c] = (int8_t)pr;
+      if (ks + 1 < KS && c + 4 < DA) crow[c + 4] = (int8_t)(pr >> 8);
     }
+  }
 }
 
-// Codes of one tensor's z (MFMA output layout) into the LDS code buffer
+// Codes of rotate_part's z (MFMA output layout) into the LDS code buffer
 // ([token][channel], kCodeStride bytes per row).
-template <int DA, bool F8>
-__device__ __forceinline__ void quant_tensor(const float (&z)[4][Part<DA>::JB][4], float inv,
-                                             int off, int tok0, int8_t* codes) {
-  constexpr int JBX = Part<DA>::JB;
+template <int DA, int TB, bool F8>
+__device__ __forceinline__ void quant_part(const float (&z)[TB][Part<DA>::JB][4], float inv,
+                                           int off, int tok0, int8_t* codes) {
   const int l = threadIdx.x & 63;
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb)
+  for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-    for (int jb = 0; jb < JBX; ++jb) {
+    for (int jb = 0; jb < Part<DA>::JB; ++jb) {
       const int j = 16 * jb + (l & 15);
       if (j < DA) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = tok0 + 16 * tb + (l >> 4) + 4 * r;
-          codes[row * kCodeStride + off + j] = code_byte<F8>(quant(z[tb][jb][r], inv));
-        }
+        int8_t* cp = codes + (tok0 + 16 * tb + (l >> 4)) * kCodeStride + off + j;
+        const uint32_t p01 = code_pair<F8>(z[tb][jb][0], z[tb][jb][1], inv);
+        const uint32_t p23 = code_pair<F8>(z[tb][jb][2], z[tb][jb][3], inv);
+        cp[0] = (int8_t)p01;                      // rows 4 r further down for r = 0..3
+        cp[4 * kCodeStride] = (int8_t)(p01 >> 8);
+        cp[8 * kCodeStride] = (int8_t)p23;
+        cp[12 * kCodeStride] = (int8_t)(p23 >> 8);
       }
     }
 }
 
-// Fallback head: RoPE'd fp16 pairs written back over the staged row (the
-// caller stores the tile with coalesced writes).
-template <int DA>
-__device__ __forceinline__ void rope_only_part(uint32_t* xrow, const float* cos_a,
-                                               const float* sin_a, int pos, int off) {
-  float y[DA];
-  rope_part<DA>(xrow, cos_a, sin_a, pos, off, y);
-  __syncthreads();   // every lane has read its inputs before any row is overwritten
-#pragma unroll
-  for (int j = 0; j < DA / 2; ++j)
-    xrow[off / 2 + j] = (uint32_t)f2h(y[2 * j]) | ((uint32_t)f2h(y[2 * j + 1]) << 16);
-}
-
-template <int DA, bool F8>
-__device__ __forceinline__ void v_part(const uint32_t* xrow, int off, float* red,
-                                       int8_t* codesT, int nl, float& scale_out) {
-  float x[DA];
+// V of a block: thread (token n = t mod 128, half h = t / 128) holds channels
+// [h D/2, (h+1) D/2) of its token; block amax; codes transposed into codesT
+// ([channel][token], kCodeStride bytes per channel row).  codesT may be the
+// staging buffer itself: every row is read before the reduction's barriers.
+template <int D, bool F8>
+__device__ __forceinline__ void v_codes(const uint32_t* xs, float* red, int8_t* codesT,
+                                        float& scale_out) {
+  constexpr int kRS = D / 2 + 1;
+  constexpr int C = D / 2;   // channels per thread
+  const int n = threadIdx.x & (kBlock - 1), h = threadIdx.x / kBlock;
+  const uint32_t* xrow = xs + n * kRS + h * (C / 2);
+  float x[C];
   float amax = 0.0f;
 #pragma unroll
-  for (int j = 0; j < DA / 2; ++j) {
-    const uint32_t pr = xrow[off / 2 + j];
+  for (int j = 0; j < C / 2; ++j) {
+    const uint32_t pr = xrow[j];
     x[2 * j] = h2f((uint16_t)(pr & 0xffffu));
     x[2 * j + 1] = h2f((uint16_t)(pr >> 16));
     amax = fmaxf(amax, fmaxf(fabsf(x[2 * j]), fabsf(x[2 * j + 1])));
   }
   float inv, scale;
   block_scale(amax, red, inv, scale);
+  int8_t* cp = codesT + h * C * kCodeStride + n;
 #pragma unroll
-  for (int r = 0; r < DA; ++r) codesT[(off + r) * kCodeStride + nl] = code_byte<F8>(quant(x[r], inv));
+  for (int r = 0; r < C; r += 2) {
+    const uint32_t pr = code_pair<F8>(x[r], x[r + 1], inv);
+    cp[r * kCodeStride] = (int8_t)pr;
+    cp[(r + 1) * kCodeStride] = (int8_t)(pr >> 8);
+  }
   scale_out = scale;
 }
 
-// Coalesced load of a block's fp16 rows [128][D] into LDS rows of D/2 + 1
-// dwords (the odd stride keeps the per-token reads conflict-free); rows past
-// N are zero.
 // Stage 128 fp16 rows (tokens n0..n0+127 of one head, row_stride elements
-// apart) into xs, kRS dwords per row, zero rows for tokens >= N.  Each wave
-// instruction moves one row straight from memory into LDS (global_load_lds,
-// lane L -> dword L of the row): no registers, no waits here.  The caller
-// waits with wait_tiles() before the barrier that publishes the rows.
+// apart) into xs, kRS dwords per row (the odd stride keeps per-token reads
+// conflict-free), zero rows for tokens >= N.  Each wave instruction moves one
+// row straight from memory into LDS (global_load_lds, lane L -> dword L of the
+// row): no registers, no waits here.  The caller waits with wait_tiles()
+// before the barrier that publishes the rows.
 template <int D>
 __device__ __forceinline__ void load_tile(const uint16_t* src, int64_t row_stride, int n0, int N,
                                           uint32_t* xs) {
@@ -434,19 +438,17 @@ __device__ __forceinline__ void store_v_codes(const int8_t* codesT, uint8_t* dst
   }
 }
 
-// A head that is not a fallback head, as seen by one wave (partition of width
-// DA at channel offset off, RoPE axis `axis`): per tensor, RoPE + rotation on
-// the MFMA, block amax, codes into the LDS buffer that held the tensor's rows,
-// coalesced store; then V: block amax and codes, stored transposed.  Every
-// wave runs the same sequence of barriers whatever its partition.
-template <int D, int DA, bool F8, bool ROT>
+// A head that is not a fallback head.  Wave w owns tokens 32w..32w+31 of the
+// block in every partition: per tensor, RoPE + rotation on the MFMA (or RoPE
+// alone), block amax, codes into the LDS buffer that held the tensor's rows,
+// coalesced store; then V: block amax and codes, stored transposed.
+template <int D, int D0, int D1, bool F8, bool ROT>
 __device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* stage_q,
-                                            uint32_t* stage_k, float* red, int blk, int bh,
-                                            int off, int axis, const float* cos_a,
-                                            const float* sin_a, const double* rot) {
+                                            uint32_t* stage_k, float* red, int blk, int bh) {
   constexpr int kRS = D / 2 + 1;
+  constexpr int TB = kBlock / 16 / (kThreads / 64);   // 16-token groups per wave
   const int w = threadIdx.x >> 6;
-  const int tok0 = (w & 1) * 64;
+  const int tok0 = 16 * TB * w;
   const int n0 = blk * kBlock;
   const int HW = a.grid_h * a.grid_w;
   const int64_t head_in = a.in.head_offset(bh, a.H);
@@ -454,30 +456,67 @@ __device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* sta
 
   load_tile<D>(a.q + head_in, a.in.token, n0, a.N, stage_q);
   load_tile<D>(a.k + head_in, a.in.token, n0, a.N, stage_k);
-  float b[Part<DA>::KS][Part<DA>::JB];   // R_a^T of this wave's partition
-  if (ROT) load_rot_frags<DA>(rot, b);
   wait_tiles();
   __syncthreads();
 
-#pragma unroll 1
-  for (int s = 0; s < 2; ++s) {
+  // one tensor (s = 0: Q, 1: K), inlined twice: straight-line code, so
+  // nothing is hoisted across the two tensors and kept live
+  auto tensor = [&](int s) {
     uint32_t* xs = s == 0 ? stage_q : stage_k;
     int8_t* codes = (int8_t*)xs;
     float inv, scale;
+    // the table reads are the same for Q and K; an opaque zero offset per
+    // tensor keeps the compiler from loading them once and holding them in
+    // registers across both tensors
+    int zero = 0;
+    asm volatile("" : "+s"(zero));
+    const float *cos_t = a.cos_t + zero, *sin_t = a.sin_t + zero, *cos_h = a.cos_h + zero;
+    const float *sin_h = a.sin_h + zero, *cos_w = a.cos_w + zero, *sin_w = a.sin_w + zero;
     // every wave is past its last read of xs once the reduction's barriers are
     // passed: the buffer takes the codes next
     if (ROT) {
-      float z[4][Part<DA>::JB][4];
-      const float amax = rotate_tensor<DA, kRS>(xs, cos_a, sin_a, b, off, tok0, n0, a.N, axis, HW,
-                                                a.grid_h, a.grid_w, z);
+      // R_a^T of each partition as B fragments, loaded (from cache) just before
+      // its use; rotation matrices in fp64 [k][r]: t at 0, h at D0^2, w at
+      // D0^2 + D1^2
+      float z0[TB][Part<D0>::JB][4], z1[TB][Part<D1>::JB][4], z2[TB][Part<D1>::JB][4];
+      float amax;
+      {
+        float b[Part<D0>::KS][Part<D0>::JB];
+        const double* rp = a.rot64 + zero;   // read again per tensor, not held
+        load_rot_frags<D0>(rp, b);
+        amax = rotate_part<D0, TB, kRS>(xs, cos_t, sin_t, b, 0, tok0, n0, a.N, 0, HW, a.grid_h,
+                                        a.grid_w, z0);
+      }
+      {
+        float b[Part<D1>::KS][Part<D1>::JB];
+        const double* rp = a.rot64 + D0 * D0 + zero;
+        load_rot_frags<D1>(rp, b);
+        amax = fmaxf(amax, rotate_part<D1, TB, kRS>(xs, cos_h, sin_h, b, D0, tok0, n0, a.N, 1,
+                                                    HW, a.grid_h, a.grid_w, z1));
+      }
+      {
+        float b[Part<D1>::KS][Part<D1>::JB];
+        const double* rp = a.rot64 + D0 * D0 + D1 * D1 + zero;
+        load_rot_frags<D1>(rp, b);
+        amax = fmaxf(amax, rotate_part<D1, TB, kRS>(xs, cos_w, sin_w, b, D0 + D1, tok0, n0,
+                                                    a.N, 2, HW, a.grid_h, a.grid_w, z2));
+      }
       block_scale(amax, red, inv, scale);
-      quant_tensor<DA, F8>(z, inv, off, tok0, codes);
+      quant_part<D0, TB, F8>(z0, inv, 0, tok0, codes);
+      quant_part<D1, TB, F8>(z1, inv, D0, tok0, codes);
+      quant_part<D1, TB, F8>(z2, inv, D0 + D1, tok0, codes);
     } else {
-      float z[4][Part<DA>::KS];
-      const float amax = rope_tensor<DA, kRS>(xs, cos_a, sin_a, off, tok0, n0, a.N, axis, HW,
-                                              a.grid_h, a.grid_w, z);
+      float z0[TB][Part<D0>::KS], z1[TB][Part<D1>::KS], z2[TB][Part<D1>::KS];
+      float amax = rope_part_a<D0, TB, kRS>(xs, cos_t, sin_t, 0, tok0, n0, a.N, 0, HW,
+                                            a.grid_h, a.grid_w, z0);
+      amax = fmaxf(amax, rope_part_a<D1, TB, kRS>(xs, cos_h, sin_h, D0, tok0, n0, a.N, 1, HW,
+                                                  a.grid_h, a.grid_w, z1));
+      amax = fmaxf(amax, rope_part_a<D1, TB, kRS>(xs, cos_w, sin_w, D0 + D1, tok0, n0, a.N,
+                                                  2, HW, a.grid_h, a.grid_w, z2));
       block_scale(amax, red, inv, scale);
-      quant_tensor_a<DA, F8>(z, inv, off, tok0, codes);
+      quant_part_a<D0, TB, F8>(z0, inv, 0, tok0, codes);
+      quant_part_a<D1, TB, F8>(z1, inv, D0, tok0, codes);
+      quant_part_a<D1, TB, F8>(z2, inv, D0 + D1, tok0, codes);
     }
     __syncthreads();
     if (F8)
@@ -490,17 +529,18 @@ __device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* sta
       else
         a.k_scale[(size_t)bh * a.NB + blk] = scale;
     }
-  }
+  };
+  tensor(0);
+  tensor(1);
   __syncthreads();
 
-  // V: staged in the Q buffer, codes (channel rows) in the K buffer
-  const int nl = tok0 + (threadIdx.x & 63);
+  // V: staged in the Q buffer, codes (channel rows) in place
   load_tile<D>(a.v + head_in, a.in.token, n0, a.N, stage_q);
   wait_tiles();
   __syncthreads();
-  int8_t* codes = (int8_t*)stage_k;
+  int8_t* codes = (int8_t*)stage_q;
   float scale;
-  v_part<DA, F8>(stage_q + nl * kRS, off, red, codes, nl, scale);
+  v_codes<D, F8>(stage_q, red, codes, scale);
   __syncthreads();
   if (F8)
     store_v_codes_f8<D>(codes, a.v4 + ((size_t)bh * a.NB + blk) * D * 128);
@@ -509,76 +549,91 @@ __device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* sta
   if (threadIdx.x == 0) a.v_scale[(size_t)bh * a.NB + blk] = scale;
 }
 
-// Fallback head: RoPE'd fp16 Q and K into the padded q_rope/k_rope rows, one
-// token per lane, wave pair a on partition a; then V^T tiles for the fp16
-// attention.
+// Fallback head, RoPE of one staged tensor in place: thread (token n, half h)
+// applies RoPE to partition t (h = 0) or partitions h and w (h = 1) of its
+// token's row in fp32 and writes the fp16 pairs back once every thread has
+// read its row.
 template <int D, int D0, int D1>
-__device__ __forceinline__ void prologue_fallback(const PrologueArgs& a, uint32_t* stage, int blk,
-                                                  int bh) {
+__device__ __forceinline__ void rope_fallback(const PrologueArgs& a, uint32_t* xs, int n0) {
   constexpr int kRS = D / 2 + 1;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int part = __builtin_amdgcn_readfirstlane(w >> 1);
-  const int nl = (w & 1) * 64 + lane;
-  const int n0 = blk * kBlock;
-  const int n = n0 + nl;
+  constexpr int NY = D0 > 2 * D1 ? D0 : 2 * D1;
+  const int n = threadIdx.x & (kBlock - 1);
+  const int half = __builtin_amdgcn_readfirstlane(threadIdx.x / kBlock);
   const int HW = a.grid_h * a.grid_w;
-  const int pos = part == 0 ? n / HW : (part == 1 ? (n / a.grid_w) % a.grid_h : n % a.grid_w);
-  const int off = part == 0 ? 0 : (part == 1 ? D0 : D0 + D1);
-  const float* cos_a = part == 0 ? a.cos_t : (part == 1 ? a.cos_h : a.cos_w);
-  const float* sin_a = part == 0 ? a.sin_t : (part == 1 ? a.sin_h : a.sin_w);
-  const int64_t head_in = a.in.head_offset(bh, a.H);
-  const size_t head_pad = (size_t)bh * a.NB * kBlock;
-  uint32_t* xrow = stage + nl * kRS;
-  // tables are read for every lane; clamp the position of a padding token
-  const int pos_c = n < a.N ? pos : 0;
-#pragma unroll 1
-  for (int s = 0; s < 2; ++s) {
-    load_tile<D>((s == 0 ? a.q : a.k) + head_in, a.in.token, n0, a.N, stage);
-    wait_tiles();
-    __syncthreads();
-    if (part == 0)
-      rope_only_part<D0>(xrow, cos_a, sin_a, pos_c, off);
-    else
-      rope_only_part<D1>(xrow, cos_a, sin_a, pos_c, off);
-    __syncthreads();
-    store_tile_all<D>((s == 0 ? a.q_rope : a.k_rope) + head_pad * D, n0, stage);
-    __syncthreads();
+  uint32_t* xrow = xs + n * kRS;
+  float y[NY];
+  if (half == 0) {
+    float yt[D0];
+    rope_part<D0>(xrow, a.cos_t, a.sin_t, axis_pos(n0 + n, a.N, 0, HW, a.grid_h, a.grid_w), 0, yt);
+#pragma unroll
+    for (int i = 0; i < D0; ++i) y[i] = yt[i];
+  } else {
+    float yh[D1], yw[D1];
+    rope_part<D1>(xrow, a.cos_h, a.sin_h, axis_pos(n0 + n, a.N, 1, HW, a.grid_h, a.grid_w), D0, yh);
+    rope_part<D1>(xrow, a.cos_w, a.sin_w, axis_pos(n0 + n, a.N, 2, HW, a.grid_h, a.grid_w),
+                  D0 + D1, yw);
+#pragma unroll
+    for (int i = 0; i < D1; ++i) {
+      y[i] = yh[i];
+      y[D1 + i] = yw[i];
+    }
   }
-  load_tile<D>(a.v + head_in, a.in.token, n0, a.N, stage);
-  wait_tiles();
-  __syncthreads();
-  store_vt_tiles<D>(stage, a.v_t + (head_pad + n0) * D);
+  __syncthreads();   // every thread has read its inputs before any row is overwritten
+  if (half == 0) {
+#pragma unroll
+    for (int j = 0; j < D0 / 2; ++j)
+      xrow[j] = (uint32_t)f2h(y[2 * j]) | ((uint32_t)f2h(y[2 * j + 1]) << 16);
+  } else {
+#pragma unroll
+    for (int j = 0; j < D1; ++j)
+      xrow[D0 / 2 + j] = (uint32_t)f2h(y[2 * j]) | ((uint32_t)f2h(y[2 * j + 1]) << 16);
+  }
 }
 
-// 3 waves per SIMD: two 6-wave work-groups per CU, so that one group's MFMA
-// phase overlaps the other's memory phases.
+// Fallback head: RoPE'd fp16 Q and K into the padded q_rope/k_rope rows, then
+// V^T tiles for the fp16 attention.
+template <int D, int D0, int D1>
+__device__ __forceinline__ void prologue_fallback(const PrologueArgs& a, uint32_t* stage_q,
+                                                  uint32_t* stage_k, int blk, int bh) {
+  const int n0 = blk * kBlock;
+  const int64_t head_in = a.in.head_offset(bh, a.H);
+  const size_t head_pad = (size_t)bh * a.NB * kBlock;
+  load_tile<D>(a.q + head_in, a.in.token, n0, a.N, stage_q);
+  load_tile<D>(a.k + head_in, a.in.token, n0, a.N, stage_k);
+  wait_tiles();
+  __syncthreads();
+  rope_fallback<D, D0, D1>(a, stage_q, n0);
+  rope_fallback<D, D0, D1>(a, stage_k, n0);
+  __syncthreads();
+  store_tile_all<D>(a.q_rope + head_pad * D, n0, stage_q);
+  store_tile_all<D>(a.k_rope + head_pad * D, n0, stage_k);
+  __syncthreads();
+  load_tile<D>(a.v + head_in, a.in.token, n0, a.N, stage_q);
+  wait_tiles();
+  __syncthreads();
+  store_vt_tiles<D>(stage_q, a.v_t + (head_pad + n0) * D);
+}
+
+// One work-group per (128-token block, head), 4 waves (one per SIMD): two
+// work-groups share a CU (LDS), so one group's MFMA phase overlaps the other's
+// memory phases.
 template <int D, int D0, int D1, bool F8, bool ROT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void k_prologue(PrologueArgs a) {
   static_assert(D0 + 2 * D1 == D, "split must be (D0, D1, D1)");
   constexpr int kRS = D / 2 + 1;   // staged fp16 row, in dwords
   static_assert(kBlock * kCodeStride <= kBlock * kRS * 4, "codes fit in a staging buffer");
   static_assert(D * kCodeStride <= kBlock * kRS * 4, "transposed codes fit in a staging buffer");
+  static_assert(Part<D0>::JB == Part<D1>::JB, "partitions share the output block count");
   // two buffers of 128 staged fp16 rows (Q and K; later V and the codes)
   __shared__ __align__(16) uint32_t stage_q[kBlock * kRS];
   __shared__ __align__(16) uint32_t stage_k[kBlock * kRS];
   __shared__ float red[16];
   const int blk = blockIdx.x, bh = blockIdx.y;
-  if (a.fallback.test(bh)) {
-    prologue_fallback<D, D0, D1>(a, stage_q, blk, bh);
-    return;
-  }
-  // wave pair 2a, 2a+1 on partition a; rotation matrices in fp64 [k][r]:
-  // t at 0, h at D0^2, w at D0^2 + D1^2
-  const int part = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) >> 1);
-  if (part == 0)
-    prologue_qk<D, D0, F8, ROT>(a, stage_q, stage_k, red, blk, bh, 0, 0, a.cos_t, a.sin_t, a.rot64);
-  else if (part == 1)
-    prologue_qk<D, D1, F8, ROT>(a, stage_q, stage_k, red, blk, bh, D0, 1, a.cos_h, a.sin_h,
-                                a.rot64 + D0 * D0);
+  if (a.fallback.test(bh))
+    prologue_fallback<D, D0, D1>(a, stage_q, stage_k, blk, bh);
   else
-    prologue_qk<D, D1, F8, ROT>(a, stage_q, stage_k, red, blk, bh, D0 + D1, 2, a.cos_w, a.sin_w,
-                                a.rot64 + D0 * D0 + D1 * D1);
+    prologue_qk<D, D0, D1, F8, ROT>(a, stage_q, stage_k, red, blk, bh);
 }
 
 template <int D, int D0, int D1>
