@@ -12,7 +12,8 @@ attention TOPS = 4*B*H*N^2*D / step time.
 
 Prints one JSON line.  Besides the contract fields it carries the roofline
 of the dominant kernel (the INT4 attention, timed with HIP events on the
-stream it runs on), the per-kernel times, and the CPU oracle timed on a bounded
+stream it runs on, with the VALU-busy share of the unit that bounds it), the
+per-kernel times, and the CPU oracle timed on a bounded
 sample on this host (cpu_baseline).
 """
 from __future__ import annotations
@@ -34,6 +35,7 @@ PEAK_I8_TOPS = 5000.0        # MI355X dense int8 MFMA (5.0 POPS)
 PEAK_F16_TFLOPS = 2500.0     # MI355X dense fp16 MFMA (2.5 PFLOPS)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E (8 TB/s)
 PMC_FILE = os.path.join(ROOT, "profiles", "int4_attn_f8_720p_pmc.txt")
+SQ_FILE = os.path.join(ROOT, "profiles", "int4_attn_f8_720p_sq_counters.txt")
 KERNEL_SRC = os.path.join(ROOT, "video_diffusion_transformers_amd", "csrc", "int4_attn.hip")
 
 
@@ -74,6 +76,25 @@ def traffic_from_profile(launch_ms: float):
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def valu_busy_from_profile():
+    """Share of the INT4 kernel's SIMD clocks with a VALU instruction issuing,
+    from the committed rocprofv3 SQ counter summary, if it was taken on the
+    current kernel source (the kernel is bound by that VALU work, not by MFMA)."""
+    if not os.path.exists(SQ_FILE):
+        return None
+    with open(SQ_FILE) as f:
+        txt = f.read()
+    if f"int4_attn.hip sha256[:16] = {kernel_hash()}" not in txt:
+        return None
+    for ln in txt.splitlines():
+        if ln.startswith("VALU share of SIMD clocks:"):
+            try:
+                return float(ln.split(":", 1)[1])
+            except ValueError:
+                return None
+    return None
 
 
 def main():
@@ -147,7 +168,8 @@ def main():
     traffic = traffic_from_profile(k2_ms)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_I8_TOPS,
                 "unit": "TOP/s", "frac": round(achieved / PEAK_I8_TOPS, 4), "traffic": traffic,
-                "kernel": "k_int4_attn_f8<128>", "algorithmic_ops_per_launch": int4_ops}
+                "kernel": "k_int4_attn_f8<128>", "algorithmic_ops_per_launch": int4_ops,
+                "limiter": "valu", "limiter_busy": valu_busy_from_profile()}
     # prologue: algorithmic HBM bytes per token per head (read Q,K,V fp16; write
     # Q,K,V codes one byte each in the FP8-lane layout; block scales are negligible)
     k1_bytes = BH * N * (3 * 2 * D + 3 * D)
