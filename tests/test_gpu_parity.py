@@ -91,13 +91,10 @@ def test_pcode_eval_random_scores(c, spread, layout):
 
 # ------------------------------------------------------------------ prologue
 
-@pytest.mark.parametrize("layout", ["packed", "fp8"])
-@pytest.mark.parametrize("name", ["tiny", "small", "480p", "720p"])
-def test_prologue_bit_exact(name, layout):
-    run = get_run(name, layout=layout)
-    run.prepare()
+def _check_prologue_heads(run, heads, layout):
+    name = run.cfg.name
     g = run.gpu_prepared()
-    for bh in HEADS[name]:
+    for bh in heads:
         fb = bool(run.mask[bh])
         p = run.oracle_prep(bh, fallback=fb)
         if fb:
@@ -118,6 +115,27 @@ def test_prologue_bit_exact(name, layout):
         assert np.array_equal(g["v4"][bh], vt(p["v_codes"], run.N_pad)), (name, bh)
         for f in ("q_scale_l2", "k_scale", "v_scale"):
             assert np.array_equal(g[f][bh].view(np.uint32), p[f].view(np.uint32)), (name, bh, f)
+
+
+@pytest.mark.parametrize("layout", ["packed", "fp8"])
+@pytest.mark.parametrize("name", ["tiny", "small", "480p", "720p"])
+def test_prologue_bit_exact(name, layout):
+    run = get_run(name, layout=layout)
+    run.prepare()
+    _check_prologue_heads(run, HEADS[name], layout)
+
+
+@pytest.mark.parametrize("layout", ["packed", "fp8"])
+def test_prologue_fallback_heads_d128_bit_exact(layout):
+    """D = 128 with fallback and INT4 heads in one launch, a ragged last block
+    (N = 306): RoPE'd fp16 Q/K and the V^T tiles of the fallback heads, codes
+    and scales of the others, bit for bit."""
+    cfg = synth.custom_config("fb128", 1, 4, (2, 9, 17), 128, (44, 42, 42), dist="video",
+                              cfg_seed=53)
+    run = Run(cfg, layout=LAYOUTS[layout])
+    run.mask = np.array([0, 1, 0, 1], np.uint8)
+    run.prepare()
+    _check_prologue_heads(run, range(cfg.BH), layout)
 
 
 # ------------------------------------------------------------------ INT4 attention
