@@ -185,7 +185,8 @@ def main():
 
     if not args.no_extras:
         # the same INT4 attention on the nibble-packed layout (i8 MFMA kernel)
-        prep_p = R.PreparedDevice(shape, with_rope=False, layout=R.LAYOUT_PACKED)
+        # (fallback heads, if any, need the fp16 RoPE'd buffers as well)
+        prep_p = R.PreparedDevice(shape, with_rope=n_fb > 0, layout=R.LAYOUT_PACKED)
         R.prepare_qkv(shape, qd, kd, vd, rr, prep_p, mask)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         R.int4_fwd(shape, prep_p, o, mask=mask)
