@@ -279,7 +279,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8",
+        "dtype": "fp8",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: B={B} H={H} grid {'x'.join(map(str, cfg.grid))} "
                                f"N={N} D={D} split {'/'.join(map(str, cfg.split))}, "
