@@ -92,11 +92,12 @@ struct Fp16Kernel {
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[sub][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = fmaxf(mx, other_half(mx));
     const float mnew = fmaxf(m, mx * a.kappa);
     const float alpha = __builtin_amdgcn_exp2f(m - mnew);
     m = mnew;
-    if (__ballot(alpha != 1.0f) != 0) {
+    // the running max moves in a minority of tiles (mostly the first ones)
+    if (__builtin_expect(__ballot(alpha != 1.0f) != 0, 0)) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -109,7 +110,7 @@ struct Fp16Kernel {
     // of nats) takes fl(fl(S kappa) - m') <= 0 instead.
     const bool exact_arg = __ballot(fabsf(mnew) > 4096.0f) != 0;
     float e[2][16];
-    if (!exact_arg) {
+    if (__builtin_expect(!exact_arg, 1)) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -197,7 +198,7 @@ struct Fp16Kernel {
       __builtin_amdgcn_s_setprio(1);
       qk(sk[buf], qf, S);
       __builtin_amdgcn_s_setprio(0);
-      if (t == NT - 1 && nv_last < kKT) {
+      if (__builtin_expect(t == NT - 1 && nv_last < kKT, 0)) {
         // opaque: nv_last is loop-invariant, and the comparisons would be
         // hoisted out of the loop and kept live as SGPR masks
         int nv = nv_last;
@@ -215,7 +216,7 @@ struct Fp16Kernel {
       __syncthreads();
     }
 
-    l += __shfl_xor(l, 32, 64);
+    l += other_half(l);
     const int query = qb * kBlock + 32 * w + col;
     if (query < N) {
       const float il = 1.0f / l;

@@ -100,7 +100,7 @@ __device__ __forceinline__ CodeCtx make_ctx(float ct, float mnew, float log2_15,
 template <int NS>
 __device__ __forceinline__ void exp_scores(const float (&f)[NS], const CodeCtx& cx,
                                            float (&y)[NS]) {
-  if (!cx.exact_arg) {
+  if (__builtin_expect(!cx.exact_arg, 1)) {
 #pragma unroll
     for (int r = 0; r < NS; ++r) y[r] = __builtin_amdgcn_exp2f(fmaf(f[r], cx.cq, cx.m15n));
   } else {
@@ -144,7 +144,7 @@ __device__ __forceinline__ v4i pcode16(const float (&f)[16], float fmax, const C
     exp_scores<1>(fm, cx, ym);
   }
   const float ymax = ym[0];
-  if (!wave_any(ymax >= 0.5f - cx.delta)) return v4i{0, 0, 0, 0};
+  if (__builtin_expect(!wave_any(ymax >= 0.5f - cx.delta), 0)) return v4i{0, 0, 0, 0};
   float g = 1.0f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) g = fminf(g, fabsf(__builtin_amdgcn_fractf(y[r]) - 0.5f));
@@ -156,7 +156,7 @@ __device__ __forceinline__ v4i pcode16(const float (&f)[16], float fmax, const C
     v = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * i + 2], 2, v);
     pk[i] = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * i + 3], 3, v);
   }
-  if (wave_any(g < cx.delta)) {
+  if (__builtin_expect(wave_any(g < cx.delta), 0)) {
     // rare: some score of the group sits within delta of a rounding boundary;
     // recompute the whole group exactly
 #pragma unroll
@@ -221,7 +221,9 @@ __device__ __forceinline__ v4i pcode16_f8(const float (&f)[16], const CodeCtx& c
     rr[r] = __builtin_rintf(y[r]);
     g = fmaxf(g, fabsf(y[r] - rr[r]));
   }
-  if (wave_any(g > 0.5f - cx.delta)) {
+  // rare (a score within delta of a rounding boundary somewhere in the
+  // wave): laid out away from the common path
+  if (__builtin_expect(wave_any(g > 0.5f - cx.delta), 0)) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       int j = (int)rr[r] + signbit01(rr[r] - y[r]);          // rne(y) + [y > rne(y)]
@@ -305,7 +307,7 @@ struct Int4Kernel {
       for (int r = 1; r < 16; ++r) smx[sub] = max(smx[sub], S[sub][r]);
     }
     int mx = max(max(smx[0], smx[1]), max(smx[2], smx[3]));
-    mx = max(mx, __shfl_xor(mx, 32, 64));
+    mx = max(mx, other_half(mx));
 
     const float ct = qs * a.k_scale[sidx];
     const float smax = (float)(mx >> 8) * ct;
@@ -458,7 +460,7 @@ struct Int4Kernel {
       pv(a, dbg, bh, t, sv[buf], P, O);
     }
 
-    l += __shfl_xor(l, 32, 64);
+    l += other_half(l);
     const int query = qb * kBlock + 32 * w + col;
     if (DBG && hh == 0) {
       dbg.m_final[32 * w + col] = m;
@@ -639,7 +641,7 @@ struct Int4F8Kernel {
       for (int r = 1; r < 16; ++r) smx[sub] = fmaxf(smx[sub], S[sub][r]);
     }
     float mx = fmaxf(fmaxf(smx[0], smx[1]), fmaxf(smx[2], smx[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = fmaxf(mx, other_half(mx));
 
     // the block scales are read through the scalar unit (uniform address):
     // as vector loads they would sit behind the next tile's loads in vmcnt order
@@ -765,7 +767,7 @@ struct Int4F8Kernel {
       qk(sk[buf], qf, S);
       __builtin_amdgcn_s_setprio(0);
       int nv = kBlock;
-      if (t == NT - 1 && nv_last < kBlock) {
+      if (__builtin_expect(t == NT - 1 && nv_last < kBlock, 0)) {
         // opaque: nv_last is loop-invariant, and the 64 comparisons would be
         // hoisted out of the loop and kept live (as SGPR masks) throughout it
         nv = nv_last;
@@ -783,7 +785,7 @@ struct Int4F8Kernel {
       __syncthreads();
     }
 
-    l += __shfl_xor(l, 32, 64);
+    l += other_half(l);
     const int query = qb * kBlock + 32 * w + col;
     if (DBG && hh == 0) {
       dbg.m_final[32 * w + col] = m;

@@ -18,6 +18,17 @@ struct HeadBits {
   __host__ __device__ bool test(int bh) const { return (w[bh >> 5] >> (bh & 31)) & 1u; }
 };
 
+// The value held by lane ^ 32 of this wave (the other 32-lane half):
+// ds_bpermute reads lane (byte address / 4) mod 64, so the thread index needs
+// no masking.  Cheaper than __shfl_xor, whose generic width handling costs
+// extra VALU per call.
+__device__ __forceinline__ int other_half(int v) {
+  return __builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 32u) << 2), v);
+}
+__device__ __forceinline__ float other_half(float v) {
+  return __int_as_float(other_half(__float_as_int(v)));
+}
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
