@@ -158,25 +158,37 @@ struct Fp16Kernel {
       for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const v8h*)(qrow + 16 * ks + 8 * hh);
     }
 
-    // per-lane byte offsets of the tile loads (fixed), the tile base moves
+    // tile loads straight into LDS: wave w, instruction i fills chunks
+    // (NW i + w) * 64 + lane of the tile.  Instruction i lands 16 K rows (32
+    // V^T rows) further down than instruction 0 and the swizzle keys repeat
+    // with that period, so its per-lane byte offset is instruction 0's plus
+    // 4096 i: the uniform part goes to the scalar base (saddr form) and one
+    // 32-bit offset register per tensor remains.
     typedef __attribute__((address_space(3))) void* lds_ptr;
     const int wu = __builtin_amdgcn_readfirstlane(w);
-    uint32_t koff[LOADS], voff[LOADS];
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int pc = (NW * i + w) * 64 + lane;   // physical chunk
+    static_assert(NW * 64 * 16 == 4096, "4 KiB per load instruction of the work-group");
+    uint32_t koff0, voff0;
+    {
+      const int pc = w * 64 + lane;   // physical chunk of instruction 0
       const int krow = pc / KCPR, vrow = pc / 8;
-      koff[i] = krow * KRB + 16 * ((pc % KCPR) ^ kswz(krow));
-      voff[i] = vrow * 128 + 16 * ((pc % 8) ^ vswz(vrow));
+      koff0 = krow * KRB + 16 * ((pc % KCPR) ^ kswz(krow));
+      voff0 = vrow * 128 + 16 * ((pc % 8) ^ vswz(vrow));
     }
     auto gload = [&](int t, int buf) {
       const uint8_t* kb = (const uint8_t*)(a.k + (head_pad + (size_t)t * kKT) * D);
       const uint8_t* vb = (const uint8_t*)(a.v_t + (head_pad + (size_t)t * kKT) * D);
+      // opaque per tile: keeps the loop from turning base + offset into
+      // per-lane 64-bit pointers held in registers
+      uint32_t ko = koff0, vo = voff0;
+      asm volatile("" : "+v"(ko), "+v"(vo));
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        __builtin_amdgcn_global_load_lds((const void*)(kb + koff[i]),
+        const uint8_t* kbi = kb + 4096 * i;
+        const uint8_t* vbi = vb + 4096 * i;
+        asm volatile("" : "+s"(kbi), "+s"(vbi));
+        __builtin_amdgcn_global_load_lds((const void*)(kbi + ko),
                                          (lds_ptr)(sk[buf] + (NW * i + wu) * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vb + voff[i]),
+        __builtin_amdgcn_global_load_lds((const void*)(vbi + vo),
                                          (lds_ptr)(sv[buf] + (NW * i + wu) * 1024), 16, 0, 0);
       }
     };
