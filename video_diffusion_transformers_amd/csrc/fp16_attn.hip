@@ -87,13 +87,16 @@ struct Fp16Kernel {
 
   __device__ __forceinline__ static void softmax(const Fp16Args& a, v16f (&S)[2], float& m,
                                                  float& l, v16f (&O)[DB], v8h (&P)[2][2]) {
-    float mx = S[0][0];
+    // scores of finite fp16 inputs are never NaN: plain v_max3 chains
+    float mx = vmax3(S[0][0], S[0][1], S[0][2]);
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+    for (int r = 3; r < 15; r += 2) mx = vmax3(mx, S[0][r], S[0][r + 1]);
+    mx = vmax3(mx, S[0][15], S[1][0]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[sub][r]);
-    mx = fmaxf(mx, other_half(mx));
-    const float mnew = fmaxf(m, mx * a.kappa);
+    for (int r = 1; r < 15; r += 2) mx = vmax3(mx, S[1][r], S[1][r + 1]);
+    mx = vmax2(mx, S[1][15]);
+    mx = vmax2(mx, other_half(mx));
+    const float mnew = vmax2(m, mx * a.kappa);
     const float alpha = __builtin_amdgcn_exp2f(m - mnew);
     m = mnew;
     // the running max moves in a minority of tiles (mostly the first ones)

@@ -632,22 +632,27 @@ struct Int4F8Kernel {
     const int hh = lane >> 5, col = lane & 31;
     const size_t sidx = (size_t)bh * a.NB + t;
 
-    // a running chain: it compiles to v_max3 with one canonicalisation per group
-    float smx[4];
+    // row max as plain v_max3 chains: the scores are exact integers or -inf,
+    // never NaN, so the quieting that fmaxf needs on MFMA results is dropped
+    float smx[4], rest[4];
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
-      smx[sub] = S[sub][0];
+      smx[sub] = vmax3(S[sub][0], S[sub][1], S[sub][2]);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) smx[sub] = fmaxf(smx[sub], S[sub][r]);
+      for (int r = 3; r < 15; r += 2) smx[sub] = vmax3(smx[sub], S[sub][r], S[sub][r + 1]);
+      rest[sub] = S[sub][15];
     }
-    float mx = fmaxf(fmaxf(smx[0], smx[1]), fmaxf(smx[2], smx[3]));
-    mx = fmaxf(mx, other_half(mx));
+    float mx = vmax3(smx[0], smx[1], rest[0]);
+    mx = vmax3(mx, smx[2], rest[1]);
+    mx = vmax3(mx, smx[3], rest[2]);
+    mx = vmax2(mx, rest[3]);
+    mx = vmax2(mx, other_half(mx));
 
     // the block scales are read through the scalar unit (uniform address):
     // as vector loads they would sit behind the next tile's loads in vmcnt order
     typedef const __attribute__((address_space(4))) float* cfloat_ptr;
     const float ct = qs * ((cfloat_ptr)a.k_scale)[sidx];
-    const float mnew = fmaxf(m, mx * ct);
+    const float mnew = vmax2(m, mx * ct);
     const float alpha = __builtin_amdgcn_exp2f(m - mnew);
     // O is kept in units of the current tile's V scale; a rescale error of an
     // ulp is far below the fp16 output rounding
@@ -662,7 +667,7 @@ struct Int4F8Kernel {
       for (int r = 0; r < 16; ++r) O[db][r] *= beta;
     const CodeCtx cx = make_ctx(ct, mnew, a.log2_15, 1.0f);
 
-    float ls = 0.0f;
+    float ls = -0.0f;   // -0 + y == y for every y: no add of a zero start
     float rr[4][16];
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {

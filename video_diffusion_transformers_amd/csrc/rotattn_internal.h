@@ -29,6 +29,20 @@ __device__ __forceinline__ float other_half(float v) {
   return __int_as_float(other_half(__float_as_int(v)));
 }
 
+// Max of floats that are never NaN, as single v_max3 / v_max instructions
+// (fmaxf must quiet signalling NaNs of operands the compiler cannot prove
+// canonical, such as MFMA results, which costs a v_max per chain).
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
