@@ -36,6 +36,7 @@ PEAK_F16_TFLOPS = 2500.0     # MI355X dense fp16 MFMA (2.5 PFLOPS)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E (8 TB/s)
 PMC_FILE = os.path.join(ROOT, "profiles", "int4_attn_f8_720p_pmc.txt")
 SQ_FILE = os.path.join(ROOT, "profiles", "int4_attn_f8_720p_sq_counters.txt")
+PROFILED_WORKLOAD = "720p"   # the workload both counter summaries were taken on
 KERNEL_SRC = os.path.join(ROOT, "video_diffusion_transformers_amd", "csrc", "int4_attn.hip")
 
 
@@ -59,10 +60,11 @@ def kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile(launch_ms: float):
+def traffic_from_profile(workload: str):
     """HBM bytes per launch of the INT4 kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
-    if not os.path.exists(PMC_FILE):
+    counter summary, if it was taken on this workload and the current kernel
+    source."""
+    if workload != PROFILED_WORKLOAD or not os.path.exists(PMC_FILE):
         return None
     vals = {}
     with open(PMC_FILE) as f:
@@ -78,11 +80,12 @@ def traffic_from_profile(launch_ms: float):
         return None
 
 
-def valu_busy_from_profile():
+def valu_busy_from_profile(workload: str):
     """Share of the INT4 kernel's SIMD clocks with a VALU instruction issuing,
-    from the committed rocprofv3 SQ counter summary, if it was taken on the
-    current kernel source (the kernel is bound by that VALU work, not by MFMA)."""
-    if not os.path.exists(SQ_FILE):
+    from the committed rocprofv3 SQ counter summary, if it was taken on this
+    workload and the current kernel source (the kernel is bound by that VALU
+    work, not by MFMA)."""
+    if workload != PROFILED_WORKLOAD or not os.path.exists(SQ_FILE):
         return None
     with open(SQ_FILE) as f:
         txt = f.read()
@@ -165,11 +168,11 @@ def main():
     int4_ops = 4.0 * n_int4 * N * N * D
     k2_ms = float(k2.mean())
     achieved = int4_ops / (k2_ms * 1e-3) / 1e12 if n_int4 else 0.0
-    traffic = traffic_from_profile(k2_ms)
+    traffic = traffic_from_profile(args.workload)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_I8_TOPS,
                 "unit": "TOP/s", "frac": round(achieved / PEAK_I8_TOPS, 4), "traffic": traffic,
                 "kernel": "k_int4_attn_f8<128>", "algorithmic_ops_per_launch": int4_ops,
-                "limiter": "valu", "limiter_busy": valu_busy_from_profile()}
+                "limiter": "valu", "limiter_busy": valu_busy_from_profile(args.workload)}
     # prologue: algorithmic HBM bytes per token per head (read Q,K,V fp16; write
     # Q,K,V codes one byte each in the FP8-lane layout; block scales are negligible)
     k1_bytes = BH * N * (3 * 2 * D + 3 * D)

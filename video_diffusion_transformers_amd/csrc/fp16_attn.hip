@@ -145,8 +145,11 @@ struct Fp16Kernel {
   }
 
   __device__ static void run(const Fp16Args& a) {
-    __shared__ __align__(16) uint8_t sk[2][kKT * KRB];
-    __shared__ __align__(16) uint8_t sv[2][D * 128];
+    // two K and two V^T buffers as separate arrays, selected at compile time:
+    // the compiler then sees that a tile load and the LDS reads of the other
+    // buffer do not overlap and does not wait for the load before them
+    __shared__ __align__(16) uint8_t sk0[kKT * KRB], sk1[kKT * KRB];
+    __shared__ __align__(16) uint8_t sv0[D * 128], sv1[D * 128];
     const int qb = blockIdx.x, bh = blockIdx.y;
     if (!a.run.test(bh)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -177,22 +180,30 @@ struct Fp16Kernel {
       koff0 = krow * KRB + 16 * ((pc % KCPR) ^ kswz(krow));
       voff0 = vrow * 128 + 16 * ((pc % 8) ^ vswz(vrow));
     }
-    auto gload = [&](int t, int buf) {
+    auto gloadK = [&](int t, uint8_t* dst) {
       const uint8_t* kb = (const uint8_t*)(a.k + (head_pad + (size_t)t * kKT) * D);
-      const uint8_t* vb = (const uint8_t*)(a.v_t + (head_pad + (size_t)t * kKT) * D);
       // opaque per tile: keeps the loop from turning base + offset into
       // per-lane 64-bit pointers held in registers
-      uint32_t ko = koff0, vo = voff0;
-      asm volatile("" : "+v"(ko), "+v"(vo));
+      uint32_t ko = koff0;
+      asm volatile("" : "+v"(ko));
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const uint8_t* kbi = kb + 4096 * i;
-        const uint8_t* vbi = vb + 4096 * i;
-        asm volatile("" : "+s"(kbi), "+s"(vbi));
+        asm volatile("" : "+s"(kbi));
         __builtin_amdgcn_global_load_lds((const void*)(kbi + ko),
-                                         (lds_ptr)(sk[buf] + (NW * i + wu) * 1024), 16, 0, 0);
+                                         (lds_ptr)(dst + (NW * i + wu) * 1024), 16, 0, 0);
+      }
+    };
+    auto gloadV = [&](int t, uint8_t* dst) {
+      const uint8_t* vb = (const uint8_t*)(a.v_t + (head_pad + (size_t)t * kKT) * D);
+      uint32_t vo = voff0;
+      asm volatile("" : "+v"(vo));
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const uint8_t* vbi = vb + 4096 * i;
+        asm volatile("" : "+s"(vbi));
         __builtin_amdgcn_global_load_lds((const void*)(vbi + vo),
-                                         (lds_ptr)(sv[buf] + (NW * i + wu) * 1024), 16, 0, 0);
+                                         (lds_ptr)(dst + (NW * i + wu) * 1024), 16, 0, 0);
       }
     };
 
@@ -202,16 +213,16 @@ struct Fp16Kernel {
     for (int db = 0; db < DB; ++db) O[db] = v16f{0.0f};
     const int nv_last = N - (NT - 1) * kKT;
 
-    gload(0, 0);
+    gloadK(0, sk0);
+    gloadV(0, sv0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-#pragma unroll 1
-    for (int t = 0; t < NT; ++t) {
-      const int buf = t & 1;
+    // tile t in (skc, svc); tile t+1 goes to (skn, svn), last read in tile t-1
+    auto step = [&](int t, const uint8_t* skc, const uint8_t* svc, uint8_t* skn, uint8_t* svn) {
       v16f S[2];
       v8h P[2][2];
       __builtin_amdgcn_s_setprio(1);
-      qk(sk[buf], qf, S);
+      qk(skc, qf, S);
       __builtin_amdgcn_s_setprio(0);
       if (__builtin_expect(t == NT - 1 && nv_last < kKT, 0)) {
         // opaque: nv_last is loop-invariant, and the comparisons would be
@@ -221,14 +232,21 @@ struct Fp16Kernel {
         mask_tail(S, nv);
       }
       softmax(a, S, m, l, O, P);
-      // tile t+1 -> the other buffers, last read in tile t-1 (before the barrier)
-      if (t + 1 < NT) gload(t + 1, buf ^ 1);
+      if (t + 1 < NT) {
+        gloadK(t + 1, skn);
+        gloadV(t + 1, svn);
+      }
       __builtin_amdgcn_s_setprio(1);
-      pv(sv[buf], P, O);
+      pv(svc, P, O);
       __builtin_amdgcn_s_setprio(0);
       // this thread's tile loads have landed in LDS before anyone passes the barrier
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
+    };
+#pragma unroll 1
+    for (int t = 0; t < NT; t += 2) {
+      step(t, sk0, sv0, sk1, sv1);
+      if (t + 1 < NT) step(t + 1, sk1, sv1, sk0, sv0);
     }
 
     l += other_half(l);
