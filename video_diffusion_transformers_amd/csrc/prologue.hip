@@ -502,6 +502,10 @@ __device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* sta
                                                     a.N, 2, HW, a.grid_h, a.grid_w, z2));
       }
       block_scale(amax, red, inv, scale);
+      // K pass, past the reduction's barriers: every wave is done with the Q
+      // codes in stage_q and has issued its last table load, so V's rows can
+      // stream in while K is quantized and stored
+      if (s == 1) load_tile<D>(a.v + head_in, a.in.token, n0, a.N, stage_q);
       quant_part<D0, TB, F8>(z0, inv, 0, tok0, codes);
       quant_part<D1, TB, F8>(z1, inv, D0, tok0, codes);
       quant_part<D1, TB, F8>(z2, inv, D0 + D1, tok0, codes);
@@ -514,6 +518,7 @@ __device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* sta
       amax = fmaxf(amax, rope_part_a<D1, TB, kRS>(xs, cos_w, sin_w, D0 + D1, tok0, n0, a.N,
                                                   2, HW, a.grid_h, a.grid_w, z2));
       block_scale(amax, red, inv, scale);
+      if (s == 1) load_tile<D>(a.v + head_in, a.in.token, n0, a.N, stage_q);
       quant_part_a<D0, TB, F8>(z0, inv, 0, tok0, codes);
       quant_part_a<D1, TB, F8>(z1, inv, D0, tok0, codes);
       quant_part_a<D1, TB, F8>(z2, inv, D0 + D1, tok0, codes);
@@ -534,8 +539,7 @@ __device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* sta
   tensor(1);
   __syncthreads();
 
-  // V: staged in the Q buffer, codes (channel rows) in place
-  load_tile<D>(a.v + head_in, a.in.token, n0, a.N, stage_q);
+  // V: staged in the Q buffer (requested during the K pass), codes in place
   wait_tiles();
   __syncthreads();
   int8_t* codes = (int8_t*)stage_q;
