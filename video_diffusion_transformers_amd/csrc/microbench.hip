@@ -75,9 +75,12 @@ __global__ __launch_bounds__(256) void k_lds(float* out, int iters) {
   const int lane = threadIdx.x & 63;
   uint4 acc = uint4{0, 0, 0, 0};
   for (int i = 0; i < iters; ++i) {
+    // the tile is unchanged across iterations: without this compiler barrier
+    // the reads would be loaded once and reused, and no LDS traffic measured
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int idx = ((lane & 31) * 9 + (lane >> 5) + 2 * j + (i & 1)) & 1023;
+      const int idx = ((lane & 31) * 9 + (lane >> 5) + 2 * j + (i & 7)) & 1023;
       const uint4 v = tile[idx];
       acc.x ^= v.x; acc.y += v.y; acc.z ^= v.z; acc.w += v.w;
     }
