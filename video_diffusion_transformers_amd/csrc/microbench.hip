@@ -177,6 +177,31 @@ static void launch_rate(void* p) {
   RateCtx* c = (RateCtx*)p;
   hipLaunchKernelGGL(c->kern, dim3(c->blocks), dim3(256), 0, 0, c->out, c->iters);
 }
+// MFMA and VALU work in the same wave: each step is one i8 32x32x32 MFMA
+// (four independent accumulators) and N independent v_fma_f32 (eight
+// chains).  Clocks per step against the MFMA alone and N FMAs alone show how
+// much of the matrix core's time can hide vector work on one SIMD.
+template <int N>
+__global__ __launch_bounds__(256) void k_mix_same(float* out, int iters) {
+  v4i a = {(int)threadIdx.x, 1, 2, 3}, b = {3, 2, 1, (int)threadIdx.x};
+  v16i c[4] = {};
+  float f[kChains];
+  for (int j = 0; j < kChains; ++j) f[j] = 1e-3f * (threadIdx.x + j);
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c[j], 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < N; ++r) f[r % kChains] = __builtin_fmaf(f[r % kChains], 0.999f, -1e-4f);
+    }
+  }
+  int s = 0;
+  for (int j = 0; j < 4; ++j) for (int r = 0; r < 16; ++r) s += c[j][r];
+  float t = 0;
+  for (int j = 0; j < kChains; ++j) t += f[j];
+  if (s == 12345 || t == 1.2345f) out[threadIdx.x] = t + (float)s;
+}
+
 struct MixCtx {
   float* out;
   int iters, blocks, vpm;
@@ -269,6 +294,19 @@ int main(int argc, char** argv) {
     const float ms = time_ms(launch_mix, &c, 3);
     const double ops = (double)blocks * 2 * c.iters * 4 * 65536.0;   // two MFMA waves per block
     printf(", \"mix_i8_with_%d_fma_per_mfma_TOPS\": %.1f", vpm, ops / (ms * 1e-3) / 1e12);
+  }
+  {
+    // same-wave mix, in SIMD clocks per step at 2.4 GHz (one step of one wave;
+    // 8 waves per SIMD share the SIMD)
+    const double steps = (double)blocks * 4 / (cus * 4) * 2000 * 4;   // per SIMD
+    void (*ks[4])(float*, int) = {k_mix_same<0>, k_mix_same<4>, k_mix_same<8>, k_mix_same<16>};
+    const int ns[4] = {0, 4, 8, 16};
+    for (int q = 0; q < 4; ++q) {
+      RateCtx c{ks[q], out, 2000, blocks};
+      const float ms = time_ms(launch_rate, &c, 3);
+      printf(", \"same_wave_i8_mfma_plus_%d_fma_clocks_per_step\": %.1f", ns[q],
+             ms * 1e-3 * 2.4e9 / steps);
+    }
   }
   printf("}\n");
   CK(hipFree(out));
