@@ -130,9 +130,9 @@ typedef enum rotattn_layout {
  *          PACKED: [B*H][NB][D][64]: row d holds the 128 keys of the block
  *          packed along keys as above (byte i of group g = keys 8g+i, 8g+4+i).
  *          FP8: [B*H][NB][D][128]: row d holds the block's 128 keys as E4M3
- *          codes, each 64-key half in the operand order of the P.V product:
- *          byte 32h+j (h in {0,1}, j < 32) is key 8(j%16/4) + 4h + j%4, plus
- *          32 when j >= 16.
+ *          codes, each 64-key half in the operand order of the P.V product
+ *          (P as FP6): byte 32h+j (h in {0,1}, j < 32) is key
+ *          32h + 8(j%16/4) + 4(j/16) + j%4.
  *  rot64:  library scratch, 3*64*64 doubles: the rotation in fp64, refilled
  *          by every rotattn_prepare_qkv call.
  *  q_scale_l2, k_scale, v_scale: [B*H][NB] fp32 block scales (amax/7).

@@ -41,7 +41,7 @@ def fp8_bytes(codes: np.ndarray) -> np.ndarray:
 def fp8_vt_blocks(codes: np.ndarray, N_pad: int) -> np.ndarray:
     """V codes [N, D] -> [NB, D, 128] FP8 bytes: per 128-token block, transposed,
     each 64-key half in the P.V operand order (byte 32h + j holds key
-    32(j/16) + 8((j%16)/4) + 4h + j%4)."""
+    32h + 8((j%16)/4) + 4(j/16) + j%4)."""
     N, D = codes.shape
     full = np.zeros((N_pad, D), np.int8)
     full[:N] = codes
@@ -49,7 +49,7 @@ def fp8_vt_blocks(codes: np.ndarray, N_pad: int) -> np.ndarray:
     for c in range(2):
         for h in range(2):
             for j in range(32):
-                perm[64 * c + 32 * h + j] = 64 * c + 32 * (j // 16) + 8 * ((j % 16) // 4) + 4 * h + j % 4
+                perm[64 * c + 32 * h + j] = 64 * c + 32 * h + 8 * ((j % 16) // 4) + 4 * (j // 16) + j % 4
     assert sorted(perm) == list(range(128))
     out = []
     for b in range(N_pad // 128):

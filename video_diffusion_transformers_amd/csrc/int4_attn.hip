@@ -17,10 +17,13 @@
 //     O^T  = 2^(m-m') O^T + v_scale_t * (V_t^T P^T)      (exact integers V.P)
 //   O = O / l  -> fp16.
 // Two implementations with the same integers:
-//  * Int4F8Kernel (production, FP8 layout): codes are the FP8 E4M3 bytes of
-//    the integers, S^T and V^T P^T run on v_mfma_scale_f32_32x32x64_f8f6f4,
-//    whose fp32 accumulators hold the integer sums exactly; O is kept in units
-//    of the current V block scale.
+//  * Int4F8Kernel (production, FP8 layout): Q/K/V codes are the FP8 E4M3
+//    bytes of the integers and S^T = K Q^T runs on the 32x32x64 f8f6f4 MFMA,
+//    whose fp32 accumulators hold the integer sums exactly.  The P codes enter
+//    V^T P^T as FP6 E2M3 values code/2 (every half-integer 0..7.5 is exact in
+//    E2M3), converted 32 at a time; the FP8 x FP6 product runs at the FP8
+//    rate and its fp32 result is PV/2 exactly.  O is kept in units of the
+//    current V block scale.
 //  * Int4Kernel (PACKED layout): two codes per byte, unpacked to 16*code in
 //    int8 lanes for v_mfma_i32_32x32x32_i8 (the int32 result is 256*I).
 // Computing S^T (keys as MFMA rows) leaves every lane holding one query's
@@ -39,6 +42,8 @@
 // points run the same device functions over every float32 score and over
 // random integer scores.
 #include <math.h>
+
+#include <type_traits>
 
 #include "rotattn_internal.h"
 
@@ -95,12 +100,14 @@ __device__ __forceinline__ CodeCtx make_ctx(float ct, float mnew, float log2_15,
   return c;
 }
 
-// y ~ 15 * 2^x of 16 scores (f = I / iscale exactly; a masked key arrives as
+// y ~ 15 * 2^x of NS scores (f = I / iscale exactly; a masked key arrives as
 // -inf and gives y = 0), the argument taken as make_ctx decided for the wave.
+// EA (exact argument) is that decision at compile time: the fp8 kernel takes
+// it once per tile and runs one of two copies of its fast path.
 template <int NS>
-__device__ __forceinline__ void exp_scores(const float (&f)[NS], const CodeCtx& cx,
-                                           float (&y)[NS]) {
-  if (__builtin_expect(!cx.exact_arg, 1)) {
+__device__ __forceinline__ void exp_scores_ea(const float (&f)[NS], const CodeCtx& cx,
+                                              float (&y)[NS], bool ea) {
+  if (!ea) {
 #pragma unroll
     for (int r = 0; r < NS; ++r) y[r] = __builtin_amdgcn_exp2f(fmaf(f[r], cx.cq, cx.m15n));
   } else {
@@ -109,6 +116,15 @@ __device__ __forceinline__ void exp_scores(const float (&f)[NS], const CodeCtx& 
     for (int r = 0; r < NS; ++r)
       y[r] = __builtin_amdgcn_exp2f((f[r] * cx.iscale * ctc - cx.mnew) + cx.l2_15);
   }
+}
+
+template <int NS>
+__device__ __forceinline__ void exp_scores(const float (&f)[NS], const CodeCtx& cx,
+                                           float (&y)[NS]) {
+  if (__builtin_expect(!cx.exact_arg, 1))
+    exp_scores_ea<NS>(f, cx, y, false);
+  else
+    exp_scores_ea<NS>(f, cx, y, true);
 }
 
 // Exact P code of one score (float f = I / iscale exactly).
@@ -189,68 +205,101 @@ __device__ __forceinline__ void stage_tau(const TauSrc& tau, float* t_lds) {
 // (-0 and +0 included).
 __device__ __forceinline__ int signbit01(float v) { return (int)(__float_as_uint(v) >> 31); }
 
-// The P code of the fp8 kernel for one lane's 16 scores of a 32-key group
-// (exact float I), as E4M3 bytes (byte r = code of score r; exact for the
-// integers 0..15).  rr receives the codes as floats; lsum accumulates the
-// unquantized 15*2^x.
+// Fast P codes of one lane's 16 scores of a 32-key group (exact float I), as
+// floats in rr (exact integers 0..15); lsum accumulates the unquantized
+// 15*2^x (CS: the codes instead, the normalizer of the code-sum variant) and
+// g the largest |y - rne(y)|.
 //
 // y = v_exp_f32(t), t = fma(I, c_t, log2(15) - m'), is within delta of
-// 15*2^x.  code = rne(y) unless some |y - rne(y)| exceeds 1/2 - delta in the
-// wave; then every score of the group is fixed exactly: the true value lies
-// within delta of y, so the code is j - 1 or j for the half-integer boundary
-// j - 1/2 nearest y (j = rne(y) + [y > rne(y)]), and it is j iff x >= tau_j
-// with x = fl(fl(I c_t) - m') -- one comparison against the staged table.
-// Masked keys (last tile) arrive as I = -inf: t = -inf, y = 0, code 0 on both
-// paths (the exact one sees x = -inf or NaN against tau_0 = -inf with j = 0).
-//
-// CS adds the codes to lsum instead of 15*2^x: the normalizer of the
-// code-sum variant, l = sum of the quantized P.
-template <bool CS = false>
-__device__ __forceinline__ v4i pcode16_f8(const float (&f)[16], const CodeCtx& cx,
-                                          const float* tau_lds, float& lsum,
-                                          float (&rr)[16]) {
-  float y[16];
-  exp_scores<16>(f, cx, y);
-  if (!CS) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) lsum += y[r];
-  }
-  float g = 0.0f;
+// 15*2^x, so rr = rne(y) is the exact code unless y lies within delta of a
+// half-integer, i.e. unless g > 1/2 - delta; the caller checks g once for a
+// whole tile and then fixes every code with exact_codes16.  Masked keys (last
+// tile) arrive as I = -inf: t = -inf, y = 0, code 0.
+template <bool CS = false, int EA = -1>
+__device__ __forceinline__ void fast_codes16(const float (&f)[16], const CodeCtx& cx, float& lsum,
+                                             float& g, float (&rr)[16]) {
+  float y[16], d[16];
+  if (EA < 0)
+    exp_scores<16>(f, cx, y);
+  else
+    exp_scores_ea<16>(f, cx, y, EA != 0);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
+    if (!CS) lsum += y[r];
     rr[r] = __builtin_rintf(y[r]);
-    g = fmaxf(g, fabsf(y[r] - rr[r]));
+    d[r] = y[r] - rr[r];
+    if (CS) lsum += rr[r];
   }
-  // rare (a score within delta of a rounding boundary somewhere in the
-  // wave): laid out away from the common path
-  if (__builtin_expect(wave_any(g > 0.5f - cx.delta), 0)) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      int j = (int)rr[r] + signbit01(rr[r] - y[r]);          // rne(y) + [y > rne(y)]
-      j = j < 0 ? 0 : (j > kTauTable - 1 ? kTauTable - 1 : j);
-      const float x = f[r] * cx.iscale * cx.ct - cx.mnew;   // fl(fl(I c_t) - m')
-      const int code = j - signbit01(x - tau_lds[j]);       // j - 1 + [x >= tau_j]
-      rr[r] = (float)(code < 0 ? 0 : code);
-    }
-  }
-  if (CS) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) lsum += rr[r];
-  }
-  uint32_t pk[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    // the untouched half of the first conversion is overwritten by the second
-    const uint32_t lo =
-        __builtin_amdgcn_cvt_pk_fp8_f32(rr[4 * i], rr[4 * i + 1], __float_as_uint(y[4 * i]), false);
-    pk[i] = __builtin_amdgcn_cvt_pk_fp8_f32(rr[4 * i + 2], rr[4 * i + 3], lo, true);
-  }
-  return v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+  // max |d| as a tree of v_max3 with |.| modifiers (depth 3) instead of one
+  // chain of eight
+  const float g0 = vmax3_abs(d[0], d[1], d[2]), g1 = vmax3_abs(d[3], d[4], d[5]);
+  const float g2 = vmax3_abs(d[6], d[7], d[8]), g3 = vmax3_abs(d[9], d[10], d[11]);
+  const float g4 = vmax3_abs(d[12], d[13], d[14]);
+  g = vmax3(g, vmax3(g0, g1, g2), vmax3_abs(g3, g4, d[15]));
 }
 
+// Exact P codes from the fast ones.  |y - 15*2^x| < delta < 1/2, so the exact
+// code is rr - 1, rr or rr + 1: it is rr - 1 iff x < tau_rr and rr + 1 iff
+// x >= tau_{rr+1}, with x = fl(fl(I c_t) - m') and the staged table (tau_0 =
+// -inf, tau_16 = +inf).  Masked keys give x = -inf (or NaN for c_t = 0), which
+// no comparison accepts: code 0.
+__device__ __forceinline__ void exact_codes16(const float (&f)[16], const CodeCtx& cx,
+                                              const float* tau_lds, float (&rr)[16]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    int c0 = (int)rr[r];
+    c0 = c0 < 0 ? 0 : (c0 > kTauTable - 2 ? kTauTable - 2 : c0);
+    const float x = f[r] * cx.iscale * cx.ct - cx.mnew;   // fl(fl(I c_t) - m')
+    const int code = c0 - (x < tau_lds[c0] ? 1 : 0) + (x >= tau_lds[c0 + 1] ? 1 : 0);
+    rr[r] = (float)code;
+  }
+}
+
+// The P codes of the fp8 kernel for 16 scores in one piece (fast codes, then
+// the exact fix when the group's own guard trips): the self-test entry points
+// run this on arbitrary scores.
+template <bool CS = false, int EA = -1>
+__device__ __forceinline__ void pcode16_f8(const float (&f)[16], const CodeCtx& cx,
+                                           const float* tau_lds, float& lsum, float (&rr)[16]) {
+  float g = 0.0f;
+  fast_codes16<CS, EA>(f, cx, lsum, g, rr);
+  // rare: laid out away from the common path
+  if (__builtin_expect(wave_any(g > 0.5f - cx.delta), 0)) exact_codes16(f, cx, tau_lds, rr);
+}
+
+// The P^T operand of one 64-key chunk as FP6 E2M3: the 32 codes a lane holds
+// for the chunk (a: its 16 keys of the first 32-key subtile, b: of the
+// second), each as code/2.  v_cvt_scalef32_2xpk16_fp6_f32 packs src0[i] into
+// 6-bit field 2i and src1[i] into field 2i + 1 (value / scale, scale 2), so
+// field j < 16 holds a[j] and field 16 + j holds b[j].  The MFMA reads field j
+// of a lane in half h as the key that byte 16h + j (j < 16) of the A operand's
+// half 0 holds, and field 16 + j as byte 16h + j of half 1; the prologue's V^T
+// order matches that.  The output must not share registers with the inputs
+// (the conversion writes its result before it has read all of its sources),
+// hence the early-clobber operand.
+__device__ __forceinline__ v8i pack_p_fp6(const float (&a)[16], const float (&b)[16]) {
+  v16f x, y;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[i] = a[2 * i];
+    y[i] = a[2 * i + 1];
+    x[8 + i] = b[2 * i];
+    y[8 + i] = b[2 * i + 1];
+  }
+  v6i r;
+  asm("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, 2.0" : "=&v"(r) : "v"(x), "v"(y));
+  return v8i{r[0], r[1], r[2], r[3], r[4], r[5], 0, 0};
+}
+
+// S^T tile MFMA: K (FP8) x Q (FP8).
 __device__ __forceinline__ v16f mfma_f8(const v8i& a, const v8i& b, const v16f& c) {
   // format 0/0: both operands FP8 E4M3; zero scales select the unscaled MFMA
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// V^T P^T MFMA: A FP8 E4M3 (format 0), B FP6 E2M3 (format 2, six dwords read).
+__device__ __forceinline__ v16f mfma_f8_f6(const v8i& a, const v8i& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 2, 0, 0, 0, 0);
 }
 
 template <int D, bool DBG>
@@ -511,12 +560,15 @@ hipError_t launch_int4(int D, int BH, const Int4Args& a, const Int4Debug* dbg, h
 // The INT4 attention on the FP8-lane layout (codes as E4M3 bytes):
 //   S^T  = K_t Q^T on v_mfma_f32_32x32x64_f8f6f4: the fp32 result is I exactly
 //          (integer products and partial sums below 2^24)
-//   O^T  accumulates V_t^T P^T straight into fp32 on the same MFMA, kept in
-//        units of the current V block scale u: O <- beta O + V^T P^T with
-//        beta = 2^(m-m') u_prev / u.  The final O is O * u / l.
+//   O^T  accumulates V_t^T (P/2)^T straight into fp32 on the same MFMA (V^T
+//        FP8, P as FP6 E2M3 code/2), kept in units of the current V block
+//        scale u: O <- beta O + V^T (P/2)^T with beta = 2^(m-m') u_prev / u.
+//        The final O is 2 O u / l.
 // No unpacking (the prologue stores operand-ready bytes) and no int->float
 // conversions; per score the VALU work is the fused argument, exp2, the l
-// sum and, for groups with a nonzero code, rndne + the guard + the packing.
+// sum, rndne and the guard, plus 1/32 of a packing instruction (32 codes to
+// FP6 in one v_cvt_scalef32_2xpk16_fp6_f32: ~2.1 SIMD clocks per code
+// against ~4.8 for the two-at-a-time FP8 conversion).
 // One work-group = 4 waves = one 128-query block of one head, 32 queries per
 // wave; two work-groups per CU, so that on each SIMD one wave's softmax (VALU)
 // overlaps the other's MFMAs, which run at raised wave priority.  Per tile:
@@ -579,7 +631,7 @@ struct Int4F8Kernel {
     }
   }
 
-  // O^T += V_t^T P^T
+  // O^T += V_t^T (P/2)^T  (P as FP6 code/2: the product is PV/2 exactly)
   __device__ __forceinline__ static void pv(const Int4Debug& dbg, int t, const uint8_t* sv,
                                             const v8i (&P)[2], v16f (&O)[DB]) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -593,18 +645,18 @@ struct Int4F8Kernel {
         v16f pvt = v16f{0.0f};
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          pvt = mfma_f8(ld32s(sv + row * kBlock, 4 * c + 2 * hh, vswz(row)), P[c], pvt);
+          pvt = mfma_f8_f6(ld32s(sv + row * kBlock, 4 * c + 2 * hh, vswz(row)), P[c], pvt);
         const int q = 32 * w + col;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int d = 32 * db + 8 * (r >> 2) + 4 * hh + (r & 3);
-          dbg.pv_int[((size_t)t * kBlock + q) * D + d] = (int32_t)pvt[r];
+          dbg.pv_int[((size_t)t * kBlock + q) * D + d] = (int32_t)(2.0f * pvt[r]);
           O[db][r] += pvt[r];
         }
       } else {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          O[db] = mfma_f8(ld32x(sv + 32 * db * kBlock, xv, c), P[c], O[db]);
+          O[db] = mfma_f8_f6(ld32x(sv + 32 * db * kBlock, xv, c), P[c], O[db]);
       }
     }
   }
@@ -625,7 +677,8 @@ struct Int4F8Kernel {
   // Softmax of key tile t (nv valid keys): running max, rescale of O, P codes,
   // row sum.
   __device__ __forceinline__ static void softmax(const Int4Args& a, const Int4Debug& dbg,
-                                                 const float* tau_lds, int bh, int t, int nv,
+                                                 const float* tau_lds, const uint8_t* sk,
+                                                 const v8i (&qf)[KS], int bh, int t, int nv,
                                                  v16f (&S)[4], float qs, float& m, float& l,
                                                  float& u, v16f (&O)[DB], v8i (&P)[2]) {
     const int lane = threadIdx.x & 63, wl = threadIdx.x >> 6;
@@ -634,18 +687,17 @@ struct Int4F8Kernel {
 
     // row max as plain v_max3 chains: the scores are exact integers or -inf,
     // never NaN, so the quieting that fmaxf needs on MFMA results is dropped
-    float smx[4], rest[4];
+    // (trees: depth 3 per subtile instead of chains of seven)
+    float smx[4];
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
-      smx[sub] = vmax3(S[sub][0], S[sub][1], S[sub][2]);
-#pragma unroll
-      for (int r = 3; r < 15; r += 2) smx[sub] = vmax3(smx[sub], S[sub][r], S[sub][r + 1]);
-      rest[sub] = S[sub][15];
+      const v16f& x = S[sub];
+      const float a0 = vmax3(x[0], x[1], x[2]), a1 = vmax3(x[3], x[4], x[5]);
+      const float a2 = vmax3(x[6], x[7], x[8]), a3 = vmax3(x[9], x[10], x[11]);
+      const float a4 = vmax3(x[12], x[13], x[14]);
+      smx[sub] = vmax3(vmax3(a0, a1, a2), a3, vmax3(a4, x[15], x[15]));
     }
-    float mx = vmax3(smx[0], smx[1], rest[0]);
-    mx = vmax3(mx, smx[2], rest[1]);
-    mx = vmax3(mx, smx[3], rest[2]);
-    mx = vmax2(mx, rest[3]);
+    float mx = vmax2(vmax3(smx[0], smx[1], smx[2]), smx[3]);
     mx = vmax2(mx, other_half(mx));
 
     // the block scales are read through the scalar unit (uniform address):
@@ -667,19 +719,29 @@ struct Int4F8Kernel {
       for (int r = 0; r < 16; ++r) O[db][r] *= beta;
     const CodeCtx cx = make_ctx(ct, mnew, a.log2_15, 1.0f);
 
-    float ls = -0.0f;   // -0 + y == y for every y: no add of a zero start
+    // P codes per 32-key subtile, each with its own (rarely taken) exact fix;
+    // the exponent-argument form is decided once per tile.  One partial sum
+    // per subtile: four independent add chains (-0 + y == y for every y: no
+    // add of a zero start)
+    float lsp[4] = {-0.0f, -0.0f, -0.0f, -0.0f};
     float rr[4][16];
+    auto codes = [&](auto ea) {
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-      float f[16];
+      for (int sub = 0; sub < 4; ++sub) {
+        float f[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) f[r] = S[sub][r];
-      const v4i pk = pcode16_f8<CS>(f, cx, tau_lds, ls, rr[sub]);
-      // 64-key chunk c = sub/2 holds subtile 2c in bytes 0-15, 2c+1 in 16-31
-#pragma unroll
-      for (int i = 0; i < 4; ++i) P[sub >> 1][4 * (sub & 1) + i] = pk[i];
-    }
-    l = fmaf(l, alpha, ls);
+        for (int r = 0; r < 16; ++r) f[r] = S[sub][r];
+        pcode16_f8<CS, decltype(ea)::value>(f, cx, tau_lds, lsp[sub], rr[sub]);
+      }
+    };
+    if (__builtin_expect(!cx.exact_arg, 1))
+      codes(std::integral_constant<int, 0>{});
+    else
+      codes(std::integral_constant<int, 1>{});
+    // 64-key chunk c = subtiles 2c and 2c+1
+    P[0] = pack_p_fp6(rr[0], rr[1]);
+    P[1] = pack_p_fp6(rr[2], rr[3]);
+    l = fmaf(l, alpha, (lsp[0] + lsp[1]) + (lsp[2] + lsp[3]));
 
     if (DBG) {
       const int q = 32 * wl + col;
@@ -779,7 +841,7 @@ struct Int4F8Kernel {
         asm volatile("" : "+v"(nv));
         mask_tail(S, nv);
       }
-      softmax(a, dbg, tau_lds, bh, t, nv, S, qs, m, l, u, O, P);
+      softmax(a, dbg, tau_lds, sk[buf], qf, bh, t, nv, S, qs, m, l, u, O, P);
       // tile t+1 -> the other buffers, last read in tile t-1 (before the barrier)
       if (t + 1 < NT) gload(t + 1, buf ^ 1);
       __builtin_amdgcn_s_setprio(1);
@@ -797,7 +859,7 @@ struct Int4F8Kernel {
       dbg.l_final[32 * w + col] = l * (1.0f / 15.0f);
     }
     if (query < a.N) {
-      const float il = u / l;
+      const float il = 2.0f * u / l;   // O accumulated PV/2
       uint16_t* orow = a.o + a.os.head_offset(bh, a.H) + (int64_t)query * a.os.token;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -861,7 +923,7 @@ __device__ __forceinline__ v4i codes_of(const float (&I)[16], float c, float m, 
   if (F8) {
     const CodeCtx cx = make_ctx(c, m, a.log2_15, 1.0f);
     float rr[16], lsum = 0.0f;
-    pcode16_f8(f, cx, tau_lds, lsum, rr);
+    pcode16_f8(f, cx, tau_lds, lsum, rr);   // codes as exact floats
     uint32_t pk[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -26,6 +26,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 
 __global__ __launch_bounds__(256) void k_copy(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                size_t n) {
@@ -202,6 +203,158 @@ __global__ __launch_bounds__(256) void k_mix_same(float* out, int iters) {
   if (s == 12345 || t == 1.2345f) out[threadIdx.x] = t + (float)s;
 }
 
+// v_exp_f32 and independent vector work in the same wave: per step one
+// exponential (eight chains) and N v_fma_f32 on eight other chains.  Clocks per
+// step against the exponential alone and N FMAs alone show whether the
+// exponential's issue cost overlaps other VALU work.
+template <int N>
+__global__ __launch_bounds__(256) void k_exp_mix(float* out, int iters) {
+  float e[kChains], f[kChains];
+  for (int j = 0; j < kChains; ++j) {
+    e[j] = -1e-3f * (threadIdx.x + j);
+    f[j] = 1e-3f * (threadIdx.x + j);
+  }
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < kChains; ++j) {
+      e[j] = __builtin_amdgcn_exp2f(e[j]);
+#pragma unroll
+      for (int r = 0; r < N; ++r) {
+        const int c = (j * N + r) % kChains;
+        f[c] = __builtin_fmaf(f[c], 0.999f, -1e-4f);
+      }
+    }
+  }
+  float s = 0;
+  for (int j = 0; j < kChains; ++j) s += e[j] + f[j];
+  if (s == 12345.678f) out[threadIdx.x] = s;
+}
+
+// v_exp_f32 in one wave and v_fma_f32 in another: even waves of a
+// work-group run exponentials (eight chains), odd waves FMAs; time against
+// each kind alone shows whether the exponentials of one wave overlap the
+// vector work of another on the same SIMD.
+__global__ __launch_bounds__(256) void k_exp_fma_waves(float* out, int iters, int mode) {
+  const int wave = threadIdx.x >> 6;
+  // mode 0: both kinds; 1: exponential waves only; 2: FMA waves only
+  const bool run_exp = (wave & 1) == 0 && mode != 2;
+  const bool run_fma = (wave & 1) == 1 && mode != 1;
+  float a[kChains];
+  for (int j = 0; j < kChains; ++j) a[j] = -1e-3f * (threadIdx.x + j);
+  if (run_exp) {
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int j = 0; j < kChains; ++j) a[j] = __builtin_amdgcn_exp2f(a[j]);
+    }
+  } else if (run_fma) {
+    for (int i = 0; i < iters * 3; ++i) {
+#pragma unroll
+      for (int j = 0; j < kChains; ++j) a[j] = __builtin_fmaf(a[j], 0.999f, -1e-4f);
+    }
+  }
+  float s = 0;
+  for (int j = 0; j < kChains; ++j) s += a[j];
+  if (s == 12345.678f) out[threadIdx.x] = s;
+}
+
+// FP8 MFMA waves beside vector waves of one instruction kind (OP 0: v_fma_f32,
+// 1: v_exp_f32, 2: v_max3_f32, 3: v_mul_f32): even waves of a work-group run
+// 32x32x64 FP8 MFMAs (four accumulators), odd waves VPM vector instructions
+// per MFMA.  mode 0: both, 1: MFMA waves only, 2: vector waves only.
+template <int OP>
+__global__ __launch_bounds__(256) void k_mix_f8(float* out, int iters, int vpm, int mode) {
+  const int wave = threadIdx.x >> 6;
+  if ((wave & 1) == 0) {
+    if (mode == 2) return;
+    v8i a = {(int)threadIdx.x, 1, 2, 3, 4, 5, 6, 7}, b = {7, 6, 5, 4, 3, 2, 1, (int)threadIdx.x};
+    v16f c[4] = {};
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        c[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c[j], 0, 0, 0, 0, 0, 0);
+    }
+    float s = 0;
+    for (int j = 0; j < 4; ++j) for (int r = 0; r < 16; ++r) s += c[j][r];
+    if (s == 12345.f) out[threadIdx.x] = s;
+  } else {
+    if (mode == 1) return;
+    float a[kChains];
+    for (int j = 0; j < kChains; ++j) a[j] = -1e-3f * (threadIdx.x + j);
+    const int n = iters * vpm * 4 / kChains;
+    for (int i = 0; i < n; ++i) {
+#pragma unroll
+      for (int j = 0; j < kChains; ++j) {
+        if (OP == 0) a[j] = __builtin_fmaf(a[j], 0.999f, -1e-4f);
+        if (OP == 1) a[j] = __builtin_amdgcn_exp2f(a[j]);
+        if (OP == 2) asm volatile("v_max3_f32 %0, %0, %1, %2" : "+v"(a[j]) : "v"(a[(j + 1) % kChains]), "v"(a[(j + 2) % kChains]));
+        if (OP == 3) a[j] = a[j] * 0.999f;
+      }
+    }
+    float s = 0;
+    for (int j = 0; j < kChains; ++j) s += a[j];
+    if (s == 12345.678f) out[threadIdx.x] = s;
+  }
+}
+
+// v_rndne_f32 (opaque, so that rint(rint(x)) is not folded)
+RATE_KERNEL(k_rndne, asm volatile("v_rndne_f32 %0, %0" : "+v"(a[j])))
+
+// v_cvt_pk_fp8_f32: two floats -> two FP8 bytes (eight independent outputs)
+__global__ __launch_bounds__(256) void k_cvt_fp8(float* out, int iters) {
+  float a[kChains];
+  uint32_t acc[kChains];
+  for (int j = 0; j < kChains; ++j) {
+    a[j] = 1e-3f * (threadIdx.x + j);
+    acc[j] = 0;
+  }
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < kChains; ++j)
+      acc[j] = __builtin_amdgcn_cvt_pk_fp8_f32(a[j], a[(j + 1) % kChains], acc[j], false);
+  }
+  uint32_t s = 0;
+  for (int j = 0; j < kChains; ++j) s ^= acc[j];
+  if (s == 0x12345678u) out[threadIdx.x] = (float)s;
+}
+
+// v_cvt_scalef32_2xpk16_fp6_f32: 32 floats -> 32 FP6 (E2M3) values in six
+// dwords per instruction; four independent outputs per step
+typedef int v6i __attribute__((ext_vector_type(6)));
+__global__ __launch_bounds__(256) void k_cvt_fp6(float* out, int iters) {
+  v16f x, y;
+  for (int j = 0; j < 16; ++j) {
+    x[j] = 0.5f * ((threadIdx.x + j) & 15);
+    y[j] = 0.25f * ((threadIdx.x + 3 * j) & 15);
+  }
+  uint32_t s = 0;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // opaque inputs: every conversion is issued (none is merged with another)
+      asm volatile("" : "+v"(x), "+v"(y));
+      const v6i r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(x, y, 1.0f);
+      s ^= (uint32_t)r[j];
+    }
+  }
+  if (s == 0x12345678u) out[threadIdx.x] = (float)s;
+}
+
+// 32x32x64 f8f6f4 MFMA with operand formats FA (A) and FB (B): 0 = FP8 E4M3,
+// 2 = FP6 E2M3 (six of the eight operand dwords are read)
+template <int FA, int FB>
+__global__ __launch_bounds__(256) void k_mfma_f8f6f4(float* out, int iters) {
+  v8i a = {(int)threadIdx.x, 1, 2, 3, 4, 5, 6, 7}, b = {7, 6, 5, 4, 3, 2, 1, (int)threadIdx.x};
+  v16f c[4] = {};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      c[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c[j], FA, FB, 0, 0, 0, 0);
+  }
+  float s = 0;
+  for (int j = 0; j < 4; ++j) for (int r = 0; r < 16; ++r) s += c[j][r];
+  if (s == 12345.f) out[threadIdx.x] = s;
+}
+
 struct MixCtx {
   float* out;
   int iters, blocks, vpm;
@@ -258,7 +411,10 @@ int main(int argc, char** argv) {
   } vk[] = {{"fma", k_fma, kChains}, {"exp", k_exp, kChains},
             {"add_fract_steps", k_fract, kChains},        // v_add + v_fract per step
             {"cvt_cvt_add_steps", k_cvt, kChains},        // f32->i32, i32->f32, v_add per step
-            {"cvt_pk_u8", k_cvtpk, kChains}};
+            {"cvt_pk_u8", k_cvtpk, kChains},
+            {"rndne", k_rndne, kChains},
+            {"cvt_pk_fp8", k_cvt_fp8, kChains},              // instructions (two values each)
+            {"cvt_2xpk16_fp6", k_cvt_fp6, 4}};               // instructions (32 values each)
   for (auto& v : vk) {
     RateCtx c{v.k, out, 4000, blocks};
     const float ms = time_ms(launch_rate, &c, 3);
@@ -305,6 +461,72 @@ int main(int argc, char** argv) {
       RateCtx c{ks[q], out, 2000, blocks};
       const float ms = time_ms(launch_rate, &c, 3);
       printf(", \"same_wave_i8_mfma_plus_%d_fma_clocks_per_step\": %.1f", ns[q],
+             ms * 1e-3 * 2.4e9 / steps);
+    }
+  }
+  {
+    const double steps_per_mfma = 65536.0 * 2;   // ops of one 32x32x64 MFMA
+    void (*ks[3])(float*, int) = {k_mfma_f8f6f4<0, 0>, k_mfma_f8f6f4<0, 2>, k_mfma_f8f6f4<2, 2>};
+    const char* nm[3] = {"fp8_fp8", "fp8_fp6", "fp6_fp6"};
+    for (int q = 0; q < 3; ++q) {
+      RateCtx c{ks[q], out, 1000, blocks};
+      const float ms = time_ms(launch_rate, &c, 3);
+      const double ops = (double)blocks * 4 * c.iters * 4 * steps_per_mfma;
+      printf(", \"mfma_%s_32x32x64_TOPS\": %.1f", nm[q], ops / (ms * 1e-3) / 1e12);
+    }
+  }
+  {
+    // FP8 MFMA waves beside vector waves: ms for both, MFMA only, vector only
+    struct F8Ctx {
+      void (*k)(float*, int, int, int);
+      float* out;
+      int iters, blocks, vpm, mode;
+    };
+    auto launch_f8 = [](void* p) {
+      F8Ctx* c = (F8Ctx*)p;
+      hipLaunchKernelGGL(c->k, dim3(c->blocks), dim3(256), 0, 0, c->out, c->iters, c->vpm, c->mode);
+    };
+    void (*ks[4])(float*, int, int, int) = {k_mix_f8<0>, k_mix_f8<1>, k_mix_f8<2>, k_mix_f8<3>};
+    const char* on[4] = {"fma", "exp", "max3", "mul"};
+    for (int op = 0; op < 4; ++op)
+      for (int vpm : {8, 16}) {
+        float t[3];
+        for (int mode = 0; mode < 3; ++mode) {
+          F8Ctx c{ks[op], out, 1000, blocks, vpm, mode};
+          t[mode] = time_ms(launch_f8, &c, 3);
+        }
+        printf(", \"f8mfma_with_%d_%s_ms_both_mfma_valu\": [%.4f, %.4f, %.4f]", vpm, on[op], t[0],
+               t[1], t[2]);
+      }
+  }
+  {
+    // exponential waves and FMA waves side by side (3 FMAs per exponential in
+    // the FMA waves), ms for both kinds and for each alone
+    struct ModeCtx {
+      float* out;
+      int iters, blocks, mode;
+    };
+    auto launch_mode = [](void* p) {
+      ModeCtx* c = (ModeCtx*)p;
+      hipLaunchKernelGGL(k_exp_fma_waves, dim3(c->blocks), dim3(256), 0, 0, c->out, c->iters,
+                         c->mode);
+    };
+    const char* nm[3] = {"both", "exp_only", "fma_only"};
+    for (int mode = 0; mode < 3; ++mode) {
+      ModeCtx c{out, 2000, blocks, mode};
+      const float ms = time_ms(launch_mode, &c, 3);
+      printf(", \"exp_and_fma_waves_%s_ms\": %.4f", nm[mode], ms);
+    }
+  }
+  {
+    // one v_exp_f32 plus N independent v_fma_f32 per step, SIMD clocks per step
+    const double steps = (double)blocks * 4 / (cus * 4) * 4000 * kChains;   // per SIMD
+    void (*ks[5])(float*, int) = {k_exp_mix<0>, k_exp_mix<1>, k_exp_mix<2>, k_exp_mix<3>,
+                                  k_exp_mix<4>};
+    for (int q = 0; q < 5; ++q) {
+      RateCtx c{ks[q], out, 4000, blocks};
+      const float ms = time_ms(launch_rate, &c, 3);
+      printf(", \"same_wave_exp_plus_%d_fma_clocks_per_step\": %.2f", q,
              ms * 1e-3 * 2.4e9 / steps);
     }
   }

@@ -415,14 +415,15 @@ __device__ __forceinline__ void store_qk_codes_f8(const int8_t* codes, uint8_t* 
 }
 
 // FP8 layout: V code bytes (LDS, [channel][token]) -> V^T block [D][128], each
-// 64-key half in the P.V operand order (byte 32h + j of a half holds key
-// 32(j/16) + 8((j%16)/4) + 4h + j%4).  Dwords move whole: j%4 is the byte.
+// 64-key half in the operand order of the P.V product with P as FP6 (byte
+// 32h + j of a half holds key 32h + 8((j%16)/4) + 4(j/16) + j%4).  Dwords move
+// whole: j%4 is the byte.
 template <int D>
 __device__ __forceinline__ void store_v_codes_f8(const int8_t* codesT, uint8_t* dst) {
   for (int i = threadIdx.x; i < D * 32; i += kThreads) {
     const int d = i / 32, q = i % 32;                 // output dword q of row d
     const int c = q / 16, h = (q / 8) & 1, j = 4 * (q & 7);
-    const int key = 64 * c + 32 * (j / 16) + 8 * ((j % 16) / 4) + 4 * h;
+    const int key = 64 * c + 32 * h + 8 * ((j % 16) / 4) + 4 * (j / 16);
     *(uint32_t*)(dst + (size_t)d * 128 + 4 * q) = *(const uint32_t*)(codesT + d * kCodeStride + key);
   }
 }
