@@ -13,8 +13,10 @@ attention TOPS = 4*B*H*N^2*D / step time.
 Prints one JSON line.  Besides the contract fields it carries the roofline
 of the dominant kernel (the INT4 attention, timed with HIP events on the
 stream it runs on, with the VALU-busy share of the unit that bounds it), the
-per-kernel times, and the CPU oracle timed on a bounded
-sample on this host (cpu_baseline).
+same for the i8-MFMA implementation of that kernel, the per-kernel times, the
+Mixed workload (4 denoising steps, a fixed seeded quarter of the heads in
+FP16, fresh inputs per step), the 480p workload, a synthetic DiT block, and
+the CPU oracle timed on a bounded sample on this host's cores (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -50,7 +52,7 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="time the step only: skip the packed-layout, mixed_fwd and all-FP16 "
                          "side figures (used for counter collection)")
-    ap.add_argument("--mixed-steps", type=int, default=2,
+    ap.add_argument("--mixed-steps", type=int, default=4,
                     help="denoising steps of the mixed workload to time as a side figure (0: skip)")
     return ap.parse_args()
 
@@ -100,6 +102,30 @@ def valu_busy_from_profile(workload: str):
     return None
 
 
+def prologue_bytes(BH: int, N: int, D: int):
+    """Algorithmic HBM bytes of the prologue (per token and head: read Q, K, V
+    fp16, write Q, K, V as INT4 codes, two per byte; block scales are
+    negligible) and the bytes its FP8-lane layout actually writes (one byte per
+    code)."""
+    algorithmic = BH * N * (3 * 2 * D + 3 * D // 2)
+    layout = BH * N * (3 * 2 * D + 3 * D)
+    return algorithmic, layout
+
+
+def time_calls(fn, reps: int) -> float:
+    """Mean ms of fn() over reps calls (HIP events on torch's current stream,
+    the stream the library enqueues on), after one untimed call."""
+    import torch
+    fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -140,7 +166,7 @@ def main():
         R.int4_fwd(shape, prep, o, mask=mask)
         if ev: ev[2].record()
         if n_fb:
-            R.fp16_fwd(shape, prep, o, head_select=mask)
+            R.fp16_fwd_prepared(shape, prep, o, head_select=mask)
         if ev: ev[3].record()
 
     for _ in range(args.warmup):
@@ -171,45 +197,50 @@ def main():
     traffic = traffic_from_profile(args.workload)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_I8_TOPS,
                 "unit": "TOP/s", "frac": round(achieved / PEAK_I8_TOPS, 4), "traffic": traffic,
-                "kernel": "k_int4_attn_f8<128>", "algorithmic_ops_per_launch": int4_ops,
+                "kernel": "k_int4_attn_f8<128>",
+                "operands": "INT4 codes as FP8 E4M3 (Q, K, V), P codes as FP6 E2M3 (code/2); "
+                            "fp32 accumulation exact on these integers; FP8 x FP6 runs at the "
+                            "FP8 rate, whose dense peak equals the i8 one",
+                "algorithmic_ops_per_launch": int4_ops,
                 "limiter": "valu", "limiter_busy": valu_busy_from_profile(args.workload)}
-    # prologue: algorithmic HBM bytes per token per head (read Q,K,V fp16; write
-    # Q,K,V codes one byte each in the FP8-lane layout; block scales are negligible)
-    k1_bytes = BH * N * (3 * 2 * D + 3 * D)
+    k1_ms = float(k1.mean())
+    pro_alg, pro_layout = prologue_bytes(BH, N, D)
     kernels = {
-        "prologue_ms": round(float(k1.mean()), 4),
-        "prologue_hbm_frac": round(k1_bytes / (float(k1.mean()) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "prologue_ms": round(k1_ms, 4),
+        "prologue_hbm_frac": round(pro_alg / (k1_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "prologue_algorithmic_bytes": pro_alg,
+        "prologue_layout_bytes": pro_layout,
+        "prologue_layout_bytes_frac": round(pro_layout / (k1_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "int4_attn_ms": round(k2_ms, 4),
         "int4_attn_ms_min": round(float(k2.min()), 4),
         "int4_attn_i8_peak_frac": round(achieved / PEAK_I8_TOPS, 4),
         "fp16_attn_ms": round(float(k3.mean()), 4),
         "event_step_ms": round(float(tot.mean()), 4),
     }
+    roofline_i8 = None
 
     if not args.no_extras:
-        # the same INT4 attention on the nibble-packed layout (i8 MFMA kernel)
-        # (fallback heads, if any, need the fp16 RoPE'd buffers as well)
+        # the same INT4 attention on the nibble-packed layout: int8 lanes on the
+        # i8 MFMA with int32 accumulation (fallback heads, if any, need the
+        # fp16 RoPE'd buffers as well)
         prep_p = R.PreparedDevice(shape, with_rope=n_fb > 0, layout=R.LAYOUT_PACKED)
         R.prepare_qkv(shape, qd, kd, vd, rr, prep_p, mask)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        R.int4_fwd(shape, prep_p, o, mask=mask)
-        e0.record()
-        for _ in range(3):
-            R.int4_fwd(shape, prep_p, o, mask=mask)
-        e1.record()
-        torch.cuda.synchronize()
-        kernels["int4_attn_packed_i8_ms"] = round(e0.elapsed_time(e1) / 3, 4)
+        i8_ms = time_calls(lambda: R.int4_fwd(shape, prep_p, o, mask=mask), 3)
         del prep_p
+        i8_ach = int4_ops / (i8_ms * 1e-3) / 1e12 if n_int4 else 0.0
+        roofline_i8 = {"bound": "mfma", "achieved": round(i8_ach, 2), "peak": PEAK_I8_TOPS,
+                       "unit": "TOP/s", "frac": round(i8_ach / PEAK_I8_TOPS, 4), "traffic": None,
+                       "kernel": "k_int4_attn<128>",
+                       "operands": "INT4 codes unpacked to int8 lanes, v_mfma_i32_32x32x32_i8 "
+                                   "with int32 accumulation",
+                       "ms": round(i8_ms, 4), "algorithmic_ops_per_launch": int4_ops}
+        kernels["int4_attn_packed_i8_ms"] = round(i8_ms, 4)
+        print(f"[bench] i8-MFMA kernel {i8_ms:.3f} ms", file=sys.stderr, flush=True)
 
         # mixed_fwd (one C call) on the same inputs, as a cross-check of the sequence
         ws = torch.empty(R.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
-        R.mixed_fwd(shape, qd, kd, vd, rr, mask, ws, o)
-        e0.record()
-        for _ in range(3):
-            R.mixed_fwd(shape, qd, kd, vd, rr, mask, ws, o)
-        e1.record()
-        torch.cuda.synchronize()
-        kernels["mixed_fwd_call_ms"] = round(e0.elapsed_time(e1) / 3, 4)
+        kernels["mixed_fwd_call_ms"] = round(
+            time_calls(lambda: R.mixed_fwd(shape, qd, kd, vd, rr, mask, ws, o), 3), 4)
         del ws
 
         # INT4 output of every head, kept for the per-head error report below
@@ -221,15 +252,7 @@ def main():
         # of the full-precision baseline) -- context figure
         all_fb = np.ones(BH, np.uint8)
         R.prepare_qkv(shape, qd, kd, vd, rr, prep, all_fb)
-        e0.record()
-        R.fp16_fwd(shape, prep, o, head_select=all_fb)
-        e1.record()
-        torch.cuda.synchronize()
-        R.fp16_fwd(shape, prep, o, head_select=all_fb)
-        e2 = torch.cuda.Event(enable_timing=True)
-        e2.record()
-        torch.cuda.synchronize()
-        f16_ms = e1.elapsed_time(e2)
+        f16_ms = time_calls(lambda: R.fp16_fwd_prepared(shape, prep, o, head_select=all_fb), 1)
         kernels["fp16_attn_all_heads_ms"] = round(f16_ms, 4)
         kernels["fp16_attn_f16_peak_frac"] = round(ops / (f16_ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4)
         kernels["int4_vs_fp16_kernel_speedup"] = round(f16_ms / k2_ms, 3) if n_int4 == BH else None
@@ -239,16 +262,24 @@ def main():
             reference="FP16 attention kernel, same inputs",
             **fallback.report(fallback.head_rel_error(o_int4, o)))
 
+        # the FP16 attention on caller tensors (staging into a workspace, then
+        # the same kernel): the RoPE'd fp16 Q'/K' of the prologue's buffers
+        # stand in for a caller's, V is the input
+        ws16 = torch.empty(R.fp16_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+        qv = prep.view("q_rope", torch.float16, BH * R.n_blocks(shape) * 128 * D)
+        kv = prep.view("k_rope", torch.float16, BH * R.n_blocks(shape) * 128 * D)
+        qr = qv.view(BH, -1, D)[:, :N].reshape(B, H, N, D).contiguous()
+        kr = kv.view(BH, -1, D)[:, :N].reshape(B, H, N, D).contiguous()
+        o2 = torch.empty_like(o)
+        kernels["fp16_fwd_caller_buffers_ms"] = round(
+            time_calls(lambda: R.fp16_fwd(shape, qr, kr, vd, o2, ws16), 1), 4)
+        del ws16, qr, kr, o2
+
         # the rotation merged into RoPE (seeded pair phases in the tables, no
         # dense rotation): prologue time and the same error report
         rr_m = R.RopeRotDevice(shape, None, phases=synth.mergeable_phases(cfg.split))
-        R.prepare_qkv(shape, qd, kd, vd, rr_m, prep, None)
-        e0.record()
-        for _ in range(3):
-            R.prepare_qkv(shape, qd, kd, vd, rr_m, prep, None)
-        e1.record()
-        torch.cuda.synchronize()
-        kernels["prologue_merged_rotation_ms"] = round(e0.elapsed_time(e1) / 3, 4)
+        kernels["prologue_merged_rotation_ms"] = round(
+            time_calls(lambda: R.prepare_qkv(shape, qd, kd, vd, rr_m, prep, None), 3), 4)
         R.int4_fwd(shape, prep, o_int4, mask=None)
         kernels["int4_merged_rotation_vs_fp16_head_error"] = dict(
             reference="FP16 attention kernel, same inputs",
@@ -265,10 +296,13 @@ def main():
     mixed = None
     if args.mixed_steps and args.workload == "720p":
         mixed = bench_mixed(args.mixed_steps)
+    p480 = None
+    if not args.no_extras and args.workload == "720p":
+        p480 = bench_workload("480p")
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, q, k, v, r32, ops)
+        cpu = cpu_baseline(cfg, ops)
 
     value = ops / (ms_per_step * 1e-3) / 1e12
     line = {
@@ -287,14 +321,17 @@ def main():
         "config": {"workload": f"{cfg.name}: B={B} H={H} grid {'x'.join(map(str, cfg.grid))} "
                                f"N={N} D={D} split {'/'.join(map(str, cfg.split))}, "
                                f"{BH - n_fb} INT4 heads + {n_fb} FP16 heads, seeded synthetic "
-                               f"fp16 Q/K/V (RoPE-partition outlier channels, sparse V token "
-                               f"outliers)",
+                               f"fp16 Q/K/V (per-channel lognormal scales with 4 temporal "
+                               f"outlier channels x10-30, Q and K scaled to a 2.5-nat logit "
+                               f"spread; sparse x15 V token outliers)",
                    "global_batch": B, "seq_len": N, "heads": H, "head_dim": D,
                    "parallelism": "single GPU"},
         "percent_i8_peak_step": round(100 * value / PEAK_I8_TOPS, 2),
         "roofline": roofline,
+        "roofline_i8_mfma_kernel": roofline_i8,
         "kernels": kernels,
         "mixed": mixed,
+        "workload_480p": p480,
         "dit_block": dit,
         "cpu_baseline": cpu,
     }
@@ -345,9 +382,10 @@ def bench_dit_block(cfg, width: int = 5120, reps: int = 2):
 
 
 def bench_mixed(steps: int):
-    """The mixed workload: 720p shape, one rotattn_mixed_fwd per denoising step
-    with fresh inputs and a per-step fallback mask (step 0: every head FP16;
-    later steps: a seeded quarter of the heads FP16).  Side figure."""
+    """The Mixed workload: 720p shape, a seeded mask sending 10 of 40 heads to
+    the FP16 attention, fixed across steps, and one rotattn_mixed_fwd per
+    denoising step with fresh seeded Q/K/V.  Each step is timed as one call
+    (HIP events) after an untimed call on the same inputs."""
     import torch
     from video_diffusion_transformers_amd import rotattn as R
     from video_diffusion_transformers_amd import synth
@@ -355,65 +393,118 @@ def bench_mixed(steps: int):
     shape = R.shape_of(cfg)
     _, r32 = synth.rotation_matrices(cfg.split)
     rr = R.RopeRotDevice(shape, r32)
-    sched = synth.fallback_schedule(cfg, steps, early_fp16_steps=1)[:, 0]
+    mask = synth.fallback_mask(cfg)
     ws = torch.empty(R.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
     o = torch.empty((cfg.B, cfg.H, cfg.N, cfg.D), dtype=torch.float16, device="cuda")
+    prep = R.PreparedDevice(shape, with_rope=True)
+    n_fb = int(mask.sum())
+    n_i4 = cfg.BH - n_fb
     per_step = []
     for s in range(steps):
         q, k, v = synth.all_heads_qkv(cfg, s)
         qd, kd, vd = (torch.from_numpy(x).cuda() for x in (q, k, v))
-        R.mixed_fwd(shape, qd, kd, vd, rr, sched[s], ws, o)      # warm
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        R.mixed_fwd(shape, qd, kd, vd, rr, sched[s], ws, o)
-        e1.record()
-        torch.cuda.synchronize()
-        per_step.append({"step": s, "fp16_heads": int(sched[s].sum()),
-                         "ms": round(e0.elapsed_time(e1), 4)})
+        del q, k, v
+        ms = time_calls(lambda: R.mixed_fwd(shape, qd, kd, vd, rr, mask, ws, o), 1)
+        # the two attention kernels of the step on their own
+        R.prepare_qkv(shape, qd, kd, vd, rr, prep, mask)
+        i4 = time_calls(lambda: R.int4_fwd(shape, prep, o, mask=mask), 1)
+        f16 = time_calls(lambda: R.fp16_fwd_prepared(shape, prep, o, head_select=mask), 1)
+        per_step.append({"step": s, "ms": round(ms, 4), "int4_attn_ms": round(i4, 4),
+                         "fp16_attn_ms": round(f16, 4)})
         del qd, kd, vd
     ms = float(np.mean([p["ms"] for p in per_step]))
-    ops = 4.0 * cfg.B * cfg.H * cfg.N ** 2 * cfg.D
+    i4 = float(np.mean([p["int4_attn_ms"] for p in per_step]))
+    f16 = float(np.mean([p["fp16_attn_ms"] for p in per_step]))
+    unit = 4.0 * cfg.N ** 2 * cfg.D
+    ops = unit * cfg.BH
     print(f"[bench] mixed {steps} step(s): " +
-          ", ".join(f"step {p['step']} ({p['fp16_heads']} FP16 heads) {p['ms']:.3f} ms"
-                    for p in per_step), file=sys.stderr, flush=True)
-    return {"workload": "720p shape, per-step fallback mask (step 0 all heads FP16, then 10 of "
-                        "40 heads FP16, seeded), fresh inputs per step",
-            "steps": steps, "per_step": per_step, "ms_per_step": round(ms, 4),
-            "effective_tops": round(ops / (ms * 1e-3) / 1e12, 2)}
+          ", ".join(f"step {p['step']} {p['ms']:.3f} ms" for p in per_step), file=sys.stderr,
+          flush=True)
+    del prep, ws, o
+    torch.cuda.empty_cache()
+    return {"workload": f"mixed: 720p shape (B=1 H=40 N=75600 D=128), {n_fb} of 40 heads FP16 "
+                        f"(seeded mask, fixed across steps), fresh seeded Q/K/V per step, one "
+                        f"rotattn_mixed_fwd per step",
+            "steps": steps, "fp16_heads": n_fb, "per_step": per_step,
+            "ms_per_step": round(ms, 4), "effective_tops": round(ops / (ms * 1e-3) / 1e12, 2),
+            "int4_attn_ms": round(i4, 4),
+            "int4_attn_i8_peak_frac": round(unit * n_i4 / (i4 * 1e-3) / 1e12 / PEAK_I8_TOPS, 4),
+            "fp16_attn_ms": round(f16, 4),
+            "fp16_attn_f16_peak_frac": round(unit * n_fb / (f16 * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4)}
 
 
-def cpu_baseline(cfg, q, k, v, r32, ops):
-    """The CPU oracle on this host: prologue of one head over all tokens plus
-    INT4 attention of a few query rows of that head, extrapolated to the whole
-    workload in the metric's unit."""
-    import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
-    rows_n = 48
+def bench_workload(name: str, reps: int = 5):
+    """Side figure: one step (prologue + INT4 attention, every head INT4) of
+    another workload, inputs resident in HBM."""
+    import torch
+    from video_diffusion_transformers_amd import rotattn as R
+    from video_diffusion_transformers_amd import synth
+    cfg = synth.CONFIGS[name]
+    shape = R.shape_of(cfg)
+    q, k, v = synth.all_heads_qkv(cfg, 0)
+    qd, kd, vd = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    del q, k, v
+    _, r32 = synth.rotation_matrices(cfg.split)
+    rr = R.RopeRotDevice(shape, r32)
+    prep = R.PreparedDevice(shape, with_rope=False)
+    o = torch.empty((cfg.B, cfg.H, cfg.N, cfg.D), dtype=torch.float16, device="cuda")
+
+    def step():
+        R.prepare_qkv(shape, qd, kd, vd, rr, prep, None)
+        R.int4_fwd(shape, prep, o)
+
+    step_ms = time_calls(step, reps)
+    pro_ms = time_calls(lambda: R.prepare_qkv(shape, qd, kd, vd, rr, prep, None), reps)
+    i4_ms = time_calls(lambda: R.int4_fwd(shape, prep, o), reps)
+    ops = 4.0 * cfg.BH * cfg.N ** 2 * cfg.D
+    pro_alg, _ = prologue_bytes(cfg.BH, cfg.N, cfg.D)
+    del qd, kd, vd, prep, o
+    torch.cuda.empty_cache()
+    print(f"[bench] {name}: step {step_ms:.3f} ms (prologue {pro_ms:.3f}, int4 {i4_ms:.3f})",
+          file=sys.stderr, flush=True)
+    return {"workload": f"{name}: B={cfg.B} H={cfg.H} grid {'x'.join(map(str, cfg.grid))} "
+                        f"N={cfg.N} D={cfg.D}, every head INT4",
+            "ms_per_step": round(step_ms, 4), "effective_tops": round(ops / (step_ms * 1e-3) / 1e12, 2),
+            "int4_attn_ms": round(i4_ms, 4),
+            "int4_attn_i8_peak_frac": round(ops / (i4_ms * 1e-3) / 1e12 / PEAK_I8_TOPS, 4),
+            "prologue_ms": round(pro_ms, 4),
+            "prologue_hbm_frac": round(pro_alg / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
+def cpu_baseline(cfg, ops, heads: int | None = None, rows: int = 256):
+    """The CPU oracle on this host's cores: for `heads` heads of the workload
+    (default: one per core, at most 16), the prologue over all N tokens plus
+    the INT4 attention of `rows` sampled query rows each, one head per worker
+    process (the oracle is single threaded per head).  The measured wall time is scaled by the ratio of the
+    whole workload's work (every head, every query row) to the sample's, both
+    from the workers' own per-head timings."""
+    from oracle import parallel
+    from video_diffusion_transformers_amd import synth
+    visible = parallel.host_cores()
+    if heads is None:
+        heads = min(visible, parallel.MAX_WORKERS, cfg.BH)   # one head per core
+    workers = min(visible, parallel.MAX_WORKERS, heads)
+    bhs = [int(x) for x in np.linspace(0, cfg.BH - 1, heads).round()]
+    jobs = [(bh, synth.sampled_rows(cfg, bh, rows), False) for bh in bhs]
     t0 = time.perf_counter()
-    tabs = O.all_rope_tables(cfg.grid, cfg.split)
-    t_tab = time.perf_counter() - t0
-    qh, kh, vh = q[0, 0], k[0, 0], v[0, 0]
-    t0 = time.perf_counter()
-    prep = O.prepare_head(qh, kh, vh, tabs, r32, cfg.grid, cfg.split)
-    t_pro = time.perf_counter() - t0
-    rows = np.arange(rows_n) * (cfg.N // rows_n)
-    t0 = time.perf_counter()
-    O.int4_attention(prep["q_codes"], prep["q_scale_l2"], prep["k_codes"], prep["k_scale"],
-                     prep["v_codes"], prep["v_scale"], rows)
-    t_att = time.perf_counter() - t0
-    full_s = t_tab + cfg.BH * t_pro + cfg.BH * t_att * cfg.N / rows_n
-    print(f"[bench] cpu oracle: prologue {t_pro:.2f}s/head, attention {t_att:.2f}s/{rows_n} rows "
-          f"-> {full_s / 3600:.1f} h extrapolated", file=sys.stderr, flush=True)
-    return {"value": round(ops / full_s / 1e12, 6), "unit": "TOP/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"head 0 of {cfg.name}: prologue over all {cfg.N} tokens ({t_pro:.2f} s) + "
-                      f"INT4 attention of {rows_n} query rows ({t_att:.2f} s), extrapolated to "
-                      f"{cfg.BH} heads x {cfg.N} rows = {full_s:.0f} s",
-            "measured_s": round(t_tab + t_pro + t_att, 2)}
+    _, secs = parallel.run_heads(cfg, 0, jobs, workers=workers)
+    wall = time.perf_counter() - t0
+    pro = np.array([secs[bh][0] for bh in bhs])
+    att = np.array([secs[bh][1] for bh in bhs])
+    sample_work = float(np.sum(pro + att))
+    full_work = cfg.BH * (float(pro.mean()) + float(att.mean()) * cfg.N / rows)
+    full_wall = wall * full_work / sample_work
+    print(f"[bench] cpu oracle: {heads} heads x ({cfg.N}-token prologue + {rows} query rows) on "
+          f"{workers} workers in {wall:.1f} s -> {full_wall / 3600:.1f} h extrapolated",
+          file=sys.stderr, flush=True)
+    return {"value": round(ops / full_wall / 1e12, 6), "unit": "TOP/s", "cores": int(workers),
+            "host_cores_visible": int(visible), "kind": "oracle",
+            "sample": f"{heads} heads of {cfg.name} (heads {bhs}), each: prologue over all {cfg.N} "
+                      f"tokens ({pro.mean():.2f} s) + INT4 attention of {rows} seeded query rows "
+                      f"({att.mean():.2f} s), one head per process on {workers} cores: "
+                      f"{wall:.1f} s wall; extrapolated to {cfg.BH} heads x {cfg.N} rows by the "
+                      f"measured per-head work = {full_wall:.0f} s",
+            "measured_s": round(wall, 2), "extrapolated": True}
 
 
 if __name__ == "__main__":

@@ -15,7 +15,8 @@
  *   rotattn_prepare_qkv  3D RoPE + partition-wise rotation + per-block INT4
  *                        quantize and pack (RoPE'd fp16 Q/K for fallback heads)
  *   rotattn_int4_fwd     integer QK^T, online softmax, u4 P, integer P.V
- *   rotattn_fp16_fwd     FP16 FlashAttention for the fallback heads
+ *   rotattn_fp16_fwd     FP16 FlashAttention for the fallback heads, on the
+ *                        caller's RoPE'd fp16 Q'/K' and V
  *   rotattn_mixed_fwd    all of the above on one stream, routed by a head mask
  *
  * Conventions (every entry point):
@@ -213,9 +214,14 @@ int rotattn_pcode_thresholds_host(float tau[15]);
 /* Host: kappa = fl32(log2(e)/sqrt(D)). */
 float rotattn_kappa_host(int32_t D);
 
+/* Bytes for the prepared buffers rotattn_prepare_qkv writes in the production
+ * form: FP8 layout with the fp16 fallback buffers (q_rope, k_rope, v_t); 0 for
+ * an invalid shape.  Equal to rotattn_workspace_bytes. */
+size_t rotattn_prepared_bytes(const rotattn_shape* s);
+
 /* Bytes for a rotattn_prepared of the given rotattn_layout (with_rope != 0
- * adds the fp16 Q'/K' arrays); 0 for an invalid shape or layout. */
-size_t rotattn_prepared_bytes(const rotattn_shape* s, int with_rope, int layout);
+ * adds the fp16 fallback buffers); 0 for an invalid shape or layout. */
+size_t rotattn_prepared_bytes_layout(const rotattn_shape* s, int with_rope, int layout);
 
 /* Lay a rotattn_prepared out in [base, base+bytes) (256-byte aligned parts). */
 int rotattn_prepared_carve(const rotattn_shape* s, void* base, size_t bytes,
@@ -286,20 +292,50 @@ int rotattn_int4_fwd_strided(const rotattn_shape* s, const rotattn_prepared* p,
                              const rotattn_debug* dbg, hipStream_t stream);
 
 /*
- * FP16 FlashAttention: O = softmax(Q'K'^T / sqrt(D)) V on fp16 MFMA with fp32
- * softmax and accumulation, for the heads with head_select_host[...] != 0
- * (all heads when NULL).  Reads p->q_rope, p->k_rope and p->v_t as written by
- * rotattn_prepare_qkv for those heads (fallback heads); o: [B][H][N][D] fp16.
+ * FP16 FlashAttention on the caller's tensors (RotateAttention page,
+ * Abstract: selective FP16 fallback for accuracy-sensitive attention):
+ * O = softmax(Q'K'^T / sqrt(D)) V on fp16 MFMA with fp32 softmax and
+ * accumulation, for the heads with head_select_host[b*H+h] != 0 (all heads
+ * when NULL).
+ *  q_rope, k_rope: RoPE'd fp16 Q' and K' [B][H][N][D] (no rotation, no
+ *          quantization -- what a fallback head of rotattn_prepare_qkv gets);
+ *  v:      fp16 V [B][H][N][D];
+ *  workspace: device scratch of at least rotattn_fp16_workspace_bytes(s)
+ *          bytes, 16-byte aligned, caller-owned; the call stages zero-padded
+ *          Q', K' and the V^T tiles of the P.V operand there (contents on
+ *          return are unspecified);
+ *  o:      fp16 [B][H][N][D], written for the selected heads only.
+ * ROTATTN_E_WORKSPACE when the workspace is too small.
  */
-int rotattn_fp16_fwd(const rotattn_shape* s, const rotattn_prepared* p,
-                     const uint8_t* head_select_host, uint16_t* o,
-                     hipStream_t stream);
+int rotattn_fp16_fwd(const rotattn_shape* s, const uint16_t* q_rope, const uint16_t* k_rope,
+                     const uint16_t* v, const uint8_t* head_select_host, void* workspace,
+                     size_t workspace_bytes, uint16_t* o, hipStream_t stream);
 
-/* rotattn_fp16_fwd writing o with o_strides (NULL = contiguous). */
-int rotattn_fp16_fwd_strided(const rotattn_shape* s, const rotattn_prepared* p,
-                             const uint8_t* head_select_host, uint16_t* o,
-                             const rotattn_strides* o_strides,
-                             hipStream_t stream);
+/* rotattn_fp16_fwd with strides for q_rope, k_rope and v (shared; NULL =
+ * contiguous) and for o (NULL = contiguous). */
+int rotattn_fp16_fwd_strided(const rotattn_shape* s, const uint16_t* q_rope,
+                             const uint16_t* k_rope, const uint16_t* v,
+                             const rotattn_strides* qkv_strides, const uint8_t* head_select_host,
+                             void* workspace, size_t workspace_bytes, uint16_t* o,
+                             const rotattn_strides* o_strides, hipStream_t stream);
+
+/* Workspace bytes for rotattn_fp16_fwd: three [B*H][N_pad][D] fp16 arrays
+ * (256-byte aligned parts); 0 for an invalid shape. */
+size_t rotattn_fp16_workspace_bytes(const rotattn_shape* s);
+
+/*
+ * The same FP16 attention on prepared buffers: reads p->q_rope, p->k_rope
+ * and p->v_t as written by rotattn_prepare_qkv for the selected heads
+ * (fallback heads); no staging.  o: [B][H][N][D] fp16.
+ */
+int rotattn_fp16_fwd_prepared(const rotattn_shape* s, const rotattn_prepared* p,
+                              const uint8_t* head_select_host, uint16_t* o,
+                              hipStream_t stream);
+
+/* rotattn_fp16_fwd_prepared writing o with o_strides (NULL = contiguous). */
+int rotattn_fp16_fwd_prepared_strided(const rotattn_shape* s, const rotattn_prepared* p,
+                                      const uint8_t* head_select_host, uint16_t* o,
+                                      const rotattn_strides* o_strides, hipStream_t stream);
 
 /* Workspace bytes for rotattn_mixed_fwd (a FP8-layout rotattn_prepared with
  * the fp16 fallback buffers). */
@@ -308,6 +344,7 @@ size_t rotattn_workspace_bytes(const rotattn_shape* s);
 /*
  * Whole forward: prepare (FP8 layout), INT4 attention for mask == 0 heads,
  * FP16 attention for mask != 0 heads, all on `stream`, writing every head of o.
+ * Every argument of the three steps is checked before the first launch.
  */
 int rotattn_mixed_fwd(const rotattn_shape* s, const uint16_t* q,
                       const uint16_t* k, const uint16_t* v,

@@ -55,7 +55,8 @@ def test_entry_points_reject_bad_arguments_before_launch():
     nul = C.c_void_p(0)
     assert L.rotattn_prepare_qkv(C.byref(s), nul, nul, nul, None, nul, None, nul) == -1
     assert L.rotattn_int4_fwd(C.byref(s), None, nul, nul, None, nul) == -1
-    assert L.rotattn_fp16_fwd(C.byref(s), None, nul, nul, nul) == -1
+    assert L.rotattn_fp16_fwd(C.byref(s), nul, nul, nul, nul, nul, 0, nul, nul) == -1
+    assert L.rotattn_fp16_fwd_prepared(C.byref(s), None, nul, nul, nul) == -1
     assert L.rotattn_mixed_fwd(C.byref(s), nul, nul, nul, None, nul, nul, 0, nul, nul) == -1
     bad = R.make_shape(1, 2, (2, 4, 4), 64, (24, 20, 22))
     assert L.rotattn_mixed_fwd(C.byref(bad), nul, nul, nul, None, nul, nul, 0, nul, nul) == -2
@@ -69,7 +70,9 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert L.rotattn_prepared_carve(C.byref(s), C.c_void_p(8), 1 << 30, 1, 1, C.byref(p)) == -5
     assert L.rotattn_prepared_carve(C.byref(s), C.c_void_p(256), 16, 1, 1, C.byref(p)) == -4
     assert L.rotattn_prepared_carve(C.byref(s), C.c_void_p(256), 1 << 30, 1, 5, C.byref(p)) == -7
-    assert L.rotattn_prepared_bytes(C.byref(s), 1, 5) == 0
+    assert L.rotattn_prepared_bytes_layout(C.byref(s), 1, 5) == 0
+    assert L.rotattn_prepared_bytes(C.byref(bad)) == 0
+    assert L.rotattn_prepared_bytes(C.byref(s)) == L.rotattn_workspace_bytes(C.byref(s))
 
 
 @pytest.mark.parametrize("layout,code_bytes", [(R.LAYOUT_PACKED, 64), (R.LAYOUT_FP8, 128)])
@@ -77,8 +80,8 @@ def test_prepared_layout_sizes(layout, code_bytes):
     s = R.shape_of(synth.CONFIGS["720p"])
     NB = R.n_blocks(s)
     assert NB == 591
-    n0 = R.lib().rotattn_prepared_bytes(C.byref(s), 0, layout)
-    n1 = R.lib().rotattn_prepared_bytes(C.byref(s), 1, layout)
+    n0 = R.lib().rotattn_prepared_bytes_layout(C.byref(s), 0, layout)
+    n1 = R.lib().rotattn_prepared_bytes_layout(C.byref(s), 1, layout)
     codes = 40 * NB * 128 * code_bytes
     assert n0 >= 3 * codes + 3 * 40 * NB * 4
     # fallback buffers: q_rope, k_rope and v_t, each [B*H][N_pad][D] fp16
@@ -146,8 +149,15 @@ def test_strided_entry_points_validate_strides():
     for st, code in ((short, -7), (odd, -5)):
         assert L.rotattn_int4_fwd_strided(C.byref(s), C.byref(p), None, fake, C.byref(st), None,
                                           None, C.c_void_p(0)) in (-1, code)
-        assert L.rotattn_fp16_fwd_strided(C.byref(s), C.byref(p), None, fake, C.byref(st),
-                                          C.c_void_p(0)) in (-1, code)
+        assert L.rotattn_fp16_fwd_prepared_strided(C.byref(s), C.byref(p), None, fake,
+                                                   C.byref(st), C.c_void_p(0)) in (-1, code)
+        ws16 = L.rotattn_fp16_workspace_bytes(C.byref(s))
+        assert L.rotattn_fp16_fwd_strided(C.byref(s), fake, fake, fake, C.byref(st), None,
+                                          C.c_void_p(1 << 24), ws16, fake, None,
+                                          C.c_void_p(0)) == code
+        assert L.rotattn_fp16_fwd_strided(C.byref(s), fake, fake, fake, None, None,
+                                          C.c_void_p(1 << 24), ws16, fake, C.byref(st),
+                                          C.c_void_p(0)) == code
         assert L.rotattn_mixed_fwd_strided(C.byref(s), fake, fake, fake, None, None, None, fake,
                                            1 << 30, fake, C.byref(st), C.c_void_p(0)) == -1
     # with valid everything else, a bad output stride is reported as such
@@ -177,3 +187,55 @@ def test_binding_layout_helpers():
     with pytest.raises(ValueError):
         R.strides_of(x[0])                                            # not 4-D
     assert set(R.NORMALIZERS) == {"exp", "codes"}
+
+
+def test_mixed_checks_every_argument_before_any_launch():
+    """rotattn_mixed_fwd refuses a misaligned output (or any other bad argument
+    of its three steps) before the prologue is enqueued.  There is no GPU
+    here, so a call that reached a launch would report a HIP error (-6)
+    instead of the argument error."""
+    L = R.lib()
+    s = R.make_shape(1, 2, (2, 4, 4), 64, (24, 20, 20))
+    fake = C.c_void_p(1 << 20)
+    rr = R.RopeRot(*([fake] * 9))
+    ws = L.rotattn_workspace_bytes(C.byref(s))
+    base = C.c_void_p(1 << 24)
+    mask = (C.c_uint8 * 2)(0, 1)
+    for o in (C.c_void_p((1 << 20) + 8), C.c_void_p((1 << 20) + 2)):   # misaligned o
+        assert L.rotattn_mixed_fwd(C.byref(s), fake, fake, fake, C.byref(rr), None, base, ws, o,
+                                   C.c_void_p(0)) == -5
+        assert L.rotattn_mixed_fwd(C.byref(s), fake, fake, fake, C.byref(rr), mask, base, ws, o,
+                                   C.c_void_p(0)) == -5
+    # misaligned inputs, a short workspace, an unaligned workspace
+    odd = C.c_void_p((1 << 20) + 4)
+    assert L.rotattn_mixed_fwd(C.byref(s), fake, odd, fake, C.byref(rr), None, base, ws, fake,
+                               C.c_void_p(0)) == -5
+    assert L.rotattn_mixed_fwd(C.byref(s), fake, fake, fake, C.byref(rr), None, base, ws - 1,
+                               fake, C.c_void_p(0)) == -4
+    assert L.rotattn_mixed_fwd(C.byref(s), fake, fake, fake, C.byref(rr), None,
+                               C.c_void_p((1 << 24) + 16), ws, fake, C.c_void_p(0)) == -5
+    # every argument valid: the call reaches its first launch, which has no GPU here
+    assert L.rotattn_mixed_fwd(C.byref(s), fake, fake, fake, C.byref(rr), None, base, ws, fake,
+                               C.c_void_p(0)) == -6
+
+
+def test_fp16_fwd_on_caller_buffers_checks_arguments():
+    """The FP16 attention on caller tensors: workspace size and alignment,
+    pointers, and the workspace formula (three [B*H][N_pad][D] fp16 arrays)."""
+    L = R.lib()
+    s = R.make_shape(1, 2, (2, 9, 17), 128, (44, 42, 42))        # N = 306, N_pad = 384
+    need = L.rotattn_fp16_workspace_bytes(C.byref(s))
+    part = 2 * 384 * 128 * 2
+    assert need == 3 * ((part + 255) // 256 * 256)
+    fake = C.c_void_p(1 << 20)
+    ws = C.c_void_p(1 << 24)
+    nul = C.c_void_p(0)
+    assert L.rotattn_fp16_fwd(C.byref(s), fake, fake, nul, None, ws, need, fake, nul) == -1
+    assert L.rotattn_fp16_fwd(C.byref(s), fake, fake, fake, None, ws, need - 1, fake, nul) == -4
+    assert L.rotattn_fp16_fwd(C.byref(s), fake, fake, fake, None, C.c_void_p((1 << 24) + 8), need,
+                              fake, nul) == -5
+    assert L.rotattn_fp16_fwd(C.byref(s), fake, fake, fake, None, ws, need,
+                              C.c_void_p((1 << 20) + 6), nul) == -5
+    none = (C.c_uint8 * 2)(0, 0)
+    assert L.rotattn_fp16_fwd(C.byref(s), fake, fake, fake, none, ws, need, fake, nul) == 0
+    assert L.rotattn_fp16_fwd(C.byref(s), fake, fake, fake, None, ws, need, fake, nul) == -6

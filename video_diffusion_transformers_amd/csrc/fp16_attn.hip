@@ -150,8 +150,9 @@ struct Fp16Kernel {
     // buffer do not overlap and does not wait for the load before them
     __shared__ __align__(16) uint8_t sk0[kKT * KRB], sk1[kKT * KRB];
     __shared__ __align__(16) uint8_t sv0[D * 128], sv1[D * 128];
-    const int qb = blockIdx.x, bh = blockIdx.y;
-    if (!a.run.test(bh)) return;
+    // bh: the head in the buffers; the run mask and O use its global index
+    const int qb = blockIdx.x, bh = blockIdx.y, gbh = a.bh0 + bh;
+    if (!a.run.test(gbh)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int col = lane & 31, hh = lane >> 5;
     const int N = a.N, NT = (N + kKT - 1) / kKT;
@@ -253,7 +254,7 @@ struct Fp16Kernel {
     const int query = qb * kBlock + 32 * w + col;
     if (query < N) {
       const float il = 1.0f / l;
-      uint16_t* orow = a.o + a.os.head_offset(bh, a.H) + (int64_t)query * a.os.token;
+      uint16_t* orow = a.o + a.os.head_offset(gbh, a.H) + (int64_t)query * a.os.token;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -274,6 +275,7 @@ __global__ __launch_bounds__(kFThreads, 2) void k_fp16_attn(Fp16Args a) {
   Fp16Kernel<D>::run(a);
 }
 
+// BH: heads in the buffers (global heads a.bh0 .. a.bh0 + BH - 1)
 hipError_t launch_fp16(int D, int BH, const Fp16Args& a, hipStream_t st) {
   dim3 grid(a.NB, BH);
   if (D == 128)

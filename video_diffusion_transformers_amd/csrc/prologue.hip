@@ -619,6 +619,47 @@ __device__ __forceinline__ void prologue_fallback(const PrologueArgs& a, uint32_
   store_vt_tiles<D>(stage_q, a.v_t + (head_pad + n0) * D);
 }
 
+// Staging for the FP16 attention on caller buffers: already RoPE'd fp16 Q', K'
+// and V of the selected heads (read through their strides) -> zero-padded
+// [N_pad][D] rows of Q' and K' and the V^T tiles of the FP16 P.V operand,
+// the layout the FP16 attention kernel reads.  One work-group per (128-token
+// block, head of the chunk [bh0, bh0 + gridDim.y)); buffers are indexed by
+// the head's place in the chunk.
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_stage_fp16(StageArgs a) {
+  constexpr int kRS = D / 2 + 1;
+  __shared__ __align__(16) uint32_t stage[kBlock * kRS];
+  const int blk = blockIdx.x, lh = blockIdx.y, bh = a.bh0 + lh;
+  if (!a.run.test(bh)) return;
+  const int n0 = blk * kBlock;
+  const int64_t head_in = a.in.head_offset(bh, a.H);
+  const size_t head_pad = (size_t)lh * a.NB * kBlock;
+  const uint16_t* src[2] = {a.q, a.k};
+  uint16_t* dst[2] = {a.q_pad, a.k_pad};
+  for (int s = 0; s < 2; ++s) {
+    load_tile<D>(src[s] + head_in, a.in.token, n0, a.N, stage);
+    wait_tiles();
+    __syncthreads();
+    store_tile_all<D>(dst[s] + head_pad * D, n0, stage);
+    __syncthreads();
+  }
+  load_tile<D>(a.v + head_in, a.in.token, n0, a.N, stage);
+  wait_tiles();
+  __syncthreads();
+  store_vt_tiles<D>(stage, a.v_t + (head_pad + n0) * D);
+}
+
+hipError_t launch_stage_fp16(int D, int nbh, const StageArgs& a, hipStream_t st) {
+  dim3 grid(a.NB, nbh);
+  if (D == 128)
+    hipLaunchKernelGGL(k_stage_fp16<128>, grid, dim3(kThreads), 0, st, a);
+  else if (D == 64)
+    hipLaunchKernelGGL(k_stage_fp16<64>, grid, dim3(kThreads), 0, st, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 // One work-group per (128-token block, head), 4 waves (one per SIMD): two
 // work-groups share a CU (LDS), so one group's MFMA phase overlaps the other's
 // memory phases.

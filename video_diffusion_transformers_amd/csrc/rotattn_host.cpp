@@ -123,7 +123,7 @@ float rotattn_kappa_host(int32_t D) {
   return (float)(1.0L / logl(2.0L) / sqrtl((long double)D));
 }
 
-size_t rotattn_prepared_bytes(const rotattn_shape* s, int with_rope, int layout) {
+size_t rotattn_prepared_bytes_layout(const rotattn_shape* s, int with_rope, int layout) {
   if (rotattn_validate(s) != ROTATTN_OK) return 0;
   if (layout != ROTATTN_LAYOUT_PACKED && layout != ROTATTN_LAYOUT_FP8) return 0;
   const size_t BH = (size_t)s->B * s->H, NB = nblocks(s), D = s->D;
@@ -142,7 +142,7 @@ int rotattn_prepared_carve(const rotattn_shape* s, void* base, size_t bytes, int
   if (!base || !out) return ROTATTN_E_NULL;
   if (layout != ROTATTN_LAYOUT_PACKED && layout != ROTATTN_LAYOUT_FP8) return ROTATTN_E_ARG;
   if (((uintptr_t)base & (kAlign - 1)) != 0) return ROTATTN_E_ALIGN;
-  if (bytes < rotattn_prepared_bytes(s, with_rope, layout)) return ROTATTN_E_WORKSPACE;
+  if (bytes < rotattn_prepared_bytes_layout(s, with_rope, layout)) return ROTATTN_E_WORKSPACE;
   const size_t BH = (size_t)s->B * s->H, NB = nblocks(s), D = s->D;
   const size_t per_code = layout == ROTATTN_LAYOUT_FP8 ? 2 : 1;
   const size_t packed = align_up(BH * NB * kBlock * D * per_code / 2);
@@ -167,6 +167,10 @@ int rotattn_prepared_carve(const rotattn_shape* s, void* base, size_t bytes, int
     out->v_t = nullptr;
   }
   return ROTATTN_OK;
+}
+
+size_t rotattn_prepared_bytes(const rotattn_shape* s) {
+  return rotattn_prepared_bytes_layout(s, 1, ROTATTN_LAYOUT_FP8);
 }
 
 // Strides of a tensor, contiguous [B][H][N][D] when st is NULL.  Every stride
@@ -194,10 +198,14 @@ int rotattn_prepare_qkv(const rotattn_shape* s, const uint16_t* q, const uint16_
   return rotattn_prepare_qkv_strided(s, q, k, v, nullptr, rr, fallback_mask_host, out, stream);
 }
 
-int rotattn_prepare_qkv_strided(const rotattn_shape* s, const uint16_t* q, const uint16_t* k,
-                                const uint16_t* v, const rotattn_strides* qkv_strides,
-                                const rotattn_rope_rot* rr, const uint8_t* fallback_mask_host,
-                                const rotattn_prepared* out, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Every argument check of the prologue, nothing enqueued.
+int check_prepare(const rotattn_shape* s, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                  const rotattn_strides* qkv_strides, const rotattn_rope_rot* rr,
+                  const uint8_t* fallback_mask_host, const rotattn_prepared* out, Strides* in) {
   const int st = rotattn_validate(s);
   if (st != ROTATTN_OK) return st;
   if (!q || !k || !v || !rr || !out) return ROTATTN_E_NULL;
@@ -210,7 +218,7 @@ int rotattn_prepare_qkv_strided(const rotattn_shape* s, const uint16_t* q, const
   const int BH = s->B * s->H;
   if (out->layout != ROTATTN_LAYOUT_PACKED && out->layout != ROTATTN_LAYOUT_FP8) return ROTATTN_E_ARG;
   int n_fb = 0;
-  const HeadBits fb = make_bits(fallback_mask_host, BH, true, false, &n_fb);
+  make_bits(fallback_mask_host, BH, true, false, &n_fb);
   if (n_fb < BH) {
     if (!out->q4 || !out->k4 || !out->v4 || !out->q_scale_l2 || !out->k_scale || !out->v_scale ||
         (rot && !out->rot64))
@@ -223,12 +231,20 @@ int rotattn_prepare_qkv_strided(const rotattn_shape* s, const uint16_t* q, const
       return ROTATTN_E_ALIGN;
   }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return ROTATTN_E_ALIGN;
-  Strides in;
-  const int sr = resolve_strides(s, qkv_strides, &in);
-  if (sr != ROTATTN_OK) return sr;
+  return resolve_strides(s, qkv_strides, in);
+}
 
-  if (rot && n_fb < BH && launch_rot_to_f64(rr->rot_t, rr->rot_h, rr->rot_w, s->d_t, s->d_h, out->rot64,
-                                     stream) != hipSuccess)
+int launch_prepare(const rotattn_shape* s, const uint16_t* q, const uint16_t* k,
+                   const uint16_t* v, const Strides& in, const rotattn_rope_rot* rr,
+                   const uint8_t* fallback_mask_host, const rotattn_prepared* out,
+                   hipStream_t stream) {
+  const bool rot = rr->rot_t != nullptr;
+  const int BH = s->B * s->H;
+  int n_fb = 0;
+  const HeadBits fb = make_bits(fallback_mask_host, BH, true, false, &n_fb);
+  if (rot && n_fb < BH &&
+      launch_rot_to_f64(rr->rot_t, rr->rot_h, rr->rot_w, s->d_t, s->d_h, out->rot64, stream) !=
+          hipSuccess)
     return ROTATTN_E_HIP;
   PrologueArgs a;
   a.q = q; a.k = k; a.v = v;
@@ -253,39 +269,41 @@ int rotattn_prepare_qkv_strided(const rotattn_shape* s, const uint16_t* q, const
              : ROTATTN_E_HIP;
 }
 
-int rotattn_int4_fwd(const rotattn_shape* s, const rotattn_prepared* p,
-                     const uint8_t* fallback_mask_host, uint16_t* o, const rotattn_debug* dbg,
-                     hipStream_t stream) {
-  return rotattn_int4_fwd_strided(s, p, fallback_mask_host, o, nullptr, nullptr, dbg, stream);
-}
-
-int rotattn_int4_fwd_strided(const rotattn_shape* s, const rotattn_prepared* p,
-                             const uint8_t* fallback_mask_host, uint16_t* o,
-                             const rotattn_strides* o_strides, const rotattn_int4_opts* opts,
-                             const rotattn_debug* dbg, hipStream_t stream) {
+// Every argument check of the INT4 attention, nothing enqueued.
+int check_int4(const rotattn_shape* s, const rotattn_prepared* p, uint16_t* o,
+               const rotattn_strides* o_strides, const rotattn_int4_opts* opts,
+               const rotattn_debug* dbg, Strides* os) {
   const int st = rotattn_validate(s);
   if (st != ROTATTN_OK) return st;
   if (!p || !o) return ROTATTN_E_NULL;
-  Strides os;
-  const int sr = resolve_strides(s, o_strides, &os);
+  const int sr = resolve_strides(s, o_strides, os);
   if (sr != ROTATTN_OK) return sr;
   if (!p->q4 || !p->k4 || !p->v4 || !p->q_scale_l2 || !p->k_scale || !p->v_scale)
     return ROTATTN_E_NULL;
   if (!aligned16(p->q4) || !aligned16(p->k4) || !aligned16(p->v4) || !aligned16(o))
     return ROTATTN_E_ALIGN;
   if (p->layout != ROTATTN_LAYOUT_PACKED && p->layout != ROTATTN_LAYOUT_FP8) return ROTATTN_E_ARG;
-  const bool f8 = p->layout == ROTATTN_LAYOUT_FP8;
   const int norm = opts ? opts->normalizer : ROTATTN_NORM_EXP;
   if (norm != ROTATTN_NORM_EXP && norm != ROTATTN_NORM_CODES) return ROTATTN_E_ARG;
-  if (norm == ROTATTN_NORM_CODES && !f8) return ROTATTN_E_UNSUPPORTED;
-  const int BH = s->B * s->H;
-  Int4Debug d{};
+  if (norm == ROTATTN_NORM_CODES && p->layout != ROTATTN_LAYOUT_FP8) return ROTATTN_E_UNSUPPORTED;
   if (dbg) {
     if (!dbg->s_int || !dbg->p_code || !dbg->pv_int || !dbg->m_final || !dbg->l_final)
       return ROTATTN_E_NULL;
     if (dbg->b < 0 || dbg->b >= s->B || dbg->h < 0 || dbg->h >= s->H || dbg->q_block < 0 ||
         dbg->q_block >= nblocks(s))
       return ROTATTN_E_ARG;
+  }
+  return ROTATTN_OK;
+}
+
+int launch_int4_all(const rotattn_shape* s, const rotattn_prepared* p,
+                    const uint8_t* fallback_mask_host, uint16_t* o, const Strides& os,
+                    const rotattn_int4_opts* opts, const rotattn_debug* dbg, hipStream_t stream) {
+  const bool f8 = p->layout == ROTATTN_LAYOUT_FP8;
+  const int norm = opts ? opts->normalizer : ROTATTN_NORM_EXP;
+  const int BH = s->B * s->H;
+  Int4Debug d{};
+  if (dbg) {
     d.s_int = dbg->s_int;
     d.p_code = dbg->p_code;
     d.pv_int = dbg->pv_int;
@@ -313,39 +331,149 @@ int rotattn_int4_fwd_strided(const rotattn_shape* s, const rotattn_prepared* p,
   return ROTATTN_OK;
 }
 
-int rotattn_fp16_fwd(const rotattn_shape* s, const rotattn_prepared* p,
-                     const uint8_t* head_select_host, uint16_t* o, hipStream_t stream) {
-  return rotattn_fp16_fwd_strided(s, p, head_select_host, o, nullptr, stream);
-}
-
-int rotattn_fp16_fwd_strided(const rotattn_shape* s, const rotattn_prepared* p,
-                             const uint8_t* head_select_host, uint16_t* o,
-                             const rotattn_strides* o_strides, hipStream_t stream) {
+// Every argument check of the FP16 attention on prepared buffers, nothing enqueued.
+int check_fp16_prepared(const rotattn_shape* s, const rotattn_prepared* p, uint16_t* o,
+                        const rotattn_strides* o_strides, Strides* os) {
   const int st = rotattn_validate(s);
   if (st != ROTATTN_OK) return st;
   if (!p || !o) return ROTATTN_E_NULL;
-  Strides os;
-  const int sr = resolve_strides(s, o_strides, &os);
+  const int sr = resolve_strides(s, o_strides, os);
   if (sr != ROTATTN_OK) return sr;
   if (!p->q_rope || !p->k_rope || !p->v_t) return ROTATTN_E_NULL;
   if (!aligned16(p->q_rope) || !aligned16(p->k_rope) || !aligned16(p->v_t) || !aligned16(o))
     return ROTATTN_E_ALIGN;
-  const int BH = s->B * s->H;
-  int n_run = 0;
+  return ROTATTN_OK;
+}
+
+// FP16 attention over the selected global heads bh0 .. bh0 + nbh - 1 whose
+// padded Q', K' and V^T tiles start at q, k, v_t.
+int launch_fp16_heads(const rotattn_shape* s, const uint16_t* q, const uint16_t* k,
+                      const uint16_t* v_t, const HeadBits& run, int bh0, int nbh, uint16_t* o,
+                      const Strides& os, hipStream_t stream) {
   Fp16Args a;
-  a.run = make_bits(head_select_host, BH, true, true, &n_run);
-  a.q = p->q_rope; a.k = p->k_rope; a.v_t = p->v_t; a.o = o;
+  a.run = run;
+  a.q = q; a.k = k; a.v_t = v_t; a.o = o;
   a.os = os;
   a.H = s->H;
   a.N = s->N;
   a.NB = nblocks(s);
   a.kappa = rotattn_kappa_host(s->D);
+  a.bh0 = bh0;
+  return launch_fp16(s->D, nbh, a, stream) == hipSuccess ? ROTATTN_OK : ROTATTN_E_HIP;
+}
+
+// Bytes of one head's staged fp16 buffers (padded Q', K', V^T tiles).
+size_t fp16_head_bytes(const rotattn_shape* s) {
+  return (size_t)nblocks(s) * kBlock * s->D * 2;
+}
+
+// Stage heads bh0 .. bh0 + nbh - 1 (selected ones only) into q_pad, k_pad,
+// v_t and run the FP16 attention on them.
+int stage_and_run_fp16(const rotattn_shape* s, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* v, const Strides& in, const HeadBits& run, int bh0,
+                       int nbh, uint16_t* q_pad, uint16_t* k_pad, uint16_t* v_t, uint16_t* o,
+                       const Strides& os, hipStream_t stream) {
+  StageArgs g;
+  g.q = q; g.k = k; g.v = v;
+  g.in = in;
+  g.H = s->H;
+  g.N = s->N;
+  g.NB = nblocks(s);
+  g.q_pad = q_pad; g.k_pad = k_pad; g.v_t = v_t;
+  g.run = run;
+  g.bh0 = bh0;
+  if (launch_stage_fp16(s->D, nbh, g, stream) != hipSuccess) return ROTATTN_E_HIP;
+  return launch_fp16_heads(s, q_pad, k_pad, v_t, run, bh0, nbh, o, os, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int rotattn_prepare_qkv_strided(const rotattn_shape* s, const uint16_t* q, const uint16_t* k,
+                                const uint16_t* v, const rotattn_strides* qkv_strides,
+                                const rotattn_rope_rot* rr, const uint8_t* fallback_mask_host,
+                                const rotattn_prepared* out, hipStream_t stream) {
+  Strides in;
+  const int st = check_prepare(s, q, k, v, qkv_strides, rr, fallback_mask_host, out, &in);
+  if (st != ROTATTN_OK) return st;
+  return launch_prepare(s, q, k, v, in, rr, fallback_mask_host, out, stream);
+}
+
+int rotattn_int4_fwd(const rotattn_shape* s, const rotattn_prepared* p,
+                     const uint8_t* fallback_mask_host, uint16_t* o, const rotattn_debug* dbg,
+                     hipStream_t stream) {
+  return rotattn_int4_fwd_strided(s, p, fallback_mask_host, o, nullptr, nullptr, dbg, stream);
+}
+
+int rotattn_int4_fwd_strided(const rotattn_shape* s, const rotattn_prepared* p,
+                             const uint8_t* fallback_mask_host, uint16_t* o,
+                             const rotattn_strides* o_strides, const rotattn_int4_opts* opts,
+                             const rotattn_debug* dbg, hipStream_t stream) {
+  Strides os;
+  const int st = check_int4(s, p, o, o_strides, opts, dbg, &os);
+  if (st != ROTATTN_OK) return st;
+  return launch_int4_all(s, p, fallback_mask_host, o, os, opts, dbg, stream);
+}
+
+int rotattn_fp16_fwd_prepared(const rotattn_shape* s, const rotattn_prepared* p,
+                              const uint8_t* head_select_host, uint16_t* o, hipStream_t stream) {
+  return rotattn_fp16_fwd_prepared_strided(s, p, head_select_host, o, nullptr, stream);
+}
+
+int rotattn_fp16_fwd_prepared_strided(const rotattn_shape* s, const rotattn_prepared* p,
+                                      const uint8_t* head_select_host, uint16_t* o,
+                                      const rotattn_strides* o_strides, hipStream_t stream) {
+  Strides os;
+  const int st = check_fp16_prepared(s, p, o, o_strides, &os);
+  if (st != ROTATTN_OK) return st;
+  int n_run = 0;
+  const HeadBits run = make_bits(head_select_host, s->B * s->H, true, true, &n_run);
   if (n_run == 0) return ROTATTN_OK;
-  return launch_fp16(s->D, BH, a, stream) == hipSuccess ? ROTATTN_OK : ROTATTN_E_HIP;
+  return launch_fp16_heads(s, p->q_rope, p->k_rope, p->v_t, run, 0, s->B * s->H, o, os, stream);
+}
+
+size_t rotattn_fp16_workspace_bytes(const rotattn_shape* s) {
+  if (rotattn_validate(s) != ROTATTN_OK) return 0;
+  return 3 * align_up((size_t)s->B * s->H * fp16_head_bytes(s));
+}
+
+int rotattn_fp16_fwd(const rotattn_shape* s, const uint16_t* q_rope, const uint16_t* k_rope,
+                     const uint16_t* v, const uint8_t* head_select_host, void* workspace,
+                     size_t workspace_bytes, uint16_t* o, hipStream_t stream) {
+  return rotattn_fp16_fwd_strided(s, q_rope, k_rope, v, nullptr, head_select_host, workspace,
+                                  workspace_bytes, o, nullptr, stream);
+}
+
+int rotattn_fp16_fwd_strided(const rotattn_shape* s, const uint16_t* q_rope,
+                             const uint16_t* k_rope, const uint16_t* v,
+                             const rotattn_strides* qkv_strides, const uint8_t* head_select_host,
+                             void* workspace, size_t workspace_bytes, uint16_t* o,
+                             const rotattn_strides* o_strides, hipStream_t stream) {
+  const int st = rotattn_validate(s);
+  if (st != ROTATTN_OK) return st;
+  if (!q_rope || !k_rope || !v || !workspace || !o) return ROTATTN_E_NULL;
+  if (!aligned16(q_rope) || !aligned16(k_rope) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(workspace))
+    return ROTATTN_E_ALIGN;
+  Strides in, os;
+  int r = resolve_strides(s, qkv_strides, &in);
+  if (r != ROTATTN_OK) return r;
+  r = resolve_strides(s, o_strides, &os);
+  if (r != ROTATTN_OK) return r;
+  if (workspace_bytes < rotattn_fp16_workspace_bytes(s)) return ROTATTN_E_WORKSPACE;
+  const int BH = s->B * s->H;
+  int n_run = 0;
+  const HeadBits run = make_bits(head_select_host, BH, true, true, &n_run);
+  if (n_run == 0) return ROTATTN_OK;
+  const size_t part = align_up((size_t)BH * fp16_head_bytes(s));
+  uint8_t* w = (uint8_t*)workspace;
+  return stage_and_run_fp16(s, q_rope, k_rope, v, in, run, 0, BH, (uint16_t*)w,
+                            (uint16_t*)(w + part), (uint16_t*)(w + 2 * part), o, os, stream);
 }
 
 size_t rotattn_workspace_bytes(const rotattn_shape* s) {
-  return rotattn_prepared_bytes(s, 1, ROTATTN_LAYOUT_FP8);
+  return rotattn_prepared_bytes_layout(s, 1, ROTATTN_LAYOUT_FP8);
 }
 
 int rotattn_mixed_fwd(const rotattn_shape* s, const uint16_t* q, const uint16_t* k,
@@ -361,24 +489,27 @@ int rotattn_mixed_fwd_strided(const rotattn_shape* s, const uint16_t* q, const u
                               const rotattn_rope_rot* rr, const uint8_t* fallback_mask_host,
                               void* workspace, size_t workspace_bytes, uint16_t* o,
                               const rotattn_strides* o_strides, hipStream_t stream) {
+  // every argument is checked before anything is enqueued
   const int st = rotattn_validate(s);
   if (st != ROTATTN_OK) return st;
   if (!q || !k || !v || !rr || !workspace || !o) return ROTATTN_E_NULL;
   rotattn_prepared p;
-  const int cs = rotattn_prepared_carve(s, workspace, workspace_bytes, 1, ROTATTN_LAYOUT_FP8, &p);
-  if (cs != ROTATTN_OK) return cs;
-  Strides chk;
-  int r = resolve_strides(s, o_strides, &chk);
+  int r = rotattn_prepared_carve(s, workspace, workspace_bytes, 1, ROTATTN_LAYOUT_FP8, &p);
   if (r != ROTATTN_OK) return r;
-  r = rotattn_prepare_qkv_strided(s, q, k, v, qkv_strides, rr, fallback_mask_host, &p, stream);
+  Strides in, os;
+  r = check_prepare(s, q, k, v, qkv_strides, rr, fallback_mask_host, &p, &in);
   if (r != ROTATTN_OK) return r;
-  r = rotattn_int4_fwd_strided(s, &p, fallback_mask_host, o, o_strides, nullptr, nullptr, stream);
+  r = check_int4(s, &p, o, o_strides, nullptr, nullptr, &os);
   if (r != ROTATTN_OK) return r;
-  if (fallback_mask_host) {
-    int n_fb = 0;
-    make_bits(fallback_mask_host, s->B * s->H, true, false, &n_fb);
-    if (n_fb > 0) r = rotattn_fp16_fwd_strided(s, &p, fallback_mask_host, o, o_strides, stream);
-  }
+  r = check_fp16_prepared(s, &p, o, o_strides, &os);
+  if (r != ROTATTN_OK) return r;
+  r = launch_prepare(s, q, k, v, in, rr, fallback_mask_host, &p, stream);
+  if (r != ROTATTN_OK) return r;
+  r = launch_int4_all(s, &p, fallback_mask_host, o, os, nullptr, nullptr, stream);
+  if (r != ROTATTN_OK) return r;
+  int n_fb = 0;
+  const HeadBits fb = make_bits(fallback_mask_host, s->B * s->H, true, false, &n_fb);
+  if (n_fb > 0) r = launch_fp16_heads(s, p.q_rope, p.k_rope, p.v_t, fb, 0, s->B * s->H, o, os, stream);
   return r;
 }
 

@@ -114,14 +114,25 @@ struct Int4Debug {
 };
 
 struct Fp16Args {
-  const uint16_t *q, *k;   // RoPE'd Q', K': [BH][N_pad][D], rows >= N zero
-  const uint16_t* v_t;     // V^T per 64-key tile: [BH][N_pad/64][D][64], operand order
+  const uint16_t *q, *k;   // RoPE'd Q', K': [heads][N_pad][D], rows >= N zero
+  const uint16_t* v_t;     // V^T per 64-key tile: [heads][N_pad/64][D][64], operand order
   uint16_t* o;
   Strides os;              // of o
   int H;
   int N, NB;
   float kappa;
-  HeadBits run;
+  HeadBits run;            // by global head index
+  int bh0;                 // global index of the heads' first (buffers hold heads bh0..)
+};
+
+// Staging of caller fp16 Q', K', V for the FP16 attention (heads bh0.. of a chunk).
+struct StageArgs {
+  const uint16_t *q, *k, *v;
+  Strides in;              // of q, k and v
+  int H, N, NB;
+  uint16_t *q_pad, *k_pad, *v_t;   // [chunk heads][N_pad][D] each (v_t as V^T tiles)
+  HeadBits run;            // by global head index
+  int bh0;
 };
 
 // Launchers (each defined next to its kernel).  Return a hipError_t.
@@ -132,6 +143,7 @@ hipError_t launch_prologue(int D, int dt, int BH, bool f8, bool rot, const Prolo
 hipError_t launch_int4(int D, int BH, const Int4Args& a, const Int4Debug* dbg, hipStream_t st);
 hipError_t launch_int4_f8(int D, int BH, const Int4Args& a, const Int4Debug* dbg, hipStream_t st);
 hipError_t launch_fp16(int D, int BH, const Fp16Args& a, hipStream_t st);
+hipError_t launch_stage_fp16(int D, int nbh, const StageArgs& a, hipStream_t st);
 hipError_t launch_pcode_sweep(bool f8, uint32_t mag_lo, uint32_t count, const float tau[15],
                               float log2_15, uint32_t* transitions, uint32_t max_transitions,
                               uint32_t* n_trans, hipStream_t st);

@@ -28,13 +28,16 @@ STATUS = {0: "ok", -1: "null pointer argument", -2: "inconsistent shape",
           -5: "device pointer not 16-byte aligned", -6: "HIP launch or runtime error",
           -7: "argument out of range"}
 
-EXPORTS = ["rotattn_validate", "rotattn_strerror", "rotattn_rope_tables_host",
-           "rotattn_rope_tables_phase_host",
-           "rotattn_pcode_thresholds_host", "rotattn_kappa_host", "rotattn_prepared_bytes",
-           "rotattn_prepared_carve", "rotattn_prepare_qkv", "rotattn_int4_fwd", "rotattn_fp16_fwd",
-           "rotattn_workspace_bytes", "rotattn_mixed_fwd", "rotattn_pcode_sweep",
-           "rotattn_pcode_eval", "rotattn_prepare_qkv_strided", "rotattn_int4_fwd_strided",
-           "rotattn_fp16_fwd_strided", "rotattn_mixed_fwd_strided"]
+EXPORTS = sorted(["rotattn_validate", "rotattn_strerror", "rotattn_rope_tables_host",
+                  "rotattn_rope_tables_phase_host",
+                  "rotattn_pcode_thresholds_host", "rotattn_kappa_host", "rotattn_prepared_bytes",
+                  "rotattn_prepared_bytes_layout", "rotattn_prepared_carve",
+                  "rotattn_prepare_qkv", "rotattn_int4_fwd", "rotattn_fp16_fwd",
+                  "rotattn_fp16_fwd_strided", "rotattn_fp16_workspace_bytes",
+                  "rotattn_fp16_fwd_prepared", "rotattn_fp16_fwd_prepared_strided",
+                  "rotattn_workspace_bytes", "rotattn_mixed_fwd", "rotattn_pcode_sweep",
+                  "rotattn_pcode_eval", "rotattn_prepare_qkv_strided", "rotattn_int4_fwd_strided",
+                  "rotattn_mixed_fwd_strided"])
 
 
 class Shape(C.Structure):
@@ -94,13 +97,18 @@ def lib() -> C.CDLL:
             "rotattn_rope_tables_phase_host": (C.c_int, [S, C.c_double] + [P] * 9),
             "rotattn_pcode_thresholds_host": (C.c_int, [P]),
             "rotattn_kappa_host": (C.c_float, [C.c_int32]),
-            "rotattn_prepared_bytes": (C.c_size_t, [S, C.c_int, C.c_int]),
+            "rotattn_prepared_bytes": (C.c_size_t, [S]),
+            "rotattn_prepared_bytes_layout": (C.c_size_t, [S, C.c_int, C.c_int]),
             "rotattn_prepared_carve": (C.c_int, [S, P, C.c_size_t, C.c_int, C.c_int,
                                                  C.POINTER(Prepared)]),
             "rotattn_prepare_qkv": (C.c_int, [S, P, P, P, C.POINTER(RopeRot), P,
                                               C.POINTER(Prepared), P]),
             "rotattn_int4_fwd": (C.c_int, [S, C.POINTER(Prepared), P, P, C.POINTER(Debug), P]),
-            "rotattn_fp16_fwd": (C.c_int, [S, P, P, P, P]),
+            "rotattn_fp16_fwd": (C.c_int, [S, P, P, P, P, P, C.c_size_t, P, P]),
+            "rotattn_fp16_fwd_strided": (C.c_int, [S, P, P, P, C.POINTER(Strides), P, P,
+                                                   C.c_size_t, P, C.POINTER(Strides), P]),
+            "rotattn_fp16_workspace_bytes": (C.c_size_t, [S]),
+            "rotattn_fp16_fwd_prepared": (C.c_int, [S, P, P, P, P]),
             "rotattn_workspace_bytes": (C.c_size_t, [S]),
             "rotattn_mixed_fwd": (C.c_int, [S, P, P, P, C.POINTER(RopeRot), P, P, C.c_size_t, P, P]),
             "rotattn_pcode_sweep": (C.c_int, [C.c_int, C.c_uint32, C.c_uint32, P, C.c_uint32, P, P]),
@@ -110,7 +118,7 @@ def lib() -> C.CDLL:
             "rotattn_int4_fwd_strided": (C.c_int, [S, C.POINTER(Prepared), P, P,
                                                    C.POINTER(Strides), C.POINTER(Int4Opts),
                                                    C.POINTER(Debug), P]),
-            "rotattn_fp16_fwd_strided": (C.c_int, [S, P, P, P, C.POINTER(Strides), P]),
+            "rotattn_fp16_fwd_prepared_strided": (C.c_int, [S, P, P, P, C.POINTER(Strides), P]),
             "rotattn_mixed_fwd_strided": (C.c_int, [S, P, P, P, C.POINTER(Strides),
                                                     C.POINTER(RopeRot), P, P, C.c_size_t, P,
                                                     C.POINTER(Strides), P]),
@@ -252,7 +260,7 @@ class PreparedDevice:
         torch = _torch()
         self.shape = shape
         self.layout = layout
-        nbytes = lib().rotattn_prepared_bytes(C.byref(shape), int(with_rope), layout)
+        nbytes = lib().rotattn_prepared_bytes_layout(C.byref(shape), int(with_rope), layout)
         if nbytes == 0:
             check(validate(shape) or -7, "prepared_bytes")
         self.buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
@@ -294,16 +302,39 @@ def int4_fwd(shape: Shape, prep: PreparedDevice, o, mask=None, debug: Debug | No
                                          _stream(stream)), "int4_fwd")
 
 
-def fp16_fwd(shape: Shape, prep: PreparedDevice, o, head_select=None, stream=None) -> None:
+def fp16_fwd_prepared(shape: Shape, prep: PreparedDevice, o, head_select=None,
+                      stream=None) -> None:
     """FP16 attention of the selected heads from the prologue's fallback
     buffers (q_rope, k_rope, v_t of `prep`)."""
     keep, m = _mask_arg(head_select)
-    check(lib().rotattn_fp16_fwd_strided(C.byref(shape), C.byref(prep.struct), m, _ptr(o),
+    check(lib().rotattn_fp16_fwd_prepared_strided(C.byref(shape), C.byref(prep.struct), m, _ptr(o),
+                                                  _strides_arg(strides_of(o)), _stream(stream)),
+          "fp16_fwd_prepared")
+
+
+def fp16_workspace_bytes(shape: Shape) -> int:
+    return lib().rotattn_fp16_workspace_bytes(C.byref(shape))
+
+
+def fp16_fwd(shape: Shape, q_rope, k_rope, v, o, workspace, head_select=None,
+             stream=None) -> None:
+    """FP16 attention of the selected heads on caller tensors: RoPE'd fp16
+    Q'/K' and V ([B][H][N][D] views sharing one layout), staging through the
+    uint8 device tensor `workspace` (at least fp16_workspace_bytes)."""
+    keep, m = _mask_arg(head_select)
+    st = _shared_strides(q_rope, k_rope, v)
+    check(lib().rotattn_fp16_fwd_strided(C.byref(shape), _ptr(q_rope), _ptr(k_rope), _ptr(v),
+                                         _strides_arg(st), m, _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _ptr(o),
                                          _strides_arg(strides_of(o)), _stream(stream)), "fp16_fwd")
 
 
 def workspace_bytes(shape: Shape) -> int:
     return lib().rotattn_workspace_bytes(C.byref(shape))
+
+
+def prepared_bytes(shape: Shape) -> int:
+    return lib().rotattn_prepared_bytes(C.byref(shape))
 
 
 def mixed_fwd(shape: Shape, q, k, v, rr: RopeRotDevice, mask, workspace, o, stream=None) -> None:

@@ -20,6 +20,10 @@ structure the pages describe:
 * V outliers are not tied to channels or positions (MXAttention page,
   VC-Attention abstract) -- here sparse whole-token rows scaled up.
 
+The "video_literal" distribution is the same recipe without the logit
+calibration, with Q's and K's outlier channels drawn independently: rows are
+then close to one-hot (logit spreads of tens of nats).
+
 Every tensor of every head has its own stream,
 ``SeedSequence([cfg_seed, step, tensor, b, h])`` with tensor Q=0, K=1, V=2, so a
 single head can be regenerated without the others; a head's Q/K channel scales
@@ -51,7 +55,7 @@ class Config:
     grid: Tuple[int, int, int]        # (T, Hg, Wg) latent token grid
     D: int
     split: Tuple[int, int, int]       # RoPE partition widths (d_t, d_h, d_w)
-    dist: str                         # "tiny" | "video" | "diffuse"
+    dist: str                         # "tiny" | "video" | "video_literal" | "diffuse"
     cfg_seed: int
     sample_rows: int | None = None    # None: every query row is checked
     fallback: str = "none"            # "none" | "head1" | "quarter"
@@ -79,6 +83,13 @@ CONFIGS = {
                    sample_rows=256),
     "mixed": Config("mixed", 1, 40, (21, 45, 80), 128, (44, 42, 42), "video", 4,
                     sample_rows=256, fallback="quarter", steps=4),
+    # the Small and 480p shapes on the recipe exactly as stated, without the
+    # logit calibration of "video": per-channel lognormal scales and four
+    # temporal outlier channels drawn afresh for every tensor (Q and K
+    # independently), V as in "video"
+    "small_lit": Config("small_lit", 1, 8, (4, 16, 16), 128, (44, 42, 42), "video_literal", 1),
+    "480p_lit": Config("480p_lit", 1, 40, (21, 30, 52), 128, (44, 42, 42), "video_literal", 2,
+                       sample_rows=512),
 }
 
 
@@ -127,6 +138,17 @@ def _video_channel_scales(cfg: Config, b: int, h: int):
     return sq * c, sk * c
 
 
+def _qk_video_literal(rng, N, D, split):
+    """Q or K of the literal recipe, from the tensor's own stream: per-channel
+    scale exp(0.5 z), four channels of the temporal partition (chosen without
+    replacement) raised by independent factors in [10, 30], then
+    x = scale * N(0, 1).  No rescaling of the logit spread."""
+    sig = np.exp(0.5 * rng.standard_normal(D))
+    ch = rng.choice(split[0], size=4, replace=False)
+    sig[ch] *= rng.uniform(10.0, 30.0, size=4)
+    return rng.standard_normal((N, D)) * sig[None, :]
+
+
 def _v_video(rng, N, D):
     x = rng.standard_normal((N, D))
     n_out = max(1, int(round(0.002 * N)))
@@ -149,6 +171,8 @@ def head_qkv(cfg: Config, step: int, b: int, h: int):
             else:
                 scales = _video_channel_scales(cfg, b, h)[0 if tensor == TENSOR_Q else 1]
                 x = rng.standard_normal((N, D)) * scales[None, :]
+        elif cfg.dist == "video_literal":
+            x = _v_video(rng, N, D) if tensor == TENSOR_V else _qk_video_literal(rng, N, D, cfg.split)
         elif cfg.dist == "diffuse":
             # no outliers; scaled logits have a standard deviation of about
             # one nat, so rows are spread and every P code occurs
@@ -159,15 +183,28 @@ def head_qkv(cfg: Config, step: int, b: int, h: int):
     return tuple(out)
 
 
-def all_heads_qkv(cfg: Config, step: int = 0):
-    """float16 Q, K, V for every head, each [B, H, N, D] contiguous."""
+def all_heads_qkv(cfg: Config, step: int = 0, workers: int | None = None):
+    """float16 Q, K, V for every head, each [B, H, N, D] contiguous.  Heads are
+    drawn on a thread pool (each head has its own streams, so the result does
+    not depend on the number of workers; numpy's generators release the GIL)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
     shape = (cfg.B, cfg.H, cfg.N, cfg.D)
     q = np.empty(shape, np.float16)
     k = np.empty(shape, np.float16)
     v = np.empty(shape, np.float16)
-    for b in range(cfg.B):
-        for h in range(cfg.H):
-            q[b, h], k[b, h], v[b, h] = head_qkv(cfg, step, b, h)
+
+    def one(bh):
+        b, h = divmod(bh, cfg.H)
+        q[b, h], k[b, h], v[b, h] = head_qkv(cfg, step, b, h)
+
+    n = workers if workers is not None else min(16, len(os.sched_getaffinity(0)))
+    if n <= 1 or cfg.BH == 1:
+        for bh in range(cfg.BH):
+            one(bh)
+    else:
+        with ThreadPoolExecutor(max_workers=n) as ex:
+            list(ex.map(one, range(cfg.BH)))
     return q, k, v
 
 
