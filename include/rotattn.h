@@ -62,8 +62,12 @@ typedef enum rotattn_status {
   ROTATTN_E_WORKSPACE = -4,     /* workspace smaller than rotattn_workspace_bytes() */
   ROTATTN_E_ALIGN = -5,         /* a device pointer is not 16-byte aligned */
   ROTATTN_E_HIP = -6,           /* a HIP launch or runtime call failed */
-  ROTATTN_E_ARG = -7            /* another argument is out of range (debug q-block, sweep range) */
+  ROTATTN_E_ARG = -7,           /* another argument is out of range (debug q-block, sweep range) */
+  ROTATTN_E_SCRATCH = -8        /* a head's staging exceeds ROTATTN_NOALLOC_SCRATCH_BYTES */
 } rotattn_status;
+
+/* Size of the library's static device scratch (rotattn_fp16_fwd_noalloc). */
+#define ROTATTN_NOALLOC_SCRATCH_BYTES (256u << 20)
 
 /* Problem shape. */
 typedef struct rotattn_shape {
@@ -322,6 +326,23 @@ int rotattn_fp16_fwd_strided(const rotattn_shape* s, const uint16_t* q_rope,
 /* Workspace bytes for rotattn_fp16_fwd: three [B*H][N_pad][D] fp16 arrays
  * (256-byte aligned parts); 0 for an invalid shape. */
 size_t rotattn_fp16_workspace_bytes(const rotattn_shape* s);
+
+/*
+ * rotattn_fp16_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same staging and FP16 attention (identical output), with the staging in
+ * a static device array of ROTATTN_NOALLOC_SCRATCH_BYTES held by each GPU the
+ * library runs on until the process ends, heads processed in chunks that fit
+ * it, all on `stream`.  Q', K', V and O contiguous [B][H][N][D].  No
+ * allocation and no synchronization; the scratch's device address is looked
+ * up once per device.  ROTATTN_E_SCRATCH when one head's staging (three
+ * [N_pad][D] fp16 arrays) exceeds the scratch (N_pad * D > 44,739,242 values).
+ * Every call on a GPU shares that GPU's scratch: calls that overlap on one GPU
+ * (other streams, other threads) race and must be serialized by the caller.
+ */
+int rotattn_fp16_fwd_noalloc(const rotattn_shape* s, const uint16_t* q_rope,
+                             const uint16_t* k_rope, const uint16_t* v,
+                             const uint8_t* head_select_host, uint16_t* o, hipStream_t stream);
 
 /*
  * The same FP16 attention on prepared buffers: reads p->q_rope, p->k_rope

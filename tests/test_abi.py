@@ -239,3 +239,22 @@ def test_fp16_fwd_on_caller_buffers_checks_arguments():
     none = (C.c_uint8 * 2)(0, 0)
     assert L.rotattn_fp16_fwd(C.byref(s), fake, fake, fake, none, ws, need, fake, nul) == 0
     assert L.rotattn_fp16_fwd(C.byref(s), fake, fake, fake, None, ws, need, fake, nul) == -6
+
+
+def test_noalloc_rejects_heads_beyond_the_scratch():
+    """rotattn_fp16_fwd_noalloc refuses a head whose staging exceeds the static
+    scratch before it looks anything up on a device (no GPU here)."""
+    L = R.lib()
+    fake = C.c_void_p(1 << 20)
+    big = R.make_shape(1, 1, (1, 600, 600), 128, (44, 42, 42))      # N_pad * D > 44.7 M values
+    assert R.validate(big) == 0
+    assert L.rotattn_fp16_fwd_noalloc(C.byref(big), fake, fake, fake, None, fake,
+                                      C.c_void_p(0)) == -8
+    assert L.rotattn_strerror(-8).decode() == R.STATUS[-8]
+    s = R.make_shape(1, 2, (2, 4, 4), 64, (24, 20, 20))
+    assert L.rotattn_fp16_fwd_noalloc(C.byref(s), fake, C.c_void_p(0), fake, None, fake,
+                                      C.c_void_p(0)) == -1
+    assert L.rotattn_fp16_fwd_noalloc(C.byref(s), fake, fake, fake, None,
+                                      C.c_void_p((1 << 20) + 2), C.c_void_p(0)) == -5
+    none = (C.c_uint8 * 2)(0, 0)
+    assert L.rotattn_fp16_fwd_noalloc(C.byref(s), fake, fake, fake, none, fake, C.c_void_p(0)) == 0

@@ -4,9 +4,18 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "rotattn_internal.h"
 
 using namespace rotattn;
+
+// Device scratch of rotattn_fp16_fwd_noalloc: staged Q', K' and V^T tiles of
+// as many heads as fit, a chunk of heads at a time.  Each GPU the library
+// runs on holds its own copy for the life of the process.  In host code the
+// name stands for a host-side shadow, never the device address: the address
+// is taken once per device with hipGetSymbolAddress and kept in g_scratch.
+static __device__ __align__(256) uint8_t scratch[ROTATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -67,6 +76,7 @@ const char* rotattn_strerror(int status) {
     case ROTATTN_E_ALIGN: return "device pointer not 16-byte aligned";
     case ROTATTN_E_HIP: return "HIP launch or runtime error";
     case ROTATTN_E_ARG: return "argument out of range";
+    case ROTATTN_E_SCRATCH: return "one head exceeds the library's static scratch";
     default: return "unknown status";
   }
 }
@@ -386,6 +396,24 @@ int stage_and_run_fp16(const rotattn_shape* s, const uint16_t* q, const uint16_t
   return launch_fp16_heads(s, q_pad, k_pad, v_t, run, bh0, nbh, o, os, stream);
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current); NULL if the lookup fails.
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev] = ptr;
+  }
+  return g_scratch[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -470,6 +498,43 @@ int rotattn_fp16_fwd_strided(const rotattn_shape* s, const uint16_t* q_rope,
   uint8_t* w = (uint8_t*)workspace;
   return stage_and_run_fp16(s, q_rope, k_rope, v, in, run, 0, BH, (uint16_t*)w,
                             (uint16_t*)(w + part), (uint16_t*)(w + 2 * part), o, os, stream);
+}
+
+int rotattn_fp16_fwd_noalloc(const rotattn_shape* s, const uint16_t* q_rope,
+                             const uint16_t* k_rope, const uint16_t* v,
+                             const uint8_t* head_select_host, uint16_t* o, hipStream_t stream) {
+  const int st = rotattn_validate(s);
+  if (st != ROTATTN_OK) return st;
+  if (!q_rope || !k_rope || !v || !o) return ROTATTN_E_NULL;
+  if (!aligned16(q_rope) || !aligned16(k_rope) || !aligned16(v) || !aligned16(o))
+    return ROTATTN_E_ALIGN;
+  // three staged arrays per head, each part 256-byte aligned
+  const size_t per_head = 3 * align_up(fp16_head_bytes(s));
+  const int chunk = (int)(ROTATTN_NOALLOC_SCRATCH_BYTES / per_head);
+  if (chunk < 1) return ROTATTN_E_SCRATCH;
+  const int BH = s->B * s->H;
+  int n_run = 0;
+  const HeadBits run = make_bits(head_select_host, BH, true, true, &n_run);
+  if (n_run == 0) return ROTATTN_OK;
+  uint8_t* base = (uint8_t*)scratch_on_current_device();
+  if (!base) return ROTATTN_E_HIP;
+  Strides in, os;
+  resolve_strides(s, nullptr, &in);
+  resolve_strides(s, nullptr, &os);
+  for (int bh0 = 0; bh0 < BH; bh0 += chunk) {
+    const int nbh = BH - bh0 < chunk ? BH - bh0 : chunk;
+    bool any = false;
+    for (int i = bh0; i < bh0 + nbh; ++i) any = any || run.test(i);
+    if (!any) continue;
+    // the staging of this chunk follows the previous chunk's attention on the
+    // same stream, so it never overwrites data still being read
+    const size_t part = align_up((size_t)nbh * fp16_head_bytes(s));
+    const int r = stage_and_run_fp16(s, q_rope, k_rope, v, in, run, bh0, nbh, (uint16_t*)base,
+                                     (uint16_t*)(base + part), (uint16_t*)(base + 2 * part), o,
+                                     os, stream);
+    if (r != ROTATTN_OK) return r;
+  }
+  return ROTATTN_OK;
 }
 
 size_t rotattn_workspace_bytes(const rotattn_shape* s) {

@@ -26,7 +26,8 @@ LAYOUTS = {"packed": LAYOUT_PACKED, "fp8": LAYOUT_FP8}
 STATUS = {0: "ok", -1: "null pointer argument", -2: "inconsistent shape",
           -3: "unsupported head dimension, RoPE split or head count", -4: "workspace too small",
           -5: "device pointer not 16-byte aligned", -6: "HIP launch or runtime error",
-          -7: "argument out of range"}
+          -7: "argument out of range", -8: "one head exceeds the library's static scratch"}
+NOALLOC_SCRATCH_BYTES = 256 << 20   # ROTATTN_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = sorted(["rotattn_validate", "rotattn_strerror", "rotattn_rope_tables_host",
                   "rotattn_rope_tables_phase_host",
@@ -35,6 +36,7 @@ EXPORTS = sorted(["rotattn_validate", "rotattn_strerror", "rotattn_rope_tables_h
                   "rotattn_prepare_qkv", "rotattn_int4_fwd", "rotattn_fp16_fwd",
                   "rotattn_fp16_fwd_strided", "rotattn_fp16_workspace_bytes",
                   "rotattn_fp16_fwd_prepared", "rotattn_fp16_fwd_prepared_strided",
+                  "rotattn_fp16_fwd_noalloc",
                   "rotattn_workspace_bytes", "rotattn_mixed_fwd", "rotattn_pcode_sweep",
                   "rotattn_pcode_eval", "rotattn_prepare_qkv_strided", "rotattn_int4_fwd_strided",
                   "rotattn_mixed_fwd_strided"])
@@ -109,6 +111,7 @@ def lib() -> C.CDLL:
                                                    C.c_size_t, P, C.POINTER(Strides), P]),
             "rotattn_fp16_workspace_bytes": (C.c_size_t, [S]),
             "rotattn_fp16_fwd_prepared": (C.c_int, [S, P, P, P, P]),
+            "rotattn_fp16_fwd_noalloc": (C.c_int, [S, P, P, P, P, P, P]),
             "rotattn_workspace_bytes": (C.c_size_t, [S]),
             "rotattn_mixed_fwd": (C.c_int, [S, P, P, P, C.POINTER(RopeRot), P, P, C.c_size_t, P, P]),
             "rotattn_pcode_sweep": (C.c_int, [C.c_int, C.c_uint32, C.c_uint32, P, C.c_uint32, P, P]),
@@ -310,6 +313,19 @@ def fp16_fwd_prepared(shape: Shape, prep: PreparedDevice, o, head_select=None,
     check(lib().rotattn_fp16_fwd_prepared_strided(C.byref(shape), C.byref(prep.struct), m, _ptr(o),
                                                   _strides_arg(strides_of(o)), _stream(stream)),
           "fp16_fwd_prepared")
+
+
+def fp16_fwd_noalloc(shape: Shape, q_rope, k_rope, v, o, head_select=None,
+                     stream=None) -> None:
+    """FP16 attention on contiguous caller tensors with the staging in the
+    library's static device scratch (no allocation; calls that overlap on one
+    GPU race)."""
+    keep, m = _mask_arg(head_select)
+    for t in (q_rope, k_rope, v, o):
+        if not t.is_contiguous():
+            raise ValueError("fp16_fwd_noalloc takes contiguous [B][H][N][D] tensors")
+    check(lib().rotattn_fp16_fwd_noalloc(C.byref(shape), _ptr(q_rope), _ptr(k_rope), _ptr(v), m,
+                                         _ptr(o), _stream(stream)), "fp16_fwd_noalloc")
 
 
 def fp16_workspace_bytes(shape: Shape) -> int:
