@@ -11,9 +11,10 @@ grid 21x45x80, N=75600, D=128, all heads INT4).  The metric is effective
 attention TOPS = 4*B*H*N^2*D / step time.
 
 Prints one JSON line.  Besides the contract fields it carries the roofline
-of the dominant kernel (the INT4 attention, timed with HIP events on the
-stream it runs on, with the VALU-busy share of the unit that bounds it), the
-same for the i8-MFMA implementation of that kernel, the per-kernel times, the
+of the dominant kernel (the INT4 attention on the FP6 layout, timed with HIP
+events on the stream it runs on, with the VALU-busy share of the unit that
+bounds it), the same for the FP8-layout and i8-MFMA implementations of that
+kernel, the per-kernel times, the
 Mixed workload (4 denoising steps, a fixed seeded quarter of the heads in
 FP16, fresh inputs per step), the 480p workload, a synthetic DiT block, and
 the CPU oracle timed on a bounded sample on this host's cores (cpu_baseline).
@@ -33,11 +34,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "effective attention TOPS at 1 MI355X + % of i8 MFMA peak, N=75600 D=128"
-PEAK_I8_TOPS = 5000.0        # MI355X dense int8 MFMA (5.0 POPS)
+PEAK_I8_TOPS = 5000.0        # MI355X dense int8 MFMA (5.0 POPS); dense fp8 is the same
+PEAK_FP6_TOPS = 10100.0      # MI355X dense fp6 MFMA (10.1 POPS)
 PEAK_F16_TFLOPS = 2500.0     # MI355X dense fp16 MFMA (2.5 PFLOPS)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E (8 TB/s)
-PMC_FILE = os.path.join(ROOT, "profiles", "int4_attn_f8_720p_pmc.txt")
-SQ_FILE = os.path.join(ROOT, "profiles", "int4_attn_f8_720p_sq_counters.txt")
+PMC_FILE = os.path.join(ROOT, "profiles", "int4_attn_fp6_720p_pmc.txt")
+SQ_FILE = os.path.join(ROOT, "profiles", "int4_attn_fp6_720p_sq_counters.txt")
 PROFILED_WORKLOAD = "720p"   # the workload both counter summaries were taken on
 KERNEL_SRC = os.path.join(ROOT, "video_diffusion_transformers_amd", "csrc", "int4_attn.hip")
 
@@ -105,8 +107,8 @@ def valu_busy_from_profile(workload: str):
 def prologue_bytes(BH: int, N: int, D: int):
     """Algorithmic HBM bytes of the prologue (per token and head: read Q, K, V
     fp16, write Q, K, V as INT4 codes, two per byte; block scales are
-    negligible) and the bytes its FP8-lane layout actually writes (one byte per
-    code)."""
+    negligible) and the bytes its FP6 layout actually writes (one byte per
+    code: 32 six-bit codes and 8 pad bytes per 32 bytes)."""
     algorithmic = BH * N * (3 * 2 * D + 3 * D // 2)
     layout = BH * N * (3 * 2 * D + 3 * D)
     return algorithmic, layout
@@ -152,7 +154,7 @@ def main():
     _, r32 = synth.rotation_matrices(cfg.split)
     rr = R.RopeRotDevice(shape, r32)
     mask = synth.fallback_mask(cfg)
-    prep = R.PreparedDevice(shape, with_rope=True)
+    prep = R.PreparedDevice(shape, with_rope=True, layout=R.LAYOUT_FP6)
     o = torch.empty((B, H, N, D), dtype=torch.float16, device="cuda")
     BH = B * H
     n_fb = int(mask.sum())
@@ -195,12 +197,13 @@ def main():
     k2_ms = float(k2.mean())
     achieved = int4_ops / (k2_ms * 1e-3) / 1e12 if n_int4 else 0.0
     traffic = traffic_from_profile(args.workload)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_I8_TOPS,
-                "unit": "TOP/s", "frac": round(achieved / PEAK_I8_TOPS, 4), "traffic": traffic,
-                "kernel": "k_int4_attn_f8<128>",
-                "operands": "INT4 codes as FP8 E4M3 (Q, K, V), P codes as FP6 E2M3 (code/2); "
-                            "fp32 accumulation exact on these integers; FP8 x FP6 runs at the "
-                            "FP8 rate, whose dense peak equals the i8 one",
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP6_TOPS,
+                "unit": "TOP/s", "frac": round(achieved / PEAK_FP6_TOPS, 4), "traffic": traffic,
+                "kernel": "k_int4_attn_f8<128, false, false, true> (FP6 layout)",
+                "operands": "INT4 codes as FP6 E2M3 (Q, K, V) and P codes as FP6 E2M3 "
+                            "(code/2), both MFMA operands FP6; fp32 accumulation exact on these "
+                            "integers; priced against the dense fp6 peak",
+                "frac_of_i8_fp8_peak": round(achieved / PEAK_I8_TOPS, 4),
                 "algorithmic_ops_per_launch": int4_ops,
                 "limiter": "valu", "limiter_busy": valu_busy_from_profile(args.workload)}
     k1_ms = float(k1.mean())
@@ -217,9 +220,26 @@ def main():
         "fp16_attn_ms": round(float(k3.mean()), 4),
         "event_step_ms": round(float(tot.mean()), 4),
     }
-    roofline_i8 = None
+    roofline_i8 = roofline_f8 = None
 
     if not args.no_extras:
+        # the same INT4 attention on the FP8 layout: Q, K, V codes as E4M3, P as
+        # FP6 (FP8 x FP6 runs at the FP8 rate)
+        prep_8 = R.PreparedDevice(shape, with_rope=n_fb > 0, layout=R.LAYOUT_FP8)
+        R.prepare_qkv(shape, qd, kd, vd, rr, prep_8, mask)
+        f8_ms = time_calls(lambda: R.int4_fwd(shape, prep_8, o, mask=mask), 3)
+        del prep_8
+        f8_ach = int4_ops / (f8_ms * 1e-3) / 1e12 if n_int4 else 0.0
+        roofline_f8 = {"bound": "mfma", "achieved": round(f8_ach, 2), "peak": PEAK_I8_TOPS,
+                       "unit": "TOP/s", "frac": round(f8_ach / PEAK_I8_TOPS, 4), "traffic": None,
+                       "kernel": "k_int4_attn_f8<128, false, false, false> (FP8 layout)",
+                       "operands": "INT4 codes as FP8 E4M3 (Q, K, V), P codes as FP6 E2M3 "
+                                   "(code/2); FP8 x FP6 runs at the FP8 rate, whose dense peak "
+                                   "equals the i8 one",
+                       "ms": round(f8_ms, 4), "algorithmic_ops_per_launch": int4_ops}
+        kernels["int4_attn_fp8_layout_ms"] = round(f8_ms, 4)
+        print(f"[bench] FP8-layout kernel {f8_ms:.3f} ms", file=sys.stderr, flush=True)
+
         # the same INT4 attention on the nibble-packed layout: int8 lanes on the
         # i8 MFMA with int32 accumulation (fallback heads, if any, need the
         # fp16 RoPE'd buffers as well)
@@ -316,7 +336,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8",
+        "dtype": "fp6",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: B={B} H={H} grid {'x'.join(map(str, cfg.grid))} "
                                f"N={N} D={D} split {'/'.join(map(str, cfg.split))}, "
@@ -328,6 +348,7 @@ def main():
                    "parallelism": "single GPU"},
         "percent_i8_peak_step": round(100 * value / PEAK_I8_TOPS, 2),
         "roofline": roofline,
+        "roofline_fp8_layout_kernel": roofline_f8,
         "roofline_i8_mfma_kernel": roofline_i8,
         "kernels": kernels,
         "mixed": mixed,

@@ -116,10 +116,18 @@ typedef struct rotattn_strides {
  *      the integer (every integer in [-15, 15] is exact in E4M3); the attention
  *      kernel multiplies them on the f8f6f4 MFMA with fp32 accumulation.  The
  *      integer products and sums are the same exact integers as on i8 MFMA.
+ *  ROTATTN_LAYOUT_FP6: the codes as FP6 E2M3 values (sign, 2 exponent bits
+ *      with bias 1, 3 mantissa bits: every integer in [-7, 7] is exact); the
+ *      kernel multiplies them on the f8f6f4 MFMA with both operands FP6, at
+ *      twice the FP8 rate, with the same exact integer results.  Byte
+ *      positions as in the FP8 layout, in groups of 32 codes: a group's 32
+ *      bytes hold its 32 six-bit fields packed little-endian (field k in bits
+ *      6k..6k+5 of bytes 0..23) and 8 zero bytes.
  */
 typedef enum rotattn_layout {
   ROTATTN_LAYOUT_PACKED = 0,
-  ROTATTN_LAYOUT_FP8 = 1
+  ROTATTN_LAYOUT_FP8 = 1,
+  ROTATTN_LAYOUT_FP6 = 2
 } rotattn_layout;
 
 /*
@@ -131,6 +139,8 @@ typedef enum rotattn_layout {
  *          channels 8g..8g+7 occupies 4 bytes; byte i holds channel 8g+i in
  *          its low nibble and 8g+4+i in its high nibble.
  *          FP8: [B*H][N_pad][D] bytes, E4M3 of the code, channel order.
+ *          FP6: [B*H][N_pad][D] bytes, group g of a row = channels
+ *          32g..32g+31, channel 32g+k in field k.
  *  v4:     V codes per 128-token block, transposed (channel-major).
  *          PACKED: [B*H][NB][D][64]: row d holds the 128 keys of the block
  *          packed along keys as above (byte i of group g = keys 8g+i, 8g+4+i).
@@ -138,6 +148,9 @@ typedef enum rotattn_layout {
  *          codes, each 64-key half in the operand order of the P.V product
  *          (P as FP6): byte 32h+j (h in {0,1}, j < 32) is key
  *          32h + 8(j%16/4) + 4(j/16) + j%4.
+ *          FP6: [B*H][NB][D][128]: row d in four groups g = 2c+h (c, h in
+ *          {0,1}); field k of group g is key 64c + 32(k/16) + 8(k%16/4) +
+ *          4h + k%4.
  *  rot64:  library scratch, 3*64*64 doubles: the rotation in fp64, refilled
  *          by every rotattn_prepare_qkv call.
  *  q_scale_l2, k_scale, v_scale: [B*H][NB] fp32 block scales (amax/7).
@@ -219,7 +232,7 @@ int rotattn_pcode_thresholds_host(float tau[15]);
 float rotattn_kappa_host(int32_t D);
 
 /* Bytes for the prepared buffers rotattn_prepare_qkv writes in the production
- * form: FP8 layout with the fp16 fallback buffers (q_rope, k_rope, v_t); 0 for
+ * form: FP6 layout with the fp16 fallback buffers (q_rope, k_rope, v_t); 0 for
  * an invalid shape.  Equal to rotattn_workspace_bytes. */
 size_t rotattn_prepared_bytes(const rotattn_shape* s);
 
@@ -260,7 +273,7 @@ int rotattn_prepare_qkv_strided(const rotattn_shape* s, const uint16_t* q,
 /*
  * INT4 attention over the heads with fallback_mask_host[...] == 0 (all heads
  * when NULL): I = q4.k4^T (i8 MFMA for the PACKED layout, f8f6f4 MFMA for
- * FP8), one-pass online softmax over 128-key tiles in the log2 domain, P codes
+ * FP8 and FP6), one-pass online softmax over 128-key tiles in the log2 domain, P codes
  * rne(15*2^(s-m)) against the running max, PV = codes.v4 on the same MFMA
  * kind, O = acc / l written as fp16 into o [B][H][N][D].
  * dbg != NULL additionally runs one instrumented work-group for (dbg->b,
@@ -275,7 +288,7 @@ int rotattn_int4_fwd(const rotattn_shape* s, const rotattn_prepared* p,
  * l as the sum of the unquantized 2^x; ROTATTN_NORM_CODES as the sum of the
  * P codes / 15, so that O is the quantized P's weighted mean of V (the other
  * reading of the quantized FlashAttention on the RotateAttention page,
- * Abstract; FP8 layout only, ROTATTN_E_UNSUPPORTED for PACKED).
+ * Abstract; FP8 and FP6 layouts only, ROTATTN_E_UNSUPPORTED for PACKED).
  */
 typedef enum rotattn_normalizer {
   ROTATTN_NORM_EXP = 0,
@@ -358,12 +371,12 @@ int rotattn_fp16_fwd_prepared_strided(const rotattn_shape* s, const rotattn_prep
                                       const uint8_t* head_select_host, uint16_t* o,
                                       const rotattn_strides* o_strides, hipStream_t stream);
 
-/* Workspace bytes for rotattn_mixed_fwd (a FP8-layout rotattn_prepared with
+/* Workspace bytes for rotattn_mixed_fwd (an FP6-layout rotattn_prepared with
  * the fp16 fallback buffers). */
 size_t rotattn_workspace_bytes(const rotattn_shape* s);
 
 /*
- * Whole forward: prepare (FP8 layout), INT4 attention for mask == 0 heads,
+ * Whole forward: prepare (FP6 layout), INT4 attention for mask == 0 heads,
  * FP16 attention for mask != 0 heads, all on `stream`, writing every head of o.
  * Every argument of the three steps is checked before the first launch.
  */

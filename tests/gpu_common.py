@@ -58,6 +58,65 @@ def fp8_vt_blocks(codes: np.ndarray, N_pad: int) -> np.ndarray:
     return np.stack(out)
 
 
+def _e2m3_value(bits: int) -> float:
+    """Value of a 6-bit FP6 E2M3 pattern: sign bit 5, exponent bits 4-3 (bias
+    1, 0 = subnormal), mantissa bits 2-0."""
+    s, e, m = bits >> 5, (bits >> 3) & 3, bits & 7
+    mag = m / 8 if e == 0 else 2.0 ** (e - 1) * (1 + m / 8)
+    return -mag if s else mag
+
+
+# code -> E2M3 bits, found by search over the 64 patterns (+0 for code 0)
+E2M3 = {c: min(b for b in range(64) if _e2m3_value(b) == c) for c in range(-7, 8)}
+
+
+def _pack_fields(fields: np.ndarray) -> np.ndarray:
+    """[..., 32] six-bit fields -> [..., 32] bytes: field k in bits 6k..6k+5 of
+    the first 24 bytes (little-endian), then 8 zero bytes."""
+    bits = ((fields[..., :, None].astype(np.uint8) >> np.arange(6, dtype=np.uint8)) & 1)
+    bits = bits.reshape(*fields.shape[:-1], 192)
+    packed = np.packbits(bits, axis=-1, bitorder="little")          # [..., 24]
+    pad = np.zeros((*fields.shape[:-1], 8), np.uint8)
+    return np.concatenate([packed, pad], axis=-1)
+
+
+def fp6_rows(codes: np.ndarray) -> np.ndarray:
+    """Q/K codes [n, D] -> the FP6 layout's rows [n, D]: per 32-channel group,
+    channel 32g + k in field k."""
+    n, D = codes.shape
+    lut = np.array([E2M3[c] for c in range(-7, 8)], np.uint8)
+    f = lut[codes.astype(np.int16) + 7].reshape(n, D // 32, 32)
+    return _pack_fields(f).reshape(n, D)
+
+
+def fp6_vt_blocks(codes: np.ndarray, N_pad: int) -> np.ndarray:
+    """V codes [N, D] -> [NB, D, 128] FP6 layout: per 128-token block, row d in
+    groups g = 2c + h whose field k holds key 64c + 32(k/16) + 8((k%16)/4) +
+    4h + k%4."""
+    N, D = codes.shape
+    full = np.zeros((N_pad, D), np.int16)
+    full[:N] = codes
+    lut = np.array([E2M3[c] for c in range(-7, 8)], np.uint8)
+    keys = np.array([[64 * (g // 2) + 32 * (k // 16) + 8 * ((k % 16) // 4) + 4 * (g % 2) + k % 4
+                      for k in range(32)] for g in range(4)])
+    assert sorted(keys.ravel()) == list(range(128))
+    out = []
+    for b in range(N_pad // 128):
+        blk = full[b * 128:(b + 1) * 128]                # [128 keys, D]
+        f = lut[blk[keys] + 7]                           # [4, 32, D]
+        out.append(_pack_fields(f.transpose(2, 0, 1)).reshape(D, 128))
+    return np.stack(out)
+
+
+def code_rows(codes: np.ndarray, layout: str) -> np.ndarray:
+    """Q/K codes in the bytes of a prepared layout ("packed", "fp8", "fp6")."""
+    return {"packed": pack_rows, "fp8": fp8_bytes, "fp6": fp6_rows}[layout](codes)
+
+
+def v_blocks(codes: np.ndarray, N_pad: int, layout: str) -> np.ndarray:
+    return {"packed": pack_vt_blocks, "fp8": fp8_vt_blocks, "fp6": fp6_vt_blocks}[layout](codes, N_pad)
+
+
 def fp16_vt_tiles(v: np.ndarray, N_pad: int) -> np.ndarray:
     """fp16 V [N, D] -> [N_pad/64, D, 64] V^T tiles in the fp16 P.V operand
     order: position 32s + 4c + i holds key 32s + 4c' + i, c' = c with bits 0
@@ -88,7 +147,7 @@ def pack_vt_blocks(codes: np.ndarray, N_pad: int) -> np.ndarray:
 class Run:
     """One config on the device: inputs, RoPE/rotation, prepared buffers."""
 
-    def __init__(self, cfg: synth.Config, step: int = 0, layout: int = 1, merged: bool = False):
+    def __init__(self, cfg: synth.Config, step: int = 0, layout: int = 2, merged: bool = False):
         """merged: the rotation is merged into the RoPE tables (seeded pair
         phases, no dense rotation matrices)."""
         torch = torch_cuda()
@@ -123,8 +182,9 @@ class Run:
         torch.cuda.synchronize()
         BH, D, NB, N = self.cfg.BH, self.cfg.D, self.NB, self.cfg.N
         p = self.prep
-        w = D if self.layout == self.R.LAYOUT_FP8 else D // 2      # bytes per code row
-        vw = 128 if self.layout == self.R.LAYOUT_FP8 else 64
+        byte = self.layout in (self.R.LAYOUT_FP8, self.R.LAYOUT_FP6)  # one byte per code
+        w = D if byte else D // 2      # bytes per code row
+        vw = 128 if byte else 64
         out = {
             "q4": p.view("q4", torch.uint8, BH * self.N_pad * w).cpu().numpy().reshape(BH, self.N_pad, w),
             "k4": p.view("k4", torch.uint8, BH * self.N_pad * w).cpu().numpy().reshape(BH, self.N_pad, w),

@@ -63,7 +63,7 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert L.rotattn_pcode_sweep(1, 0, 0, nul, 0, nul, nul) == -1
     t = (C.c_uint32 * 4)()
     assert L.rotattn_pcode_sweep(1, 0x7B000000, 0x01000000, t, 1, t, nul) == -7
-    assert L.rotattn_pcode_sweep(2, 0, 16, t, 1, t, nul) == -7          # unknown layout
+    assert L.rotattn_pcode_sweep(3, 0, 16, t, 1, t, nul) == -7          # unknown layout
     assert L.rotattn_pcode_eval(1, t, 1000, C.c_float(1.0), C.c_float(0.0), t, nul) == -7
     # an unaligned workspace is refused by the carve, and so is an unknown layout
     p = R.Prepared()
@@ -75,7 +75,8 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert L.rotattn_prepared_bytes(C.byref(s)) == L.rotattn_workspace_bytes(C.byref(s))
 
 
-@pytest.mark.parametrize("layout,code_bytes", [(R.LAYOUT_PACKED, 64), (R.LAYOUT_FP8, 128)])
+@pytest.mark.parametrize("layout,code_bytes", [(R.LAYOUT_PACKED, 64), (R.LAYOUT_FP8, 128),
+                                              (R.LAYOUT_FP6, 128)])
 def test_prepared_layout_sizes(layout, code_bytes):
     s = R.shape_of(synth.CONFIGS["720p"])
     NB = R.n_blocks(s)

@@ -12,18 +12,18 @@ import pytest
 import oracle as O
 from video_diffusion_transformers_amd import synth
 
-from gpu_common import (Run, check_out, fp8_bytes, fp8_vt_blocks, fp16_vt_tiles, pack_rows,
-                        pack_vt_blocks, pool_reference, torch_cuda)
+from gpu_common import (Run, check_out, code_rows, fp16_vt_tiles, pool_reference, torch_cuda,
+                        v_blocks)
 
 pytestmark = pytest.mark.gpu
 
 _RUNS = {}
 
 
-LAYOUTS = {"packed": 0, "fp8": 1}
+LAYOUTS = {"packed": 0, "fp8": 1, "fp6": 2}
 
 
-def get_run(name, step=0, layout="fp8", merged=False):
+def get_run(name, step=0, layout="fp6", merged=False):
     """Workloads stay resident for the whole module (tens of GB at most); the
     denoising steps of the mixed workload, and the merged-rotation variant of
     a workload, replace one another."""
@@ -135,19 +135,17 @@ def _check_prologue_heads(run, heads, layout):
             v = run.host[2].reshape(run.cfg.BH, N, run.cfg.D)[bh]
             assert np.array_equal(g["v_t"][bh], fp16_vt_tiles(v, run.N_pad)), (name, bh, "v_t")
             continue
-        f8 = layout == "fp8"
         for t in ("q", "k"):
-            codes = p[f"{t}_codes"]
-            want = np.zeros((run.N_pad, run.cfg.D if f8 else run.cfg.D // 2), np.uint8)
-            want[:run.cfg.N] = fp8_bytes(codes) if f8 else pack_rows(codes)
+            rows = code_rows(p[f"{t}_codes"], layout)
+            want = np.zeros((run.N_pad, rows.shape[1]), np.uint8)
+            want[:run.cfg.N] = rows
             assert np.array_equal(g[f"{t}4"][bh], want), (name, bh, t)
-        vt = fp8_vt_blocks if f8 else pack_vt_blocks
-        assert np.array_equal(g["v4"][bh], vt(p["v_codes"], run.N_pad)), (name, bh)
+        assert np.array_equal(g["v4"][bh], v_blocks(p["v_codes"], run.N_pad, layout)), (name, bh)
         for f in ("q_scale_l2", "k_scale", "v_scale"):
             assert np.array_equal(g[f][bh].view(np.uint32), p[f].view(np.uint32)), (name, bh, f)
 
 
-@pytest.mark.parametrize("layout", ["packed", "fp8"])
+@pytest.mark.parametrize("layout", ["packed", "fp8", "fp6"])
 @pytest.mark.parametrize("name", ["tiny", "small", "480p", "720p"])
 def test_prologue_bit_exact(name, layout):
     run = get_run(name, layout=layout)
@@ -155,7 +153,7 @@ def test_prologue_bit_exact(name, layout):
     _check_prologue_heads(run, HEADS[name], layout)
 
 
-@pytest.mark.parametrize("layout", ["packed", "fp8"])
+@pytest.mark.parametrize("layout", ["packed", "fp8", "fp6"])
 def test_prologue_fallback_heads_d128_bit_exact(layout):
     """D = 128 with fallback and INT4 heads in one launch, a ragged last block
     (N = 306): RoPE'd fp16 Q/K and the V^T tiles of the fallback heads, codes
@@ -184,7 +182,7 @@ def _debug_buffers(run):
     return bufs, R
 
 
-@pytest.mark.parametrize("layout", ["packed", "fp8"])
+@pytest.mark.parametrize("layout", ["packed", "fp8", "fp6"])
 @pytest.mark.parametrize("name,bh,qb", [("tiny", 0, 0), ("small", 3, 5), ("small", 6, 7),
                                         ("480p", 23, 255), ("480p", 0, 17), ("720p", 5, 590),
                                         ("720p", 39, 300)])
@@ -222,7 +220,7 @@ def test_int4_integer_dumps_bit_exact(name, bh, qb, layout):
     assert np.all(np.abs(l_fin - rec["l_final"]) <= rtol * rec["l_final"])
 
 
-@pytest.mark.parametrize("layout", ["packed", "fp8"])
+@pytest.mark.parametrize("layout", ["packed", "fp8", "fp6"])
 @pytest.mark.parametrize("name", ["tiny", "small", "480p", "720p"])
 def test_int4_output_within_tolerance(name, layout):
     """Every INT4 head against the oracle: every row at Tiny and Small, the
@@ -246,7 +244,7 @@ def test_int4_output_within_tolerance(name, layout):
 
 # ------------------------------------------------------------------ rotation merged into RoPE
 
-@pytest.mark.parametrize("layout", ["packed", "fp8"])
+@pytest.mark.parametrize("layout", ["packed", "fp8", "fp6"])
 @pytest.mark.parametrize("name", ["tiny", "small", "720p"])
 def test_merged_rotation_prologue_and_output(name, layout):
     """Phase tables and no dense rotation (the prologue's RoPE-only path):
@@ -256,7 +254,6 @@ def test_merged_rotation_prologue_and_output(name, layout):
     run = get_run(name, layout=layout, merged=True)
     run.prepare()
     g = run.gpu_prepared()
-    f8 = layout == "fp8"
     N = run.cfg.N
     for bh in HEADS[name]:
         fb = bool(run.mask[bh])
@@ -266,8 +263,9 @@ def test_merged_rotation_prologue_and_output(name, layout):
                 assert np.array_equal(g[f"{t}_rope"][bh][:N], p[f"{t}_rope"].view(np.uint16))
             continue
         for t in ("q", "k"):
-            want = np.zeros((run.N_pad, run.cfg.D if f8 else run.cfg.D // 2), np.uint8)
-            want[:N] = fp8_bytes(p[f"{t}_codes"]) if f8 else pack_rows(p[f"{t}_codes"])
+            rows = code_rows(p[f"{t}_codes"], layout)
+            want = np.zeros((run.N_pad, rows.shape[1]), np.uint8)
+            want[:N] = rows
             assert np.array_equal(g[f"{t}4"][bh], want), (name, bh, t)
         for f in ("q_scale_l2", "k_scale", "v_scale"):
             assert np.array_equal(g[f][bh].view(np.uint32), p[f].view(np.uint32)), (name, bh, f)
@@ -552,7 +550,7 @@ def test_ragged_shapes_and_masks(bhg, D, split):
         check_out(og[bh], ref, f"{cfg.name} head {bh}")
 
 
-@pytest.mark.parametrize("layout", ["packed", "fp8"])
+@pytest.mark.parametrize("layout", ["packed", "fp8", "fp6"])
 def test_diffuse_inputs_use_every_code(layout):
     """Diffuse logits (every P code occurs, many near-ties) on the small shape."""
     torch = torch_cuda()
@@ -585,9 +583,9 @@ def test_literal_recipe_parity(name):
     of every head (every row at Small, 512 seeded rows per head at 480p)."""
     torch = torch_cuda()
     from video_diffusion_transformers_amd import rotattn as R
-    run = Run(synth.CONFIGS[name])
+    run = Run(synth.CONFIGS[name], layout=LAYOUTS["fp6"])
     run.prepare()
-    _check_prologue_heads(run, HEADS[name], "fp8")
+    _check_prologue_heads(run, HEADS[name], "fp6")
     o = run.empty_out()
     R.int4_fwd(run.shape, run.prep, o, mask=run.mask)
     torch.cuda.synchronize()
@@ -660,7 +658,7 @@ def _check_all_heads(run, mask, what):
     return og
 
 
-@pytest.mark.parametrize("layout", ["fp8", "packed"])
+@pytest.mark.parametrize("layout", ["mixed", "packed", "fp8", "fp6"])
 def test_degenerate_inputs(layout):
     """Zero Q and K (every score 0: all codes 15, uniform weights), zero V
     (block scale 0: the output is exactly 0), fp16 extremes (logits of ~10^10
@@ -687,8 +685,8 @@ def test_degenerate_inputs(layout):
     run = _run_with(cfg, q, k, v)
     mask = np.zeros(cfg.BH, np.uint8)
     mask[5] = mask[6] = 1
-    if layout == "packed":
-        prep = R.PreparedDevice(run.shape, with_rope=True, layout=R.LAYOUT_PACKED)
+    if layout != "mixed":
+        prep = R.PreparedDevice(run.shape, with_rope=True, layout=LAYOUTS[layout])
         R.prepare_qkv(run.shape, run.q, run.k, run.v, run.rr, prep, mask)
         o = run.empty_out()
         R.int4_fwd(run.shape, prep, o, mask=mask)
@@ -696,9 +694,9 @@ def test_degenerate_inputs(layout):
         og = o.reshape(cfg.BH, cfg.N, cfg.D).cpu().numpy()
         rows = np.arange(cfg.N)
         for bh in range(5):
-            check_out(og[bh], run.oracle_int4(bh, rows)[0], f"degenerate packed head {bh}")
-        return
-    og = _check_all_heads(run, mask, "degenerate")
+            check_out(og[bh], run.oracle_int4(bh, rows)[0], f"degenerate {layout} head {bh}")
+    else:
+        og = _check_all_heads(run, mask, "degenerate")
     assert not og[1].any()                                     # exactly zero
     vm = v[0, 0].astype(np.float64).mean(axis=0)               # uniform weights: mean of V
     assert np.abs(og[0].astype(np.float64) - vm[None, :]).max() <= 0.05 * np.abs(v[0, 0]).max()

@@ -291,14 +291,18 @@ __device__ __forceinline__ v8i pack_p_fp6(const float (&a)[16], const float (&b)
   return v8i{r[0], r[1], r[2], r[3], r[4], r[5], 0, 0};
 }
 
-// S^T tile MFMA: K (FP8) x Q (FP8).
-__device__ __forceinline__ v16f mfma_f8(const v8i& a, const v8i& b, const v16f& c) {
-  // format 0/0: both operands FP8 E4M3; zero scales select the unscaled MFMA
+// S^T tile MFMA: K x Q, both FP8 E4M3 (format 0) or both FP6 E2M3 (format 2,
+// six dwords of each operand read); zero scales select the unscaled MFMA.
+template <bool F6>
+__device__ __forceinline__ v16f mfma_qk(const v8i& a, const v8i& b, const v16f& c) {
+  if (F6) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 2, 0, 0, 0, 0);
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// V^T P^T MFMA: A FP8 E4M3 (format 0), B FP6 E2M3 (format 2, six dwords read).
-__device__ __forceinline__ v16f mfma_f8_f6(const v8i& a, const v8i& b, const v16f& c) {
+// V^T P^T MFMA: A (V^T) FP8 E4M3 or FP6 E2M3, B (P^T) FP6 E2M3.
+template <bool F6>
+__device__ __forceinline__ v16f mfma_pv(const v8i& a, const v8i& b, const v16f& c) {
+  if (F6) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 2, 0, 0, 0, 0);
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 2, 0, 0, 0, 0);
 }
 
@@ -557,13 +561,18 @@ hipError_t launch_int4(int D, int BH, const Int4Args& a, const Int4Debug* dbg, h
 
 // ------------------------------------------------------------- fp8 kernel
 //
-// The INT4 attention on the FP8-lane layout (codes as E4M3 bytes):
+// The INT4 attention on the FP8-lane layout (codes as E4M3 bytes) or on the
+// FP6 layout (codes as E2M3 fields: the integers -7..7 are exact there too):
 //   S^T  = K_t Q^T on v_mfma_f32_32x32x64_f8f6f4: the fp32 result is I exactly
 //          (integer products and partial sums below 2^24)
 //   O^T  accumulates V_t^T (P/2)^T straight into fp32 on the same MFMA (V^T
-//        FP8, P as FP6 E2M3 code/2), kept in units of the current V block
-//        scale u: O <- beta O + V^T (P/2)^T with beta = 2^(m-m') u_prev / u.
+//        FP8 or FP6, P as FP6 E2M3 code/2), kept in units of the current V
+//        block scale u: O <- beta O + V^T (P/2)^T with beta = 2^(m-m') u_prev / u.
 //        The final O is 2 O u / l.
+// With both operands FP6 the MFMA runs at twice the FP8 rate.  The FP6 layout
+// keeps the FP8 layout's byte positions: each 32-code operand group is 24
+// bytes of fields and 8 bytes of padding, so the tiles, their swizzle and the
+// operand offsets are the same, and an operand read is 24 bytes, not 32.
 // No unpacking (the prologue stores operand-ready bytes) and no int->float
 // conversions; per score the VALU work is the fused argument, exp2, the l
 // sum, rndne and the guard, plus 1/32 of a packing instruction (32 codes to
@@ -574,7 +583,7 @@ hipError_t launch_int4(int D, int BH, const Int4Args& a, const Int4Debug* dbg, h
 // overlaps the other's MFMAs, which run at raised wave priority.  Per tile:
 // S, softmax, then the K/V tiles of t+1 are requested straight into the other
 // LDS buffers (global_load_lds) while P.V of tile t runs; one barrier per tile.
-template <int D, bool DBG, bool CS>
+template <int D, bool DBG, bool CS, bool F6>
 struct Int4F8Kernel {
   static constexpr int KS = D / 64;        // k-steps of 64 channels for QK^T
   static constexpr int DB = D / 32;        // 32-channel blocks of O^T
@@ -595,7 +604,14 @@ struct Int4F8Kernel {
   __device__ __forceinline__ static int vswz(int row) { return (row >> 1) & 7; }
 
   __device__ __forceinline__ static v8i ld32(const uint8_t* p) {
-    const uint4 a = *(const uint4*)p, b = *(const uint4*)(p + 16);
+    const uint4 a = *(const uint4*)p;
+    if (F6) {
+      const uint2 b = *(const uint2*)(p + 16);
+      // dwords 6 and 7 are not read by an FP6 operand: left undefined (no moves)
+      const int u = __builtin_nondeterministic_value(0);
+      return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, u, u};
+    }
+    const uint4 b = *(const uint4*)(p + 16);
     return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
   }
   // 32 bytes of a swizzled row: logical chunks c0, c0 + 1
@@ -612,6 +628,13 @@ struct Int4F8Kernel {
   // recomputed (3 VALU) instead of being held in registers across the loop.
   __device__ __forceinline__ static v8i ld32x(const uint8_t* tile, uint32_t x, int k) {
     const uint4 a = *(const uint4*)(tile + (x ^ (64u * k)));
+    if (F6) {
+      // a whole 16-byte read (fields 16..23 and the pad): 8-byte reads get
+      // paired across subtiles by the compiler and then moved into place
+      v4i b = *(const v4i*)(tile + (x ^ (64u * k + 16u)));
+      asm volatile("" : "+v"(b));
+      return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, b[0], b[1], b[2], b[3]};
+    }
     const uint4 b = *(const uint4*)(tile + (x ^ (64u * k + 16u)));
     return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
   }
@@ -627,7 +650,7 @@ struct Int4F8Kernel {
       S[sub] = v16f{0.0f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        S[sub] = mfma_f8(ld32x(sk + 32 * sub * D, x, ks), qf[ks], S[sub]);
+        S[sub] = mfma_qk<F6>(ld32x(sk + 32 * sub * D, x, ks), qf[ks], S[sub]);
     }
   }
 
@@ -645,7 +668,7 @@ struct Int4F8Kernel {
         v16f pvt = v16f{0.0f};
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          pvt = mfma_f8_f6(ld32s(sv + row * kBlock, 4 * c + 2 * hh, vswz(row)), P[c], pvt);
+          pvt = mfma_pv<F6>(ld32s(sv + row * kBlock, 4 * c + 2 * hh, vswz(row)), P[c], pvt);
         const int q = 32 * w + col;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -656,7 +679,7 @@ struct Int4F8Kernel {
       } else {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          O[db] = mfma_f8_f6(ld32x(sv + 32 * db * kBlock, xv, c), P[c], O[db]);
+          O[db] = mfma_pv<F6>(ld32x(sv + 32 * db * kBlock, xv, c), P[c], O[db]);
       }
     }
   }
@@ -876,26 +899,37 @@ struct Int4F8Kernel {
   }
 };
 
-template <int D, bool DBG, bool CS>
+template <int D, bool DBG, bool CS, bool F6>
 __global__ __launch_bounds__(256, 2) void k_int4_attn_f8(Int4Args a, Int4Debug dbg) {
-  Int4F8Kernel<D, DBG, CS>::run(a, dbg);
+  Int4F8Kernel<D, DBG, CS, F6>::run(a, dbg);
 }
 
-template <int D, bool CS>
+template <int D, bool CS, bool F6>
 static void launch_int4_f8_t(int BH, const Int4Args& a, const Int4Debug* dbg, hipStream_t st) {
   if (dbg == nullptr) {
     Int4Debug none{};
-    hipLaunchKernelGGL((k_int4_attn_f8<D, false, CS>), dim3(a.NB, BH), dim3(256), 0, st, a, none);
+    hipLaunchKernelGGL((k_int4_attn_f8<D, false, CS, F6>), dim3(a.NB, BH), dim3(256), 0, st, a,
+                       none);
   } else {
-    hipLaunchKernelGGL((k_int4_attn_f8<D, true, CS>), dim3(1), dim3(256), 0, st, a, *dbg);
+    hipLaunchKernelGGL((k_int4_attn_f8<D, true, CS, F6>), dim3(1), dim3(256), 0, st, a, *dbg);
   }
+}
+
+template <int D>
+static void launch_int4_f8_d(int BH, const Int4Args& a, const Int4Debug* dbg, hipStream_t st) {
+  if (a.f6)
+    a.code_sum ? launch_int4_f8_t<D, true, true>(BH, a, dbg, st)
+               : launch_int4_f8_t<D, false, true>(BH, a, dbg, st);
+  else
+    a.code_sum ? launch_int4_f8_t<D, true, false>(BH, a, dbg, st)
+               : launch_int4_f8_t<D, false, false>(BH, a, dbg, st);
 }
 
 hipError_t launch_int4_f8(int D, int BH, const Int4Args& a, const Int4Debug* dbg, hipStream_t st) {
   if (D == 128)
-    a.code_sum ? launch_int4_f8_t<128, true>(BH, a, dbg, st) : launch_int4_f8_t<128, false>(BH, a, dbg, st);
+    launch_int4_f8_d<128>(BH, a, dbg, st);
   else
-    a.code_sum ? launch_int4_f8_t<64, true>(BH, a, dbg, st) : launch_int4_f8_t<64, false>(BH, a, dbg, st);
+    launch_int4_f8_d<64>(BH, a, dbg, st);
   return hipGetLastError();
 }
 

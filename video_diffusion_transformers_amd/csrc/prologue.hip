@@ -428,6 +428,77 @@ __device__ __forceinline__ void store_v_codes_f8(const int8_t* codesT, uint8_t* 
   }
 }
 
+// FP6 E2M3 fields of four int8 codes in [-7, 7], one code per byte in and one
+// field per byte out: sign in bit 5, and the magnitudes 0..7 are exact E2M3
+// values (exponent bias 1): 0, 1.0, 2.0, 1.5 x 2, 4.0, 1.25 x 4, 1.5 x 4,
+// 1.75 x 4 have the bits 0, 8, 16, 20, 24, 26, 28, 30, looked up per byte
+// with v_perm_b32 (selector bytes 0..3 pick from the low table dword, 4..7
+// from the high one).
+__device__ __forceinline__ uint32_t e2m3_fields4(uint32_t c) {
+  const uint32_t neg = (c >> 7) & 0x01010101u;
+  const uint32_t flip = (neg << 7) - neg;                         // 0x7f in negative bytes
+  const uint32_t mag = ((c ^ flip) + neg) & 0x07070707u;         // |c| per byte
+  return __builtin_amdgcn_perm(0x1e1c1a18u, 0x14100800u, mag) | (neg << 5);
+}
+
+// 32 fields (one per byte of f[0..7], field 4i + j in byte j of f[i]) packed
+// six bits each, field k at bits 6k..6k+5 of the 192-bit little-endian word
+// out[0..5]: the FP6 operand of one lane half of a 32x32x64 f8f6f4 MFMA.
+__device__ __forceinline__ void pack_fields32(const uint32_t (&f)[8], uint32_t (&out)[6]) {
+  uint32_t w[8];   // 24 bits: four fields
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t x = f[i];
+    w[i] = (x & 0x3fu) | ((x >> 2) & 0xfc0u) | ((x >> 4) & 0x3f000u) | ((x >> 6) & 0xfc0000u);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    out[3 * h] = w[4 * h] | (w[4 * h + 1] << 24);
+    out[3 * h + 1] = (w[4 * h + 1] >> 8) | (w[4 * h + 2] << 16);
+    out[3 * h + 2] = (w[4 * h + 2] >> 16) | (w[4 * h + 3] << 8);
+  }
+}
+
+// FP6 layout: Q/K int8 codes (LDS, [token][channel]) -> rows [128][D], each
+// 32-channel group in 32 bytes: channel 32g + k in field k of the group's 24
+// FP6 bytes, then 8 zero bytes.
+template <int D>
+__device__ __forceinline__ void store_qk_codes_f6(const int8_t* codes, uint8_t* dst) {
+  constexpr int kG = D / 32;   // groups per token
+  for (int i = threadIdx.x; i < kBlock * kG; i += kThreads) {
+    const int n = i / kG, g = i % kG;
+    const uint32_t* src = (const uint32_t*)(codes + n * kCodeStride + 32 * g);
+    uint32_t f[8], o[6];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = e2m3_fields4(src[j]);
+    pack_fields32(f, o);
+    uint8_t* d = dst + (size_t)n * D + 32 * g;
+    *(uint4*)d = uint4{o[0], o[1], o[2], o[3]};
+    *(uint4*)(d + 16) = uint4{o[4], o[5], 0u, 0u};
+  }
+}
+
+// FP6 layout: V int8 codes (LDS, [channel][token]) -> V^T block [D][128], each
+// row in four 32-byte groups g = 2c + h (64-key chunk c, MFMA lane half h) of
+// 24 FP6 bytes and 8 zero bytes.  Field k of group (c, h) holds key
+// 64c + 32(k/16) + 8((k%16)/4) + 4h + k%4: the key that field k of the P^T
+// operand (FP6, taken from the S^T accumulator layout) holds in lane half h.
+// The fields come four at a time: k%4 is the byte of a code dword.
+template <int D>
+__device__ __forceinline__ void store_v_codes_f6(const int8_t* codesT, uint8_t* dst) {
+  for (int i = threadIdx.x; i < D * 4; i += kThreads) {
+    const int d = i / 4, g = i % 4, c = g / 2, h = g % 2;
+    const int8_t* row = codesT + d * kCodeStride + 64 * c + 4 * h;
+    uint32_t f[8], o[6];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = e2m3_fields4(*(const uint32_t*)(row + 32 * (j / 4) + 8 * (j % 4)));
+    pack_fields32(f, o);
+    uint8_t* dp = dst + (size_t)d * 128 + 32 * g;
+    *(uint4*)dp = uint4{o[0], o[1], o[2], o[3]};
+    *(uint4*)(dp + 16) = uint4{o[4], o[5], 0u, 0u};
+  }
+}
+
 // V codes (LDS, [channel][token]) -> packed V^T block [D][64] in global memory.
 template <int D>
 __device__ __forceinline__ void store_v_codes(const int8_t* codesT, uint8_t* dst) {
@@ -443,11 +514,13 @@ __device__ __forceinline__ void store_v_codes(const int8_t* codesT, uint8_t* dst
 // block in every partition: per tensor, RoPE + rotation on the MFMA (or RoPE
 // alone), block amax, codes into the LDS buffer that held the tensor's rows,
 // coalesced store; then V: block amax and codes, stored transposed.
-template <int D, int D0, int D1, bool F8, bool ROT>
+template <int D, int D0, int D1, int LAY, bool ROT>
 __device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* stage_q,
                                             uint32_t* stage_k, float* red, int blk, int bh) {
   constexpr int kRS = D / 2 + 1;
   constexpr int TB = kBlock / 16 / (kThreads / 64);   // 16-token groups per wave
+  // LDS codes: E4M3 bytes for the FP8 layout, int8 for the others
+  constexpr bool F8 = LAY == ROTATTN_LAYOUT_FP8;
   const int w = threadIdx.x >> 6;
   const int tok0 = 16 * TB * w;
   const int n0 = blk * kBlock;
@@ -525,8 +598,10 @@ __device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* sta
       quant_part_a<D1, TB, F8>(z2, inv, D0 + D1, tok0, codes);
     }
     __syncthreads();
-    if (F8)
+    if (LAY == ROTATTN_LAYOUT_FP8)
       store_qk_codes_f8<D>(codes, (s == 0 ? a.q4 : a.k4) + pad_row * D);
+    else if (LAY == ROTATTN_LAYOUT_FP6)
+      store_qk_codes_f6<D>(codes, (s == 0 ? a.q4 : a.k4) + pad_row * D);
     else
       store_qk_codes<D>(codes, (s == 0 ? a.q4 : a.k4) + pad_row * (D / 2));
     if (threadIdx.x == 0) {
@@ -547,8 +622,10 @@ __device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* sta
   float scale;
   v_codes<D, F8>(stage_q, red, codes, scale);
   __syncthreads();
-  if (F8)
+  if (LAY == ROTATTN_LAYOUT_FP8)
     store_v_codes_f8<D>(codes, a.v4 + ((size_t)bh * a.NB + blk) * D * 128);
+  else if (LAY == ROTATTN_LAYOUT_FP6)
+    store_v_codes_f6<D>(codes, a.v4 + ((size_t)bh * a.NB + blk) * D * 128);
   else
     store_v_codes<D>(codes, a.v4 + ((size_t)bh * a.NB + blk) * D * 64);
   if (threadIdx.x == 0) a.v_scale[(size_t)bh * a.NB + blk] = scale;
@@ -663,7 +740,7 @@ hipError_t launch_stage_fp16(int D, int nbh, const StageArgs& a, hipStream_t st)
 // One work-group per (128-token block, head), 4 waves (one per SIMD): two
 // work-groups share a CU (LDS), so one group's MFMA phase overlaps the other's
 // memory phases.
-template <int D, int D0, int D1, bool F8, bool ROT>
+template <int D, int D0, int D1, int LAY, bool ROT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void k_prologue(PrologueArgs a) {
   static_assert(D0 + 2 * D1 == D, "split must be (D0, D1, D1)");
@@ -679,31 +756,35 @@ void k_prologue(PrologueArgs a) {
   if (a.fallback.test(bh))
     prologue_fallback<D, D0, D1>(a, stage_q, stage_k, blk, bh);
   else
-    prologue_qk<D, D0, D1, F8, ROT>(a, stage_q, stage_k, red, blk, bh);
+    prologue_qk<D, D0, D1, LAY, ROT>(a, stage_q, stage_k, red, blk, bh);
+}
+
+template <int D, int D0, int D1, int LAY>
+static void launch_prologue_l(bool rot, dim3 grid, const PrologueArgs& a, hipStream_t st) {
+  if (rot)
+    hipLaunchKernelGGL((k_prologue<D, D0, D1, LAY, true>), grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_prologue<D, D0, D1, LAY, false>), grid, dim3(kThreads), 0, st, a);
 }
 
 template <int D, int D0, int D1>
-static void launch_prologue_t(bool f8, bool rot, dim3 grid, const PrologueArgs& a, hipStream_t st) {
-  if (f8) {
-    if (rot)
-      hipLaunchKernelGGL((k_prologue<D, D0, D1, true, true>), grid, dim3(kThreads), 0, st, a);
-    else
-      hipLaunchKernelGGL((k_prologue<D, D0, D1, true, false>), grid, dim3(kThreads), 0, st, a);
-  } else {
-    if (rot)
-      hipLaunchKernelGGL((k_prologue<D, D0, D1, false, true>), grid, dim3(kThreads), 0, st, a);
-    else
-      hipLaunchKernelGGL((k_prologue<D, D0, D1, false, false>), grid, dim3(kThreads), 0, st, a);
-  }
+static void launch_prologue_t(int layout, bool rot, dim3 grid, const PrologueArgs& a,
+                              hipStream_t st) {
+  if (layout == ROTATTN_LAYOUT_FP8)
+    launch_prologue_l<D, D0, D1, ROTATTN_LAYOUT_FP8>(rot, grid, a, st);
+  else if (layout == ROTATTN_LAYOUT_FP6)
+    launch_prologue_l<D, D0, D1, ROTATTN_LAYOUT_FP6>(rot, grid, a, st);
+  else
+    launch_prologue_l<D, D0, D1, ROTATTN_LAYOUT_PACKED>(rot, grid, a, st);
 }
 
-hipError_t launch_prologue(int D, int dt, int BH, bool f8, bool rot, const PrologueArgs& a,
+hipError_t launch_prologue(int D, int dt, int BH, int layout, bool rot, const PrologueArgs& a,
                            hipStream_t st) {
   dim3 grid(a.NB, BH);
   if (D == 128 && dt == 44)
-    launch_prologue_t<128, 44, 42>(f8, rot, grid, a, st);
+    launch_prologue_t<128, 44, 42>(layout, rot, grid, a, st);
   else if (D == 64 && dt == 24)
-    launch_prologue_t<64, 24, 20>(f8, rot, grid, a, st);
+    launch_prologue_t<64, 24, 20>(layout, rot, grid, a, st);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

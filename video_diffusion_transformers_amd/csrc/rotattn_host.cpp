@@ -133,11 +133,21 @@ float rotattn_kappa_host(int32_t D) {
   return (float)(1.0L / logl(2.0L) / sqrtl((long double)D));
 }
 
+static bool valid_layout(int layout) {
+  return layout == ROTATTN_LAYOUT_PACKED || layout == ROTATTN_LAYOUT_FP8 ||
+         layout == ROTATTN_LAYOUT_FP6;
+}
+
+// FP8 and FP6: one byte per code (FP6 groups of 32 codes in 24 bytes + 8 pad)
+static bool byte_layout(int layout) {
+  return layout == ROTATTN_LAYOUT_FP8 || layout == ROTATTN_LAYOUT_FP6;
+}
+
 size_t rotattn_prepared_bytes_layout(const rotattn_shape* s, int with_rope, int layout) {
   if (rotattn_validate(s) != ROTATTN_OK) return 0;
-  if (layout != ROTATTN_LAYOUT_PACKED && layout != ROTATTN_LAYOUT_FP8) return 0;
+  if (!valid_layout(layout)) return 0;
   const size_t BH = (size_t)s->B * s->H, NB = nblocks(s), D = s->D;
-  const size_t per_code = layout == ROTATTN_LAYOUT_FP8 ? 2 : 1;   // half-bytes per code
+  const size_t per_code = byte_layout(layout) ? 2 : 1;   // half-bytes per code
   const size_t packed = align_up(BH * NB * kBlock * D * per_code / 2);
   const size_t scales = align_up(BH * NB * sizeof(float));
   // fallback buffers: q_rope, k_rope, v_t, each [B*H][N_pad][D] fp16
@@ -150,11 +160,11 @@ int rotattn_prepared_carve(const rotattn_shape* s, void* base, size_t bytes, int
   const int st = rotattn_validate(s);
   if (st != ROTATTN_OK) return st;
   if (!base || !out) return ROTATTN_E_NULL;
-  if (layout != ROTATTN_LAYOUT_PACKED && layout != ROTATTN_LAYOUT_FP8) return ROTATTN_E_ARG;
+  if (!valid_layout(layout)) return ROTATTN_E_ARG;
   if (((uintptr_t)base & (kAlign - 1)) != 0) return ROTATTN_E_ALIGN;
   if (bytes < rotattn_prepared_bytes_layout(s, with_rope, layout)) return ROTATTN_E_WORKSPACE;
   const size_t BH = (size_t)s->B * s->H, NB = nblocks(s), D = s->D;
-  const size_t per_code = layout == ROTATTN_LAYOUT_FP8 ? 2 : 1;
+  const size_t per_code = byte_layout(layout) ? 2 : 1;
   const size_t packed = align_up(BH * NB * kBlock * D * per_code / 2);
   const size_t scales = align_up(BH * NB * sizeof(float));
   const size_t rope = align_up(BH * NB * kBlock * D * 2);
@@ -180,7 +190,7 @@ int rotattn_prepared_carve(const rotattn_shape* s, void* base, size_t bytes, int
 }
 
 size_t rotattn_prepared_bytes(const rotattn_shape* s) {
-  return rotattn_prepared_bytes_layout(s, 1, ROTATTN_LAYOUT_FP8);
+  return rotattn_prepared_bytes_layout(s, 1, ROTATTN_LAYOUT_FP6);
 }
 
 // Strides of a tensor, contiguous [B][H][N][D] when st is NULL.  Every stride
@@ -226,7 +236,7 @@ int check_prepare(const rotattn_shape* s, const uint16_t* q, const uint16_t* k, 
   if (n_rot != 0 && n_rot != 3) return ROTATTN_E_NULL;
   const bool rot = n_rot == 3;
   const int BH = s->B * s->H;
-  if (out->layout != ROTATTN_LAYOUT_PACKED && out->layout != ROTATTN_LAYOUT_FP8) return ROTATTN_E_ARG;
+  if (!valid_layout(out->layout)) return ROTATTN_E_ARG;
   int n_fb = 0;
   make_bits(fallback_mask_host, BH, true, false, &n_fb);
   if (n_fb < BH) {
@@ -273,7 +283,7 @@ int launch_prepare(const rotattn_shape* s, const uint16_t* q, const uint16_t* k,
   a.grid_w = s->grid_w;
   a.kappa = rotattn_kappa_host(s->D);
   a.fallback = fb;
-  return launch_prologue(s->D, s->d_t, BH, out->layout == ROTATTN_LAYOUT_FP8, rot, a, stream) ==
+  return launch_prologue(s->D, s->d_t, BH, out->layout, rot, a, stream) ==
                  hipSuccess
              ? ROTATTN_OK
              : ROTATTN_E_HIP;
@@ -292,10 +302,10 @@ int check_int4(const rotattn_shape* s, const rotattn_prepared* p, uint16_t* o,
     return ROTATTN_E_NULL;
   if (!aligned16(p->q4) || !aligned16(p->k4) || !aligned16(p->v4) || !aligned16(o))
     return ROTATTN_E_ALIGN;
-  if (p->layout != ROTATTN_LAYOUT_PACKED && p->layout != ROTATTN_LAYOUT_FP8) return ROTATTN_E_ARG;
+  if (!valid_layout(p->layout)) return ROTATTN_E_ARG;
   const int norm = opts ? opts->normalizer : ROTATTN_NORM_EXP;
   if (norm != ROTATTN_NORM_EXP && norm != ROTATTN_NORM_CODES) return ROTATTN_E_ARG;
-  if (norm == ROTATTN_NORM_CODES && p->layout != ROTATTN_LAYOUT_FP8) return ROTATTN_E_UNSUPPORTED;
+  if (norm == ROTATTN_NORM_CODES && !byte_layout(p->layout)) return ROTATTN_E_UNSUPPORTED;
   if (dbg) {
     if (!dbg->s_int || !dbg->p_code || !dbg->pv_int || !dbg->m_final || !dbg->l_final)
       return ROTATTN_E_NULL;
@@ -309,7 +319,7 @@ int check_int4(const rotattn_shape* s, const rotattn_prepared* p, uint16_t* o,
 int launch_int4_all(const rotattn_shape* s, const rotattn_prepared* p,
                     const uint8_t* fallback_mask_host, uint16_t* o, const Strides& os,
                     const rotattn_int4_opts* opts, const rotattn_debug* dbg, hipStream_t stream) {
-  const bool f8 = p->layout == ROTATTN_LAYOUT_FP8;
+  const bool f8 = byte_layout(p->layout);
   const int norm = opts ? opts->normalizer : ROTATTN_NORM_EXP;
   const int BH = s->B * s->H;
   Int4Debug d{};
@@ -334,6 +344,7 @@ int launch_int4_all(const rotattn_shape* s, const rotattn_prepared* p,
   a.NB = nblocks(s);
   a.log2_15 = log2_15_f();
   a.code_sum = norm == ROTATTN_NORM_CODES;
+  a.f6 = p->layout == ROTATTN_LAYOUT_FP6;
   rotattn_pcode_thresholds_host(a.tau);
   auto launch = f8 ? launch_int4_f8 : launch_int4;
   if (n_run > 0 && launch(s->D, BH, a, nullptr, stream) != hipSuccess) return ROTATTN_E_HIP;
@@ -538,7 +549,7 @@ int rotattn_fp16_fwd_noalloc(const rotattn_shape* s, const uint16_t* q_rope,
 }
 
 size_t rotattn_workspace_bytes(const rotattn_shape* s) {
-  return rotattn_prepared_bytes_layout(s, 1, ROTATTN_LAYOUT_FP8);
+  return rotattn_prepared_bytes_layout(s, 1, ROTATTN_LAYOUT_FP6);
 }
 
 int rotattn_mixed_fwd(const rotattn_shape* s, const uint16_t* q, const uint16_t* k,
@@ -559,7 +570,7 @@ int rotattn_mixed_fwd_strided(const rotattn_shape* s, const uint16_t* q, const u
   if (st != ROTATTN_OK) return st;
   if (!q || !k || !v || !rr || !workspace || !o) return ROTATTN_E_NULL;
   rotattn_prepared p;
-  int r = rotattn_prepared_carve(s, workspace, workspace_bytes, 1, ROTATTN_LAYOUT_FP8, &p);
+  int r = rotattn_prepared_carve(s, workspace, workspace_bytes, 1, ROTATTN_LAYOUT_FP6, &p);
   if (r != ROTATTN_OK) return r;
   Strides in, os;
   r = check_prepare(s, q, k, v, qkv_strides, rr, fallback_mask_host, &p, &in);
@@ -581,11 +592,11 @@ int rotattn_mixed_fwd_strided(const rotattn_shape* s, const uint16_t* q, const u
 int rotattn_pcode_sweep(int layout, uint32_t mag_lo, uint32_t count, uint32_t* transitions,
                         uint32_t max_transitions, uint32_t* n_transitions, hipStream_t stream) {
   if (!transitions || !n_transitions) return ROTATTN_E_NULL;
-  if (layout != ROTATTN_LAYOUT_PACKED && layout != ROTATTN_LAYOUT_FP8) return ROTATTN_E_ARG;
+  if (!valid_layout(layout)) return ROTATTN_E_ARG;
   if (count == 0 || (uint64_t)mag_lo + count > 0x7B800000ull) return ROTATTN_E_ARG;
   float tau[15];
   rotattn_pcode_thresholds_host(tau);
-  return launch_pcode_sweep(layout == ROTATTN_LAYOUT_FP8, mag_lo, count, tau, log2_15_f(),
+  return launch_pcode_sweep(byte_layout(layout), mag_lo, count, tau, log2_15_f(),
                             transitions, max_transitions, n_transitions, stream) == hipSuccess
              ? ROTATTN_OK
              : ROTATTN_E_HIP;
@@ -594,12 +605,12 @@ int rotattn_pcode_sweep(int layout, uint32_t mag_lo, uint32_t count, uint32_t* t
 int rotattn_pcode_eval(int layout, const int32_t* I, uint32_t n, float c, float m, uint8_t* codes,
                        hipStream_t stream) {
   if (!I || !codes) return ROTATTN_E_NULL;
-  if (layout != ROTATTN_LAYOUT_PACKED && layout != ROTATTN_LAYOUT_FP8) return ROTATTN_E_ARG;
+  if (!valid_layout(layout)) return ROTATTN_E_ARG;
   if (n == 0 || (n % 4096u) != 0) return ROTATTN_E_ARG;
   if (!(c >= 0.0f) || !isfinite(m)) return ROTATTN_E_ARG;
   float tau[15];
   rotattn_pcode_thresholds_host(tau);
-  return launch_pcode_eval(layout == ROTATTN_LAYOUT_FP8, I, n, c, m, tau, log2_15_f(), codes,
+  return launch_pcode_eval(byte_layout(layout), I, n, c, m, tau, log2_15_f(), codes,
                            stream) == hipSuccess
              ? ROTATTN_OK
              : ROTATTN_E_HIP;

@@ -101,7 +101,8 @@ struct Int4Args {
   int N, NB;
   float log2_15;                // fl32(log2(15))
   float tau[15];                // P-code thresholds
-  bool code_sum;                // normalizer: sum of the P codes (FP8 layout) instead of sum 2^x
+  bool code_sum;                // normalizer: sum of the P codes (FP8/FP6 layouts) instead of sum 2^x
+  bool f6;                      // FP6 layout: Q, K, V codes as FP6 E2M3 (else FP8 E4M3)
   HeadBits run;                 // bit set: run this head
 };
 
@@ -138,7 +139,7 @@ struct StageArgs {
 // Launchers (each defined next to its kernel).  Return a hipError_t.
 hipError_t launch_rot_to_f64(const float* rt, const float* rh, const float* rw, int dt, int dh,
                              double* out, hipStream_t st);
-hipError_t launch_prologue(int D, int dt, int BH, bool f8, bool rot, const PrologueArgs& a,
+hipError_t launch_prologue(int D, int dt, int BH, int layout, bool rot, const PrologueArgs& a,
                            hipStream_t st);
 hipError_t launch_int4(int D, int BH, const Int4Args& a, const Int4Debug* dbg, hipStream_t st);
 hipError_t launch_int4_f8(int D, int BH, const Int4Args& a, const Int4Debug* dbg, hipStream_t st);

@@ -21,7 +21,8 @@ BLOCK = 128
 MAX_HEADS = 4096
 LAYOUT_PACKED = 0      # two INT4 codes per byte, i8 MFMA
 LAYOUT_FP8 = 1         # one INT4 code per byte as FP8 E4M3, f8f6f4 MFMA
-LAYOUTS = {"packed": LAYOUT_PACKED, "fp8": LAYOUT_FP8}
+LAYOUT_FP6 = 2         # INT4 codes as FP6 E2M3 fields, 32 per 32 bytes, f8f6f4 MFMA at the FP6 rate
+LAYOUTS = {"packed": LAYOUT_PACKED, "fp8": LAYOUT_FP8, "fp6": LAYOUT_FP6}
 
 STATUS = {0: "ok", -1: "null pointer argument", -2: "inconsistent shape",
           -3: "unsupported head dimension, RoPE split or head count", -4: "workspace too small",
@@ -258,7 +259,7 @@ class RopeRotDevice:
 class PreparedDevice:
     """Device buffers of a rotattn_prepared, carved from one allocation."""
 
-    def __init__(self, shape: Shape, with_rope: bool = True, layout: int = LAYOUT_FP8,
+    def __init__(self, shape: Shape, with_rope: bool = True, layout: int = LAYOUT_FP6,
                  device="cuda"):
         torch = _torch()
         self.shape = shape
@@ -296,7 +297,7 @@ def prepare_qkv(shape: Shape, q, k, v, rr: RopeRotDevice, prep: PreparedDevice, 
 def int4_fwd(shape: Shape, prep: PreparedDevice, o, mask=None, debug: Debug | None = None,
              stream=None, normalizer: str = "exp") -> None:
     """normalizer "exp": l = sum of the unquantized 2^x; "codes": the sum of
-    the P codes (FP8 layout)."""
+    the P codes (FP8 and FP6 layouts)."""
     keep, m = _mask_arg(mask)
     dbg = C.byref(debug) if debug is not None else None
     opts = Int4Opts(NORMALIZERS[normalizer])
@@ -364,7 +365,7 @@ def mixed_fwd(shape: Shape, q, k, v, rr: RopeRotDevice, mask, workspace, o, stre
           "mixed_fwd")
 
 
-def pcode_sweep(mag_lo: int, count: int, max_transitions: int = 4096, layout: int = LAYOUT_FP8,
+def pcode_sweep(mag_lo: int, count: int, max_transitions: int = 4096, layout: int = LAYOUT_FP6,
                 stream=None):
     """Transitions (magnitude bits, code before, code after) of the device P code."""
     torch = _torch()
@@ -375,7 +376,7 @@ def pcode_sweep(mag_lo: int, count: int, max_transitions: int = 4096, layout: in
     return trans, n
 
 
-def pcode_eval(I, c: float, m: float, layout: int = LAYOUT_FP8, stream=None):
+def pcode_eval(I, c: float, m: float, layout: int = LAYOUT_FP6, stream=None):
     torch = _torch()
     codes = torch.empty(I.numel(), dtype=torch.uint8, device=I.device)
     check(lib().rotattn_pcode_eval(layout, _ptr(I), I.numel(), C.c_float(c), C.c_float(m),
