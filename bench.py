@@ -365,7 +365,8 @@ def bench_dit_block(cfg, width: int = 5120, reps: int = 2):
     projection GEMM (fp16 GEMMs on hipBLASLt, seeded random weights).  INT4
     attention with the prologue reading the projection's token-major output in
     place and O written token-major, against the same block with contiguous
-    copies around the attention, and against FP16 attention on every head."""
+    copies around the attention, against the library's own QKV projection with
+    the prologue as its epilogue, and against FP16 attention on every head."""
     import torch
     from video_diffusion_transformers_amd import dit_block, rotattn as R, synth
     shape = R.shape_of(cfg)
@@ -376,6 +377,7 @@ def bench_dit_block(cfg, width: int = 5120, reps: int = 2):
     res = {}
     for key, kw in (("int4_fused_ms", dict(fp16=False, fused=True)),
                     ("int4_unfused_ms", dict(fp16=False, fused=False)),
+                    ("int4_gemm_prologue_ms", dict(fp16=False, gemm_prologue=True)),
                     ("fp16_fused_ms", dict(fp16=True, fused=True))):
         blk.forward(x, **kw)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -394,6 +396,15 @@ def bench_dit_block(cfg, width: int = 5120, reps: int = 2):
     e1.record()
     torch.cuda.synchronize()
     res["projections_ms"] = round(e0.elapsed_time(e1) / reps, 3)
+    # the QKV projection + prologue: hipBLASLt GEMM then the prologue on its
+    # token-major output, against the one fused launch
+    q, k, v = blk.qkv.view(cfg.B, cfg.N, 3, cfg.H, cfg.D).permute(2, 0, 3, 1, 4)
+    res["qkv_gemm_ms"] = round(time_calls(lambda: torch.matmul(x, blk.w_qkv, out=blk.qkv), reps), 3)
+    res["prologue_strided_ms"] = round(
+        time_calls(lambda: R.prepare_qkv(shape, q, k, v, blk.rr, blk.prep), reps), 3)
+    res["qkv_gemm_prologue_fused_ms"] = round(
+        time_calls(lambda: R.qkv_proj_prepare(shape, x, blk.w_qkv_rows, None, blk.rr, blk.prep),
+                   reps), 3)
     res["int4_vs_fp16_block_speedup"] = round(res["fp16_fused_ms"] / res["int4_fused_ms"], 3)
     print(f"[bench] DiT block: {res}", file=sys.stderr, flush=True)
     del blk, x

@@ -271,6 +271,38 @@ int rotattn_prepare_qkv_strided(const rotattn_shape* s, const uint16_t* q,
                                 hipStream_t stream);
 
 /*
+ * The DiT block's QKV projection with the prologue as its epilogue, in one
+ * launch (RotateAttention page, Abstract: the INT4 attention inside the DiT
+ * block, end to end): Q, K and V are never written to memory.  For every
+ * 128-token block of every batch entry and every (Q|K|V, head), a work-group
+ * computes the projection tile x . w^T (+ bias) on fp16 MFMA with fp32
+ * accumulation, rounds it once to fp16 (round to nearest even) and runs the
+ * prologue on it in LDS, writing `out` exactly as rotattn_prepare_qkv writes
+ * it for those fp16 Q, K, V (codes and scales, or for fallback heads the
+ * RoPE'd Q', K' and the V^T tiles).
+ *  x:       fp16 [B][N][C] input, element strides x_batch and x_token (channel
+ *           stride 1; multiples of 8; x_token <= 2^24), 16-byte aligned.
+ *  C:       model width, a multiple of 64 (<= x_token).
+ *  w:       fp16 [3*H*D][C], row r = output channel r: rows h*D + d are head
+ *           h's Q channel d, then H*D rows of K, then H*D rows of V (a fused
+ *           QKV linear layer's weight); 16-byte aligned.
+ *  bias:    fp16 [3*H*D] in the same order, or NULL.
+ *  qkv_out: NULL, or fp16 [3][B*H][N_pad][D] (16-byte aligned) that receives
+ *           the rounded projection, rows >= N zero: Q, K and V per head as the
+ *           prologue saw them.
+ * Only D = 128 with the (44, 42, 42) split; other shapes return
+ * ROTATTN_E_UNSUPPORTED.  Argument errors are returned before anything is
+ * enqueued.
+ */
+int rotattn_qkv_proj_prepare(const rotattn_shape* s, const uint16_t* x,
+                             int64_t x_batch, int64_t x_token, int32_t C,
+                             const uint16_t* w, const uint16_t* bias,
+                             const rotattn_rope_rot* rr,
+                             const uint8_t* fallback_mask_host,
+                             const rotattn_prepared* out, uint16_t* qkv_out,
+                             hipStream_t stream);
+
+/*
  * INT4 attention over the heads with fallback_mask_host[...] == 0 (all heads
  * when NULL): I = q4.k4^T (i8 MFMA for the PACKED layout, f8f6f4 MFMA for
  * FP8 and FP6), one-pass online softmax over 128-key tiles in the log2 domain, P codes

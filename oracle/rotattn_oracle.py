@@ -41,6 +41,11 @@ R5  P code = rne(15 * 2^x) with x = s - m against the running max after the
 R6  Normalizer l = sum of the unquantized 2^x.
 R7  FP16 fallback: plain softmax attention on RoPE'd fp16 Q/K (no rotation,
     no quantization), per (batch, head).
+R8  The step before the attention in the DiT block (the pages place the
+    attention inside it and quote end-to-end figures, nothing more): the
+    usual fused linear layer, [Q | K | V] = x W^T + b with W's rows in the
+    order Q heads, K heads, V heads and head h taking channels h*D..h*D+D-1
+    of each; each output is the exact sum rounded once to fp16.
 
 Exact rounding rules (so that codes are well defined bit for bit):
 * RoPE in float32, no fused multiply-add:
@@ -393,6 +398,30 @@ def fp16_attention(q_rope16, k_rope16, v16, rows):
     D = q_rope16.shape[1]
     out = softmax_attention(q_rope16, k_rope16, v16, rows, 1.0 / math.sqrt(D))
     return out.astype(np.float16), out
+
+
+# --------------------------------------------------------------------------
+# the QKV projection before the attention  [R8]
+# --------------------------------------------------------------------------
+
+def qkv_projection(x16, w16, b16=None):
+    """R8: x [n, C] fp16, W [3 H D, C] fp16 (row r = output channel r), b
+    [3 H D] fp16 or None -> fp16 [n, 3 H D]: the float64 sum over C (+ b),
+    rounded once to fp16 (round to nearest even).  Every product of two fp16
+    values is exact in float64; the sum is exact too whenever it needs no more
+    than float64's 53 bits (the tests' exact cases), else within float64's
+    own error, far below fp16's rounding."""
+    acc = np.asarray(x16, np.float64) @ np.asarray(w16, np.float64).T
+    if b16 is not None:
+        acc = acc + np.asarray(b16, np.float64)[None, :]
+    return acc.astype(np.float16)
+
+
+def split_qkv(y16, H: int, D: int):
+    """R8: the projection output [n, 3 H D] -> Q, K, V, each [H, n, D]."""
+    n = y16.shape[0]
+    t = np.asarray(y16).reshape(n, 3, H, D)
+    return tuple(np.ascontiguousarray(t[:, i].transpose(1, 0, 2)) for i in range(3))
 
 
 # --------------------------------------------------------------------------

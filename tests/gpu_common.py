@@ -147,9 +147,11 @@ def pack_vt_blocks(codes: np.ndarray, N_pad: int) -> np.ndarray:
 class Run:
     """One config on the device: inputs, RoPE/rotation, prepared buffers."""
 
-    def __init__(self, cfg: synth.Config, step: int = 0, layout: int = 2, merged: bool = False):
+    def __init__(self, cfg: synth.Config, step: int = 0, layout: int = 2, merged: bool = False,
+                 qkv=None):
         """merged: the rotation is merged into the RoPE tables (seeded pair
-        phases, no dense rotation matrices)."""
+        phases, no dense rotation matrices).  qkv: host fp16 Q, K, V
+        [B][H][N][D] to use instead of the workload's seeded ones."""
         torch = torch_cuda()
         from video_diffusion_transformers_amd import rotattn as R
         self.R = R
@@ -158,7 +160,7 @@ class Run:
         self.shape = R.shape_of(cfg)
         self.NB = R.n_blocks(self.shape)
         self.N_pad = self.NB * 128
-        q, k, v = synth.all_heads_qkv(cfg, step)
+        q, k, v = synth.all_heads_qkv(cfg, step) if qkv is None else qkv
         self.host = (q, k, v)
         self.q, self.k, self.v = (torch.from_numpy(x).cuda() for x in (q, k, v))
         self.merged = merged
@@ -224,6 +226,34 @@ class Run:
         p = self.oracle_prep(bh, fallback=True)
         v = self.host[2].reshape(self.cfg.BH, self.cfg.N, self.cfg.D)[bh]
         return O.fp16_attention(p["q_rope"], p["k_rope"], v, rows)
+
+
+def check_prologue_heads(run, heads, layout: str, preps):
+    """The prepared buffers of `run` for the given heads against the oracle's
+    prologue outputs `preps` {bh: prepare_head(...)}: codes in the bytes of
+    `layout` and scale bits of INT4 heads; RoPE'd Q'/K' and V^T tiles of
+    fallback heads; bit for bit."""
+    name = run.cfg.name
+    g = run.gpu_prepared()
+    for bh in heads:
+        fb = bool(run.mask[bh])
+        p = preps[bh]
+        if fb:
+            N = run.cfg.N
+            for t in ("q", "k"):
+                assert np.array_equal(g[f"{t}_rope"][bh][:N], p[f"{t}_rope"].view(np.uint16))
+                assert not g[f"{t}_rope"][bh][N:].any()
+            v = run.host[2].reshape(run.cfg.BH, N, run.cfg.D)[bh]
+            assert np.array_equal(g["v_t"][bh], fp16_vt_tiles(v, run.N_pad)), (name, bh, "v_t")
+            continue
+        for t in ("q", "k"):
+            rows = code_rows(p[f"{t}_codes"], layout)
+            want = np.zeros((run.N_pad, rows.shape[1]), np.uint8)
+            want[:run.cfg.N] = rows
+            assert np.array_equal(g[f"{t}4"][bh], want), (name, bh, t)
+        assert np.array_equal(g["v4"][bh], v_blocks(p["v_codes"], run.N_pad, layout)), (name, bh)
+        for f in ("q_scale_l2", "k_scale", "v_scale"):
+            assert np.array_equal(g[f][bh].view(np.uint32), p[f].view(np.uint32)), (name, bh, f)
 
 
 def check_out(o_gpu: np.ndarray, o_ref16: np.ndarray, what: str):

@@ -259,3 +259,36 @@ def test_noalloc_rejects_heads_beyond_the_scratch():
                                       C.c_void_p((1 << 20) + 2), C.c_void_p(0)) == -5
     none = (C.c_uint8 * 2)(0, 0)
     assert L.rotattn_fp16_fwd_noalloc(C.byref(s), fake, fake, fake, none, fake, C.c_void_p(0)) == 0
+
+
+def test_qkv_proj_prepare_checks_every_argument_before_any_launch():
+    """The fused QKV projection + prologue: NULL inputs, an unsupported head
+    size, a width that is not a multiple of 64 or exceeds the row stride,
+    misaligned inputs or strides; every argument valid reaches the launch
+    (no GPU here: HIP error)."""
+    L = R.lib()
+    s = R.make_shape(1, 2, (2, 9, 17), 128, (44, 42, 42))          # N = 306
+    fake = C.c_void_p(1 << 20)
+    nul = C.c_void_p(0)
+    rr = R.RopeRot(*([fake] * 9))
+    p = R.Prepared()
+    assert L.rotattn_prepared_carve(C.byref(s), C.c_void_p(1 << 24), 1 << 30, 1, R.LAYOUT_FP6,
+                                    C.byref(p)) == 0
+    C_ = 256
+
+    def call(shape=s, x=fake, xb=306 * C_, xt=C_, width=C_, w=fake, bias=None, out=None):
+        return L.rotattn_qkv_proj_prepare(C.byref(shape), x, xb, xt, width, w, bias, C.byref(rr),
+                                          None, C.byref(p), out, nul)
+
+    assert call(x=nul) == -1
+    assert call(w=nul) == -1
+    assert call(shape=R.make_shape(1, 2, (2, 4, 4), 64, (24, 20, 20))) == -3
+    assert call(width=100, xt=104) == -7                 # not a multiple of 64
+    assert call(width=0) == -7
+    assert call(xt=C_ - 64) == -7                        # row stride below the width
+    assert call(x=C.c_void_p((1 << 20) + 8)) == -5
+    assert call(w=C.c_void_p((1 << 20) + 4)) == -5
+    assert call(xt=C_ + 4) == -5                         # 8-byte row stride
+    assert call(out=C.c_void_p((1 << 20) + 2)) == -5
+    assert call() == -6
+    assert call(bias=fake, out=fake) == -6

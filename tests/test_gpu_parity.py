@@ -12,8 +12,8 @@ import pytest
 import oracle as O
 from video_diffusion_transformers_amd import synth
 
-from gpu_common import (Run, check_out, code_rows, fp16_vt_tiles, pool_reference, torch_cuda,
-                        v_blocks)
+from gpu_common import (Run, check_out, check_prologue_heads, code_rows, pool_reference,
+                        torch_cuda)
 
 pytestmark = pytest.mark.gpu
 
@@ -121,28 +121,7 @@ def test_pcode_eval_random_scores(c, spread, layout):
 # ------------------------------------------------------------------ prologue
 
 def _check_prologue_heads(run, heads, layout):
-    name = run.cfg.name
-    g = run.gpu_prepared()
-    preps = oracle_preps(run, list(heads))
-    for bh in heads:
-        fb = bool(run.mask[bh])
-        p = preps[bh]
-        if fb:
-            N = run.cfg.N
-            for t in ("q", "k"):
-                assert np.array_equal(g[f"{t}_rope"][bh][:N], p[f"{t}_rope"].view(np.uint16))
-                assert not g[f"{t}_rope"][bh][N:].any()
-            v = run.host[2].reshape(run.cfg.BH, N, run.cfg.D)[bh]
-            assert np.array_equal(g["v_t"][bh], fp16_vt_tiles(v, run.N_pad)), (name, bh, "v_t")
-            continue
-        for t in ("q", "k"):
-            rows = code_rows(p[f"{t}_codes"], layout)
-            want = np.zeros((run.N_pad, rows.shape[1]), np.uint8)
-            want[:run.cfg.N] = rows
-            assert np.array_equal(g[f"{t}4"][bh], want), (name, bh, t)
-        assert np.array_equal(g["v4"][bh], v_blocks(p["v_codes"], run.N_pad, layout)), (name, bh)
-        for f in ("q_scale_l2", "k_scale", "v_scale"):
-            assert np.array_equal(g[f][bh].view(np.uint32), p[f].view(np.uint32)), (name, bh, f)
+    check_prologue_heads(run, heads, layout, oracle_preps(run, list(heads)))
 
 
 @pytest.mark.parametrize("layout", ["packed", "fp8", "fp6"])

@@ -510,13 +510,16 @@ __device__ __forceinline__ void store_v_codes(const int8_t* codesT, uint8_t* dst
   }
 }
 
-// A head that is not a fallback head.  Wave w owns tokens 32w..32w+31 of the
-// block in every partition: per tensor, RoPE + rotation on the MFMA (or RoPE
-// alone), block amax, codes into the LDS buffer that held the tensor's rows,
-// coalesced store; then V: block amax and codes, stored transposed.
-template <int D, int D0, int D1, int LAY, bool ROT>
-__device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* stage_q,
-                                            uint32_t* stage_k, float* red, int blk, int bh) {
+// One tensor of a head that is not a fallback head (s = 0: Q, 1: K) from its
+// 128 staged fp16 rows xs (kRS dwords per row, rows past N zero).  Wave w owns
+// tokens 32w..32w+31 of the block in every partition: RoPE + rotation on the
+// MFMA (or RoPE alone), block amax, codes into xs (every wave is past its last
+// read of the rows once the reduction's barriers are passed), coalesced
+// store, block scale.  mid() runs right after the reduction, before the codes
+// are made: the prologue requests V's rows there.
+template <int D, int D0, int D1, int LAY, bool ROT, class Mid>
+__device__ __forceinline__ void quant_qk_tile(const PrologueArgs& a, uint32_t* xs, float* red,
+                                              int s, int blk, int bh, Mid mid) {
   constexpr int kRS = D / 2 + 1;
   constexpr int TB = kBlock / 16 / (kThreads / 64);   // 16-token groups per wave
   // LDS codes: E4M3 bytes for the FP8 layout, int8 for the others
@@ -525,102 +528,85 @@ __device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* sta
   const int tok0 = 16 * TB * w;
   const int n0 = blk * kBlock;
   const int HW = a.grid_h * a.grid_w;
-  const int64_t head_in = a.in.head_offset(bh, a.H);
   const size_t pad_row = ((size_t)bh * a.NB + blk) * kBlock;   // first code row of this block
-
-  load_tile<D>(a.q + head_in, a.in.token, n0, a.N, stage_q);
-  load_tile<D>(a.k + head_in, a.in.token, n0, a.N, stage_k);
-  wait_tiles();
-  __syncthreads();
-
-  // one tensor (s = 0: Q, 1: K), inlined twice: straight-line code, so
-  // nothing is hoisted across the two tensors and kept live
-  auto tensor = [&](int s) {
-    uint32_t* xs = s == 0 ? stage_q : stage_k;
-    int8_t* codes = (int8_t*)xs;
-    float inv, scale;
-    // the table reads are the same for Q and K; an opaque zero offset per
-    // tensor keeps the compiler from loading them once and holding them in
-    // registers across both tensors
-    int zero = 0;
-    asm volatile("" : "+s"(zero));
-    const float *cos_t = a.cos_t + zero, *sin_t = a.sin_t + zero, *cos_h = a.cos_h + zero;
-    const float *sin_h = a.sin_h + zero, *cos_w = a.cos_w + zero, *sin_w = a.sin_w + zero;
-    // every wave is past its last read of xs once the reduction's barriers are
-    // passed: the buffer takes the codes next
-    if (ROT) {
-      // R_a^T of each partition as B fragments, loaded (from cache) just before
-      // its use; rotation matrices in fp64 [k][r]: t at 0, h at D0^2, w at
-      // D0^2 + D1^2
-      float z0[TB][Part<D0>::JB][4], z1[TB][Part<D1>::JB][4], z2[TB][Part<D1>::JB][4];
-      float amax;
-      {
-        float b[Part<D0>::KS][Part<D0>::JB];
-        const double* rp = a.rot64 + zero;   // read again per tensor, not held
-        load_rot_frags<D0>(rp, b);
-        amax = rotate_part<D0, TB, kRS>(xs, cos_t, sin_t, b, 0, tok0, n0, a.N, 0, HW, a.grid_h,
-                                        a.grid_w, z0);
-      }
-      {
-        float b[Part<D1>::KS][Part<D1>::JB];
-        const double* rp = a.rot64 + D0 * D0 + zero;
-        load_rot_frags<D1>(rp, b);
-        amax = fmaxf(amax, rotate_part<D1, TB, kRS>(xs, cos_h, sin_h, b, D0, tok0, n0, a.N, 1,
-                                                    HW, a.grid_h, a.grid_w, z1));
-      }
-      {
-        float b[Part<D1>::KS][Part<D1>::JB];
-        const double* rp = a.rot64 + D0 * D0 + D1 * D1 + zero;
-        load_rot_frags<D1>(rp, b);
-        amax = fmaxf(amax, rotate_part<D1, TB, kRS>(xs, cos_w, sin_w, b, D0 + D1, tok0, n0,
-                                                    a.N, 2, HW, a.grid_h, a.grid_w, z2));
-      }
-      block_scale(amax, red, inv, scale);
-      // K pass, past the reduction's barriers: every wave is done with the Q
-      // codes in stage_q and has issued its last table load, so V's rows can
-      // stream in while K is quantized and stored
-      if (s == 1) load_tile<D>(a.v + head_in, a.in.token, n0, a.N, stage_q);
-      quant_part<D0, TB, F8>(z0, inv, 0, tok0, codes);
-      quant_part<D1, TB, F8>(z1, inv, D0, tok0, codes);
-      quant_part<D1, TB, F8>(z2, inv, D0 + D1, tok0, codes);
-    } else {
-      float z0[TB][Part<D0>::KS], z1[TB][Part<D1>::KS], z2[TB][Part<D1>::KS];
-      float amax = rope_part_a<D0, TB, kRS>(xs, cos_t, sin_t, 0, tok0, n0, a.N, 0, HW,
-                                            a.grid_h, a.grid_w, z0);
-      amax = fmaxf(amax, rope_part_a<D1, TB, kRS>(xs, cos_h, sin_h, D0, tok0, n0, a.N, 1, HW,
-                                                  a.grid_h, a.grid_w, z1));
-      amax = fmaxf(amax, rope_part_a<D1, TB, kRS>(xs, cos_w, sin_w, D0 + D1, tok0, n0, a.N,
-                                                  2, HW, a.grid_h, a.grid_w, z2));
-      block_scale(amax, red, inv, scale);
-      if (s == 1) load_tile<D>(a.v + head_in, a.in.token, n0, a.N, stage_q);
-      quant_part_a<D0, TB, F8>(z0, inv, 0, tok0, codes);
-      quant_part_a<D1, TB, F8>(z1, inv, D0, tok0, codes);
-      quant_part_a<D1, TB, F8>(z2, inv, D0 + D1, tok0, codes);
+  int8_t* codes = (int8_t*)xs;
+  float inv, scale;
+  // the table reads are the same for Q and K; an opaque zero offset per
+  // tensor keeps the compiler from loading them once and holding them in
+  // registers across both tensors
+  int zero = 0;
+  asm volatile("" : "+s"(zero));
+  const float *cos_t = a.cos_t + zero, *sin_t = a.sin_t + zero, *cos_h = a.cos_h + zero;
+  const float *sin_h = a.sin_h + zero, *cos_w = a.cos_w + zero, *sin_w = a.sin_w + zero;
+  if (ROT) {
+    // R_a^T of each partition as B fragments, loaded (from cache) just before
+    // its use; rotation matrices in fp64 [k][r]: t at 0, h at D0^2, w at
+    // D0^2 + D1^2
+    float z0[TB][Part<D0>::JB][4], z1[TB][Part<D1>::JB][4], z2[TB][Part<D1>::JB][4];
+    float amax;
+    {
+      float b[Part<D0>::KS][Part<D0>::JB];
+      const double* rp = a.rot64 + zero;   // read again per tensor, not held
+      load_rot_frags<D0>(rp, b);
+      amax = rotate_part<D0, TB, kRS>(xs, cos_t, sin_t, b, 0, tok0, n0, a.N, 0, HW, a.grid_h,
+                                      a.grid_w, z0);
     }
-    __syncthreads();
-    if (LAY == ROTATTN_LAYOUT_FP8)
-      store_qk_codes_f8<D>(codes, (s == 0 ? a.q4 : a.k4) + pad_row * D);
-    else if (LAY == ROTATTN_LAYOUT_FP6)
-      store_qk_codes_f6<D>(codes, (s == 0 ? a.q4 : a.k4) + pad_row * D);
+    {
+      float b[Part<D1>::KS][Part<D1>::JB];
+      const double* rp = a.rot64 + D0 * D0 + zero;
+      load_rot_frags<D1>(rp, b);
+      amax = fmaxf(amax, rotate_part<D1, TB, kRS>(xs, cos_h, sin_h, b, D0, tok0, n0, a.N, 1,
+                                                  HW, a.grid_h, a.grid_w, z1));
+    }
+    {
+      float b[Part<D1>::KS][Part<D1>::JB];
+      const double* rp = a.rot64 + D0 * D0 + D1 * D1 + zero;
+      load_rot_frags<D1>(rp, b);
+      amax = fmaxf(amax, rotate_part<D1, TB, kRS>(xs, cos_w, sin_w, b, D0 + D1, tok0, n0,
+                                                  a.N, 2, HW, a.grid_h, a.grid_w, z2));
+    }
+    block_scale(amax, red, inv, scale);
+    mid();
+    quant_part<D0, TB, F8>(z0, inv, 0, tok0, codes);
+    quant_part<D1, TB, F8>(z1, inv, D0, tok0, codes);
+    quant_part<D1, TB, F8>(z2, inv, D0 + D1, tok0, codes);
+  } else {
+    float z0[TB][Part<D0>::KS], z1[TB][Part<D1>::KS], z2[TB][Part<D1>::KS];
+    float amax = rope_part_a<D0, TB, kRS>(xs, cos_t, sin_t, 0, tok0, n0, a.N, 0, HW,
+                                          a.grid_h, a.grid_w, z0);
+    amax = fmaxf(amax, rope_part_a<D1, TB, kRS>(xs, cos_h, sin_h, D0, tok0, n0, a.N, 1, HW,
+                                                a.grid_h, a.grid_w, z1));
+    amax = fmaxf(amax, rope_part_a<D1, TB, kRS>(xs, cos_w, sin_w, D0 + D1, tok0, n0, a.N,
+                                                2, HW, a.grid_h, a.grid_w, z2));
+    block_scale(amax, red, inv, scale);
+    mid();
+    quant_part_a<D0, TB, F8>(z0, inv, 0, tok0, codes);
+    quant_part_a<D1, TB, F8>(z1, inv, D0, tok0, codes);
+    quant_part_a<D1, TB, F8>(z2, inv, D0 + D1, tok0, codes);
+  }
+  __syncthreads();
+  if (LAY == ROTATTN_LAYOUT_FP8)
+    store_qk_codes_f8<D>(codes, (s == 0 ? a.q4 : a.k4) + pad_row * D);
+  else if (LAY == ROTATTN_LAYOUT_FP6)
+    store_qk_codes_f6<D>(codes, (s == 0 ? a.q4 : a.k4) + pad_row * D);
+  else
+    store_qk_codes<D>(codes, (s == 0 ? a.q4 : a.k4) + pad_row * (D / 2));
+  if (threadIdx.x == 0) {
+    if (s == 0)
+      a.q_scale_l2[(size_t)bh * a.NB + blk] = scale * a.kappa;
     else
-      store_qk_codes<D>(codes, (s == 0 ? a.q4 : a.k4) + pad_row * (D / 2));
-    if (threadIdx.x == 0) {
-      if (s == 0)
-        a.q_scale_l2[(size_t)bh * a.NB + blk] = scale * a.kappa;
-      else
-        a.k_scale[(size_t)bh * a.NB + blk] = scale;
-    }
-  };
-  tensor(0);
-  tensor(1);
-  __syncthreads();
+      a.k_scale[(size_t)bh * a.NB + blk] = scale;
+  }
+}
 
-  // V: staged in the Q buffer (requested during the K pass), codes in place
-  wait_tiles();
-  __syncthreads();
-  int8_t* codes = (int8_t*)stage_q;
+// V of a head that is not a fallback head, from its staged fp16 rows xs:
+// block amax, codes (in place), stored transposed, block scale.
+template <int D, int LAY>
+__device__ __forceinline__ void quant_v_tile(const PrologueArgs& a, uint32_t* xs, float* red,
+                                             int blk, int bh) {
+  int8_t* codes = (int8_t*)xs;
   float scale;
-  v_codes<D, F8>(stage_q, red, codes, scale);
+  v_codes<D, LAY == ROTATTN_LAYOUT_FP8>(xs, red, codes, scale);
   __syncthreads();
   if (LAY == ROTATTN_LAYOUT_FP8)
     store_v_codes_f8<D>(codes, a.v4 + ((size_t)bh * a.NB + blk) * D * 128);
@@ -629,6 +615,31 @@ __device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* sta
   else
     store_v_codes<D>(codes, a.v4 + ((size_t)bh * a.NB + blk) * D * 64);
   if (threadIdx.x == 0) a.v_scale[(size_t)bh * a.NB + blk] = scale;
+}
+
+// A head that is not a fallback head: Q and K staged together, each tensor
+// inlined on its own (straight-line code, so nothing is hoisted across the two
+// tensors and kept live); V's rows are requested during the K pass, once every
+// wave is done with the Q codes in stage_q, and stream in while K is
+// quantized and stored.
+template <int D, int D0, int D1, int LAY, bool ROT>
+__device__ __forceinline__ void prologue_qk(const PrologueArgs& a, uint32_t* stage_q,
+                                            uint32_t* stage_k, float* red, int blk, int bh) {
+  const int n0 = blk * kBlock;
+  const int64_t head_in = a.in.head_offset(bh, a.H);
+  load_tile<D>(a.q + head_in, a.in.token, n0, a.N, stage_q);
+  load_tile<D>(a.k + head_in, a.in.token, n0, a.N, stage_k);
+  wait_tiles();
+  __syncthreads();
+  quant_qk_tile<D, D0, D1, LAY, ROT>(a, stage_q, red, 0, blk, bh, [] {});
+  quant_qk_tile<D, D0, D1, LAY, ROT>(a, stage_k, red, 1, blk, bh, [&] {
+    load_tile<D>(a.v + head_in, a.in.token, n0, a.N, stage_q);
+  });
+  __syncthreads();
+  // V: staged in the Q buffer, codes in place
+  wait_tiles();
+  __syncthreads();
+  quant_v_tile<D, LAY>(a, stage_q, red, blk, bh);
 }
 
 // Fallback head, RoPE of one staged tensor in place: thread (token n, half h)
@@ -787,6 +798,216 @@ hipError_t launch_prologue(int D, int dt, int BH, int layout, bool rot, const Pr
     launch_prologue_t<64, 24, 20>(layout, rot, grid, a, st);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ------------------------------------------------- QKV projection + prologue
+//
+// The step before the attention in a DiT block, fused: the QKV projection of
+// the block's input computes one 128-token x 128-channel tile (one head's Q,
+// K or V for one token block) per work-group, and the tile, rounded to fp16
+// in LDS, goes straight into the prologue's work above instead of through
+// HBM.  Projection: C^T = W_rows X_tokens^T on v_mfma_f32_32x32x16_f16 with
+// fp32 accumulation (W rows and X rows are both contiguous along the
+// reduction), 4 waves of 64 channels x 64 tokens.  Both tiles stream through
+// LDS in 64-deep stages (global_load_lds into XOR-swizzled rows), double
+// buffered, one barrier per stage.  + bias in fp32, one rounding to fp16; each
+// lane then holds 4 consecutive channels of one token per 32x32 block: two
+// dword writes of the staged row.
+
+constexpr int kGK = 64;                      // reduction depth of one stage
+constexpr int kGRow = kGK * 2;               // bytes of a tile row in a stage
+constexpr int kGTile = 128 * kGRow;          // bytes of one 128-row tile of a stage
+constexpr int kGStage = 2 * kGTile;          // W tile, then X tile
+
+// XOR swizzle of the 16-byte chunks of a 128-byte row: the 16 rows a
+// ds_read_b128 reads together land on 16 different chunk columns of the 64
+// banks (two rows per 256-byte bank row).
+__device__ __forceinline__ int gswz(int row) { return (row >> 1) & 7; }
+
+template <int D, int D0, int D1, int LAY, bool ROT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void k_qkv_proj_prologue(QkvProjArgs a) {
+  static_assert(D == 128, "one 128-channel head per work-group tile");
+  constexpr int kRS = D / 2 + 1;
+  constexpr int kStaged = kBlock * kRS * 4;            // bytes of the staged fp16 tile
+  static_assert(kStaged >= kGStage, "stage 0 sits inside the staging buffer");
+  // stage 0 in the buffer that later holds the staged tile, stage 1 in an
+  // array of its own: separate arrays let the compiler see that the next
+  // stage's loads into one never alias the operand reads of the other, so it
+  // does not wait for them before those reads
+  __shared__ __align__(16) uint8_t staged[kStaged];
+  __shared__ __align__(16) uint8_t stage1[kGStage];
+  __shared__ float red[16];
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+
+  // tile of this work-group: dispatch is round-robin over the 8 XCDs, so
+  // ids L, L+8, L+16, ... share an XCD (and its L2); each XCD works through
+  // groups of 64 tiles = 8 token blocks x 8 (tensor, head) pairs
+  const int L = blockIdx.x;
+  const int S = (L / 512) * 8 + (L % 8);        // group
+  const int r = (L / 8) % 64;                   // tile within the group
+  if (S >= a.SBT * a.SHT) return;
+  const int tb = (S % a.SBT) * 8 + (r % 8);     // token block over all batches
+  const int ht = (S / a.SBT) * 8 + (r / 8);     // (tensor, head) pair
+  const int H = a.p.H, NB = a.p.NB, N = a.p.N;
+  if (tb >= a.B * NB || ht >= 3 * H) return;
+  const int b = tb / NB, blk = tb % NB, t = ht / H, h = ht % H;
+  const int bh = b * H + h, n0 = blk * kBlock;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 31, hh = lane >> 5;
+  const int wm = w & 1, wn = w >> 1;            // wave's 64 channels, 64 tokens
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+
+  // stage loads: wave instruction i (0..3) fills the 1 KiB window 4i + w of a
+  // tile, rows 8 (4i + w) + lane/8; physical chunk lane%8 holds logical chunk
+  // (lane%8) ^ gswz(row), and rows 32 apart share the key, so instruction i's
+  // offset is instruction 0's plus 32 rows
+  const int lrow = 8 * w + lane / 8;
+  const int lchunk = (lane % 8) ^ gswz(lrow);
+  const size_t wrow_bytes = (size_t)a.C * 2;
+  const uint8_t* wbase = (const uint8_t*)(a.w + (size_t)ht * D * a.C);
+  const uint32_t woff = (uint32_t)(lrow * wrow_bytes) + 16 * lchunk;
+  const uint8_t* xbase = (const uint8_t*)(a.x + (int64_t)b * a.x_batch + (int64_t)n0 * a.x_token);
+  const int rmax = (N - n0 < kBlock ? N - n0 : kBlock) - 1;   // rows past N read the last valid row
+  uint32_t xoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = lrow + 32 * i;
+    xoff[i] = (uint32_t)((int64_t)(row < rmax ? row : rmax) * a.x_token * 2) + 16 * lchunk;
+  }
+  // uniform base in an SGPR pair + 32-bit lane offset (the saddr form); the
+  // offsets are made opaque per stage so that the loop does not keep per-lane
+  // 64-bit pointers in registers
+  auto gload = [&](int it, uint8_t* slot) {
+    uint32_t wo = woff, xo0 = xoff[0], xo1 = xoff[1], xo2 = xoff[2], xo3 = xoff[3];
+    asm volatile("" : "+v"(wo), "+v"(xo0), "+v"(xo1), "+v"(xo2), "+v"(xo3));
+    const uint32_t xo[4] = {xo0, xo1, xo2, xo3};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint8_t* wb = wbase + (size_t)it * kGRow + (size_t)32 * i * wrow_bytes;
+      const uint8_t* xb = xbase + (size_t)it * kGRow;
+      asm volatile("" : "+s"(wb), "+s"(xb));
+      __builtin_amdgcn_global_load_lds((const void*)(wb + wo),
+                                       (lds_ptr)(slot + (4 * i + wu) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(xb + xo[i]),
+                                       (lds_ptr)(slot + kGTile + (4 * i + wu) * 1024), 16, 0, 0);
+    }
+  };
+
+  // operand reads: logical chunk 2 ks + hh of row r sits at byte
+  // 16 ((2 ks + hh) ^ gswz(r)) = (16 (hh ^ gswz(r))) ^ 32 ks of the row;
+  // rows 32 apart share the key
+  uint32_t xa = (64 * wm + col) * kGRow + 16 * (hh ^ gswz(64 * wm + col));
+  uint32_t xb = kGTile + (64 * wn + col) * kGRow + 16 * (hh ^ gswz(64 * wn + col));
+  asm volatile("" : "+v"(xa), "+v"(xb));
+  v16f acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = v16f{0.0f};
+  const int kIters = a.C / kGK;
+
+  // stage it from `cur`: request stage it+1 into `next` (last read in
+  // iteration it-1, before the barrier), 16 MFMAs, wait, barrier
+  auto step = [&](int it, const uint8_t* cur, uint8_t* next) {
+    if (it + 1 < kIters) gload(it + 1, next);
+    // all 16 operand reads of the stage first, so that later k-steps' reads
+    // are in flight while the first MFMAs run
+    v8h fa[kGK / 16][2], fb[kGK / 16][2];
+#pragma unroll
+    for (int ks = 0; ks < kGK / 16; ++ks)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        fa[ks][m] = *(const v8h*)(cur + ((xa + 32 * kGRow * m) ^ (32 * ks)));
+        fb[ks][m] = *(const v8h*)(cur + ((xb + 32 * kGRow * m) ^ (32 * ks)));
+      }
+#pragma unroll
+    for (int ks = 0; ks < kGK / 16; ++ks)
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[ks][mi], fb[ks][ni], acc[mi][ni],
+                                                                0, 0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  gload(0, staged);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+#pragma unroll 1
+  for (int it = 0; it < kIters; it += 2) {
+    step(it, staged, stage1);
+    if (it + 1 < kIters) step(it + 1, stage1, staged);
+  }
+
+  // epilogue 1: + bias, fp16, staged rows (token n: kRS dwords, channel pairs);
+  // the last barrier above has every wave past its last stage read and every
+  // load landed
+  uint32_t* xs = (uint32_t*)staged;
+  const int nvalid = N - n0;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const int tok = 64 * wn + 32 * ni + col;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c0 = 64 * wm + 32 * mi + 8 * g + 4 * hh;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = acc[mi][ni][4 * g + e];
+          if (a.bias) v[e] += h2f(a.bias[(size_t)ht * D + c0 + e]);
+        }
+        uint32_t p0 = (uint32_t)f2h(v[0]) | ((uint32_t)f2h(v[1]) << 16);
+        uint32_t p1 = (uint32_t)f2h(v[2]) | ((uint32_t)f2h(v[3]) << 16);
+        if (tok >= nvalid) p0 = p1 = 0u;
+        xs[tok * kRS + c0 / 2] = p0;
+        xs[tok * kRS + c0 / 2 + 1] = p1;
+      }
+    }
+  __syncthreads();
+  const size_t BH = (size_t)a.B * H, N_pad = (size_t)NB * kBlock;
+  if (a.qkv_out) store_tile_all<D>(a.qkv_out + ((size_t)t * BH + bh) * N_pad * D, n0, xs);
+
+  // epilogue 2: the prologue's work on the staged tile
+  if (a.p.fallback.test(bh)) {
+    if (t < 2) {
+      rope_fallback<D, D0, D1>(a.p, xs, n0);
+      __syncthreads();
+      store_tile_all<D>((t == 0 ? a.p.q_rope : a.p.k_rope) + (size_t)bh * N_pad * D, n0, xs);
+    } else {
+      store_vt_tiles<D>(xs, a.p.v_t + ((size_t)bh * N_pad + n0) * D);
+    }
+  } else if (t < 2) {
+    quant_qk_tile<D, D0, D1, LAY, ROT>(a.p, xs, red, t, blk, bh, [] {});
+  } else {
+    quant_v_tile<D, LAY>(a.p, xs, red, blk, bh);
+  }
+}
+
+template <int LAY>
+static void launch_qkv_proj_l(bool rot, dim3 grid, const QkvProjArgs& a, hipStream_t st) {
+  if (rot)
+    hipLaunchKernelGGL((k_qkv_proj_prologue<128, 44, 42, LAY, true>), grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_qkv_proj_prologue<128, 44, 42, LAY, false>), grid, dim3(kThreads), 0, st, a);
+}
+
+hipError_t launch_qkv_proj(int D, int dt, int layout, bool rot, const QkvProjArgs& a,
+                           hipStream_t st) {
+  if (D != 128 || dt != 44) return hipErrorInvalidValue;
+  const int groups = a.SBT * a.SHT;
+  dim3 grid((unsigned)(((groups + 7) / 8) * 512));
+  if (layout == ROTATTN_LAYOUT_FP8)
+    launch_qkv_proj_l<ROTATTN_LAYOUT_FP8>(rot, grid, a, st);
+  else if (layout == ROTATTN_LAYOUT_FP6)
+    launch_qkv_proj_l<ROTATTN_LAYOUT_FP6>(rot, grid, a, st);
+  else
+    launch_qkv_proj_l<ROTATTN_LAYOUT_PACKED>(rot, grid, a, st);
   return hipGetLastError();
 }
 

@@ -222,13 +222,12 @@ int rotattn_prepare_qkv(const rotattn_shape* s, const uint16_t* q, const uint16_
 
 namespace {
 
-// Every argument check of the prologue, nothing enqueued.
-int check_prepare(const rotattn_shape* s, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                  const rotattn_strides* qkv_strides, const rotattn_rope_rot* rr,
-                  const uint8_t* fallback_mask_host, const rotattn_prepared* out, Strides* in) {
+// The prologue's checks of its tables and output buffers, nothing enqueued.
+int check_prepare_out(const rotattn_shape* s, const rotattn_rope_rot* rr,
+                      const uint8_t* fallback_mask_host, const rotattn_prepared* out) {
   const int st = rotattn_validate(s);
   if (st != ROTATTN_OK) return st;
-  if (!q || !k || !v || !rr || !out) return ROTATTN_E_NULL;
+  if (!rr || !out) return ROTATTN_E_NULL;
   if (!rr->cos_t || !rr->sin_t || !rr->cos_h || !rr->sin_h || !rr->cos_w || !rr->sin_w)
     return ROTATTN_E_NULL;
   // all three rotation matrices, or none (rotation merged into the tables)
@@ -250,14 +249,25 @@ int check_prepare(const rotattn_shape* s, const uint16_t* q, const uint16_t* k, 
     if (!aligned16(out->q_rope) || !aligned16(out->k_rope) || !aligned16(out->v_t))
       return ROTATTN_E_ALIGN;
   }
+  return ROTATTN_OK;
+}
+
+// Every argument check of the prologue, nothing enqueued.
+int check_prepare(const rotattn_shape* s, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                  const rotattn_strides* qkv_strides, const rotattn_rope_rot* rr,
+                  const uint8_t* fallback_mask_host, const rotattn_prepared* out, Strides* in) {
+  const int st = check_prepare_out(s, rr, fallback_mask_host, out);
+  if (st != ROTATTN_OK) return st;
+  if (!q || !k || !v) return ROTATTN_E_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return ROTATTN_E_ALIGN;
   return resolve_strides(s, qkv_strides, in);
 }
 
-int launch_prepare(const rotattn_shape* s, const uint16_t* q, const uint16_t* k,
-                   const uint16_t* v, const Strides& in, const rotattn_rope_rot* rr,
-                   const uint8_t* fallback_mask_host, const rotattn_prepared* out,
-                   hipStream_t stream) {
+// The prologue's arguments apart from its inputs (q, k, v, in left null), with
+// the rotation converted to fp64 on the stream when a head needs it.
+int prologue_args(const rotattn_shape* s, const rotattn_rope_rot* rr,
+                  const uint8_t* fallback_mask_host, const rotattn_prepared* out,
+                  hipStream_t stream, PrologueArgs* pa) {
   const bool rot = rr->rot_t != nullptr;
   const int BH = s->B * s->H;
   int n_fb = 0;
@@ -266,9 +276,9 @@ int launch_prepare(const rotattn_shape* s, const uint16_t* q, const uint16_t* k,
       launch_rot_to_f64(rr->rot_t, rr->rot_h, rr->rot_w, s->d_t, s->d_h, out->rot64, stream) !=
           hipSuccess)
     return ROTATTN_E_HIP;
-  PrologueArgs a;
-  a.q = q; a.k = k; a.v = v;
-  a.in = in;
+  PrologueArgs& a = *pa;
+  a.q = a.k = a.v = nullptr;
+  a.in = Strides{};
   a.H = s->H;
   a.cos_t = rr->cos_t; a.sin_t = rr->sin_t;
   a.cos_h = rr->cos_h; a.sin_h = rr->sin_h;
@@ -283,10 +293,41 @@ int launch_prepare(const rotattn_shape* s, const uint16_t* q, const uint16_t* k,
   a.grid_w = s->grid_w;
   a.kappa = rotattn_kappa_host(s->D);
   a.fallback = fb;
-  return launch_prologue(s->D, s->d_t, BH, out->layout, rot, a, stream) ==
-                 hipSuccess
+  return ROTATTN_OK;
+}
+
+int launch_prepare(const rotattn_shape* s, const uint16_t* q, const uint16_t* k,
+                   const uint16_t* v, const Strides& in, const rotattn_rope_rot* rr,
+                   const uint8_t* fallback_mask_host, const rotattn_prepared* out,
+                   hipStream_t stream) {
+  PrologueArgs a;
+  const int r = prologue_args(s, rr, fallback_mask_host, out, stream, &a);
+  if (r != ROTATTN_OK) return r;
+  a.q = q; a.k = k; a.v = v;
+  a.in = in;
+  return launch_prologue(s->D, s->d_t, s->B * s->H, out->layout, rr->rot_t != nullptr, a,
+                         stream) == hipSuccess
              ? ROTATTN_OK
              : ROTATTN_E_HIP;
+}
+
+// Every argument check of the fused QKV projection + prologue, nothing enqueued.
+int check_qkv_proj(const rotattn_shape* s, const uint16_t* x, int64_t x_batch, int64_t x_token,
+                   int32_t C, const uint16_t* w, const rotattn_rope_rot* rr,
+                   const uint8_t* fallback_mask_host, const rotattn_prepared* out,
+                   const uint16_t* qkv_out) {
+  const int st = check_prepare_out(s, rr, fallback_mask_host, out);
+  if (st != ROTATTN_OK) return st;
+  if (!x || !w) return ROTATTN_E_NULL;
+  if (s->D != 128 || s->d_t != 44) return ROTATTN_E_UNSUPPORTED;
+  // a work-group's row offsets within its 128 rows are 32-bit byte offsets
+  if (C < 64 || C % 64 != 0 || x_token < C || x_token > (1 << 24) || x_batch < 0)
+    return ROTATTN_E_ARG;
+  if (s->B > 1 && x_batch < (int64_t)s->N * x_token) return ROTATTN_E_ARG;
+  if (!aligned16(x) || !aligned16(w) || (qkv_out && !aligned16(qkv_out)) || x_token % 8 != 0 ||
+      x_batch % 8 != 0)
+    return ROTATTN_E_ALIGN;
+  return ROTATTN_OK;
 }
 
 // Every argument check of the INT4 attention, nothing enqueued.
@@ -437,6 +478,32 @@ int rotattn_prepare_qkv_strided(const rotattn_shape* s, const uint16_t* q, const
   const int st = check_prepare(s, q, k, v, qkv_strides, rr, fallback_mask_host, out, &in);
   if (st != ROTATTN_OK) return st;
   return launch_prepare(s, q, k, v, in, rr, fallback_mask_host, out, stream);
+}
+
+int rotattn_qkv_proj_prepare(const rotattn_shape* s, const uint16_t* x, int64_t x_batch,
+                             int64_t x_token, int32_t C, const uint16_t* w, const uint16_t* bias,
+                             const rotattn_rope_rot* rr, const uint8_t* fallback_mask_host,
+                             const rotattn_prepared* out, uint16_t* qkv_out,
+                             hipStream_t stream) {
+  const int st = check_qkv_proj(s, x, x_batch, x_token, C, w, rr, fallback_mask_host, out,
+                                qkv_out);
+  if (st != ROTATTN_OK) return st;
+  QkvProjArgs a;
+  const int r = prologue_args(s, rr, fallback_mask_host, out, stream, &a.p);
+  if (r != ROTATTN_OK) return r;
+  a.x = x;
+  a.x_batch = x_batch;
+  a.x_token = x_token;
+  a.w = w;
+  a.bias = bias;
+  a.qkv_out = qkv_out;
+  a.C = C;
+  a.B = s->B;
+  a.SBT = (s->B * nblocks(s) + 7) / 8;
+  a.SHT = (3 * s->H + 7) / 8;
+  return launch_qkv_proj(s->D, s->d_t, out->layout, rr->rot_t != nullptr, a, stream) == hipSuccess
+             ? ROTATTN_OK
+             : ROTATTN_E_HIP;
 }
 
 int rotattn_int4_fwd(const rotattn_shape* s, const rotattn_prepared* p,

@@ -136,6 +136,22 @@ struct StageArgs {
   int bh0;
 };
 
+// The QKV projection with the prologue as its epilogue: x [B][N][C] (channel
+// stride 1) times the fused weight w [3 H D][C] (row r = output channel r: Q
+// heads, then K, then V), + bias, rounded to fp16, then the prologue's work on
+// each 128-token x 128-channel tile.  Work-group tiles are grouped 8 token
+// blocks x 8 (tensor, head) pairs per XCD.
+struct QkvProjArgs {
+  const uint16_t* x;
+  int64_t x_batch, x_token;     // element strides of x
+  const uint16_t* w;
+  const uint16_t* bias;         // [3 H D] or null
+  uint16_t* qkv_out;            // optional [3][B H][N_pad][D] copy of the projection, or null
+  int C, B;
+  int SBT, SHT;                 // groups of 8 token blocks, of 8 (tensor, head) pairs
+  PrologueArgs p;               // q, k, v and in unused
+};
+
 // Launchers (each defined next to its kernel).  Return a hipError_t.
 hipError_t launch_rot_to_f64(const float* rt, const float* rh, const float* rw, int dt, int dh,
                              double* out, hipStream_t st);
@@ -145,6 +161,8 @@ hipError_t launch_int4(int D, int BH, const Int4Args& a, const Int4Debug* dbg, h
 hipError_t launch_int4_f8(int D, int BH, const Int4Args& a, const Int4Debug* dbg, hipStream_t st);
 hipError_t launch_fp16(int D, int BH, const Fp16Args& a, hipStream_t st);
 hipError_t launch_stage_fp16(int D, int nbh, const StageArgs& a, hipStream_t st);
+hipError_t launch_qkv_proj(int D, int dt, int layout, bool rot, const QkvProjArgs& a,
+                           hipStream_t st);
 hipError_t launch_pcode_sweep(bool f8, uint32_t mag_lo, uint32_t count, const float tau[15],
                               float log2_15, uint32_t* transitions, uint32_t max_transitions,
                               uint32_t* n_trans, hipStream_t st);

@@ -40,7 +40,7 @@ EXPORTS = sorted(["rotattn_validate", "rotattn_strerror", "rotattn_rope_tables_h
                   "rotattn_fp16_fwd_noalloc",
                   "rotattn_workspace_bytes", "rotattn_mixed_fwd", "rotattn_pcode_sweep",
                   "rotattn_pcode_eval", "rotattn_prepare_qkv_strided", "rotattn_int4_fwd_strided",
-                  "rotattn_mixed_fwd_strided"])
+                  "rotattn_mixed_fwd_strided", "rotattn_qkv_proj_prepare"])
 
 
 class Shape(C.Structure):
@@ -126,6 +126,9 @@ def lib() -> C.CDLL:
             "rotattn_mixed_fwd_strided": (C.c_int, [S, P, P, P, C.POINTER(Strides),
                                                     C.POINTER(RopeRot), P, P, C.c_size_t, P,
                                                     C.POINTER(Strides), P]),
+            "rotattn_qkv_proj_prepare": (C.c_int, [S, P, C.c_int64, C.c_int64, C.c_int32, P, P,
+                                                   C.POINTER(RopeRot), P, C.POINTER(Prepared), P,
+                                                   P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -292,6 +295,24 @@ def prepare_qkv(shape: Shape, q, k, v, rr: RopeRotDevice, prep: PreparedDevice, 
     check(lib().rotattn_prepare_qkv_strided(C.byref(shape), _ptr(q), _ptr(k), _ptr(v),
                                             _strides_arg(st), C.byref(rr.struct), m,
                                             C.byref(prep.struct), _stream(stream)), "prepare_qkv")
+
+
+def qkv_proj_prepare(shape: Shape, x, w, bias, rr: RopeRotDevice, prep: PreparedDevice,
+                     mask=None, qkv_out=None, stream=None) -> None:
+    """The QKV projection with the prologue as its epilogue: x [B][N][C] fp16
+    (channel stride 1), w [3*H*D][C] fp16 contiguous (Q heads, then K, then V),
+    bias [3*H*D] fp16 or None; qkv_out: None or fp16 [3][B*H][N_pad][D]."""
+    keep, m = _mask_arg(mask)
+    if x.dim() != 3 or x.stride(2) != 1:
+        raise ValueError("x must be [B][N][C] with channel stride 1")
+    if not w.is_contiguous() or w.dim() != 2 or w.shape[1] != x.shape[2]:
+        raise ValueError("w must be a contiguous [3*H*D][C] tensor")
+    check(lib().rotattn_qkv_proj_prepare(C.byref(shape), _ptr(x), x.stride(0), x.stride(1),
+                                         int(x.shape[2]), _ptr(w),
+                                         _ptr(bias) if bias is not None else None,
+                                         C.byref(rr.struct), m, C.byref(prep.struct),
+                                         _ptr(qkv_out) if qkv_out is not None else None,
+                                         _stream(stream)), "qkv_proj_prepare")
 
 
 def int4_fwd(shape: Shape, prep: PreparedDevice, o, mask=None, debug: Debug | None = None,

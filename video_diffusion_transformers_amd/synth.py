@@ -276,6 +276,32 @@ def sampled_rows(cfg: Config, h: int, count: int | None = None) -> np.ndarray:
     return np.sort(rng.choice(cfg.N, size=count, replace=False)).astype(np.int64)
 
 
+def projection_inputs(cfg: Config, C: int, kind: str = "normal", seed: int = 0):
+    """Seeded inputs of the QKV projection before the attention: x fp16
+    [B][N][C], w fp16 [3 H D][C] (Q heads, then K, then V), bias fp16 [3 H D].
+
+    "normal": x ~ N(0, 1), w ~ N(0, 1/C), bias ~ N(0, 0.05^2) (a random-weight
+    DiT layer: Q, K, V of unit scale).  "dyadic": x = a/64 and w = c/256,
+    bias = e/256 with small integers a, c, e, so that every partial sum of
+    a width up to 1024 is exact in float32 and the projection has one exact
+    value whatever the summation order."""
+    rng = _rng(cfg.cfg_seed, 7001, seed, C)
+    R = 3 * cfg.H * cfg.D
+    if kind == "normal":
+        x = _to_f16(rng.standard_normal((cfg.B, cfg.N, C)))
+        w = _to_f16(rng.standard_normal((R, C)) / np.sqrt(C))
+        b = _to_f16(0.05 * rng.standard_normal(R))
+    elif kind == "dyadic":
+        if C > 1024:
+            raise ValueError("dyadic projection inputs are exact up to C = 1024")
+        x = (rng.integers(-32, 33, (cfg.B, cfg.N, C)) / 64.0).astype(np.float16)
+        w = (rng.integers(-8, 9, (R, C)) / 256.0).astype(np.float16)
+        b = (rng.integers(-64, 65, R) / 256.0).astype(np.float16)
+    else:
+        raise ValueError(kind)
+    return x, w, b
+
+
 def custom_config(name, B, H, grid, D, split, dist="video", cfg_seed=11, **kw) -> Config:
     """A config outside the named set (ragged tails, fuzzing)."""
     return Config(name, B, H, tuple(grid), D, tuple(split), dist, cfg_seed, **kw)
