@@ -112,12 +112,18 @@ def test_fused_projection_prologue_exact_on_dyadic_inputs(layout):
     _unfused_equal(run, qkv_dev, SMALL_MASK, LAYOUTS[layout])
 
 
-def test_fused_projection_prologue_random_weights_small():
-    cfg, C = SMALL, 512
+# H = 3: an odd number of (tensor, head) pairs, so the 128 x 128 kernel runs alone
+ODD = synth.custom_config("proj_odd", 1, 3, (2, 9, 17), 128, (44, 42, 42), cfg_seed=63)
+
+
+@pytest.mark.parametrize("cfg,mask", [(SMALL, SMALL_MASK), (ODD, np.array([0, 0, 1], np.uint8))],
+                         ids=["H4", "H3"])
+def test_fused_projection_prologue_random_weights_small(cfg, mask):
+    C = 512
     x, w, b = synth.projection_inputs(cfg, C, "normal")
     run0 = Run(cfg, layout=LAYOUTS["fp6"])
-    run0.mask = SMALL_MASK
-    qkv_dev, got = _fused(run0, x, w, b, SMALL_MASK)
+    run0.mask = mask
+    qkv_dev, got = _fused(run0, x, w, b, mask)
     N = cfg.N
     # the projection: every output of every token
     proj = np.concatenate([got[t].reshape(cfg.H, run0.N_pad, cfg.D)[:, :N].transpose(1, 0, 2)
@@ -127,11 +133,11 @@ def test_fused_projection_prologue_random_weights_small():
     # the prologue on the kernel's own fp16 projection
     q, k, v = (got[t][:, :N].reshape(cfg.B, cfg.H, N, cfg.D) for t in range(3))
     run = Run(cfg, layout=LAYOUTS["fp6"], qkv=(q, k, v))
-    run.mask = SMALL_MASK
+    run.mask = mask
     run.prep = run0.prep
-    preps = {bh: run.oracle_prep(bh, fallback=bool(SMALL_MASK[bh])) for bh in range(cfg.BH)}
+    preps = {bh: run.oracle_prep(bh, fallback=bool(mask[bh])) for bh in range(cfg.BH)}
     check_prologue_heads(run, range(cfg.BH), "fp6", preps)
-    _unfused_equal(run0, qkv_dev, SMALL_MASK, LAYOUTS["fp6"])
+    _unfused_equal(run0, qkv_dev, mask, LAYOUTS["fp6"])
 
 
 def test_fused_projection_prologue_720p_width_5120():

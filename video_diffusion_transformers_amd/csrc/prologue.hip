@@ -32,6 +32,12 @@ namespace rotattn {
 constexpr int kThreads = 256;
 constexpr int kCodeStride = 132;   // bytes per row of the int8 code buffers (33 dwords: no bank conflicts)
 
+// Thread index within the 256 threads that run one prologue unit (a 128-token
+// block of one tensor of one head): the whole work-group in the kernels with
+// 256 threads, one half of it in the 512-thread QKV projection, whose halves
+// run two units side by side (same code path, so the same barriers).
+__device__ __forceinline__ int ltid() { return threadIdx.x & (kThreads - 1); }
+
 __device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 __device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
@@ -85,11 +91,11 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // Block-wide amax -> (inv, scale); every thread gets both.
 __device__ __forceinline__ void block_scale(float local, float* red, float& inv, float& scale) {
-  const int w = threadIdx.x >> 6;
+  const int w = ltid() >> 6;
   local = wave_max(local);
-  if ((threadIdx.x & 63) == 0) red[w] = local;
+  if ((ltid() & 63) == 0) red[w] = local;
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (ltid() == 0) {
     float amax = red[0];
     for (int i = 1; i < kThreads / 64; ++i) amax = fmaxf(amax, red[i]);
     red[8] = amax == 0.0f ? 0.0f : 7.0f / amax;   // correctly rounded division
@@ -128,7 +134,7 @@ struct Part {
 template <int DA>
 __device__ __forceinline__ void load_rot_frags(const double* rot,
                                                float (&b)[Part<DA>::KS][Part<DA>::JB]) {
-  const int l = threadIdx.x & 63;
+  const int l = ltid() & 63;
 #pragma unroll
   for (int ks = 0; ks < Part<DA>::KS; ++ks)
 #pragma unroll
@@ -179,7 +185,7 @@ __device__ __forceinline__ float rotate_part(const uint32_t* xs, const float* co
                                              int tok0, int n0, int N, int axis, int HW, int gh,
                                              int gw, float (&z)[TB][Part<DA>::JB][4]) {
   constexpr int KS = Part<DA>::KS, JB = Part<DA>::JB;
-  const int l = threadIdx.x & 63;
+  const int l = ltid() & 63;
   float amax = 0.0f;
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) {
@@ -232,7 +238,7 @@ __device__ __forceinline__ float rope_part_a(const uint32_t* xs, const float* co
                                              int axis, int HW, int gh, int gw,
                                              float (&z)[TB][Part<DA>::KS]) {
   constexpr int KS = Part<DA>::KS;
-  const int l = threadIdx.x & 63;
+  const int l = ltid() & 63;
   float amax = 0.0f;
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) {
@@ -255,7 +261,7 @@ __device__ __forceinline__ float rope_part_a(const uint32_t* xs, const float* co
 template <int DA, int TB, bool F8>
 __device__ __forceinline__ void quant_part_a(const float (&z)[TB][Part<DA>::KS], float inv, int off,
                                              int tok0, int8_t* codes) {
-  const int l = threadIdx.x & 63;
+  const int l = ltid() & 63;
   constexpr int KS = Part<DA>::KS;
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) {
@@ -275,7 +281,7 @@ __device__ __forceinline__ void quant_part_a(const float (&z)[TB][Part<DA>::KS],
 template <int DA, int TB, bool F8>
 __device__ __forceinline__ void quant_part(const float (&z)[TB][Part<DA>::JB][4], float inv,
                                            int off, int tok0, int8_t* codes) {
-  const int l = threadIdx.x & 63;
+  const int l = ltid() & 63;
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
@@ -302,7 +308,7 @@ __device__ __forceinline__ void v_codes(const uint32_t* xs, float* red, int8_t* 
                                         float& scale_out) {
   constexpr int kRS = D / 2 + 1;
   constexpr int C = D / 2;   // channels per thread
-  const int n = threadIdx.x & (kBlock - 1), h = threadIdx.x / kBlock;
+  const int n = ltid() & (kBlock - 1), h = ltid() / kBlock;
   const uint32_t* xrow = xs + n * kRS + h * (C / 2);
   float x[C];
   float amax = 0.0f;
@@ -337,8 +343,8 @@ __device__ __forceinline__ void load_tile(const uint16_t* src, int64_t row_strid
   constexpr int kRS = D / 2 + 1;
   constexpr int kW = kThreads / 64;
   typedef __attribute__((address_space(3))) void* lds_ptr;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = ltid() & 63;
+  const int w = __builtin_amdgcn_readfirstlane(ltid() >> 6);
 #pragma unroll 1
   for (int r = w; r < kBlock; r += kW) {
     if (n0 + r < N) {
@@ -359,7 +365,7 @@ template <int D>
 __device__ __forceinline__ void store_tile_all(uint16_t* dst, int n0, const uint32_t* xs) {
   constexpr int kChunks = D / 8;
   constexpr int kRS = D / 2 + 1;
-  for (int i = threadIdx.x; i < kBlock * kChunks; i += kThreads) {
+  for (int i = ltid(); i < kBlock * kChunks; i += kThreads) {
     const int r = i / kChunks, c = i % kChunks;
     const uint32_t* s_ = xs + r * kRS + 4 * c;
     *(uint4*)(dst + (size_t)(n0 + r) * D + 8 * c) = uint4{s_[0], s_[1], s_[2], s_[3]};
@@ -372,7 +378,7 @@ __device__ __forceinline__ void store_tile_all(uint16_t* dst, int n0, const uint
 template <int D>
 __device__ __forceinline__ void store_vt_tiles(const uint32_t* xs, uint16_t* dst) {
   constexpr int kRS = D / 2 + 1;
-  for (int item = threadIdx.x; item < 2 * D * 8; item += kThreads) {
+  for (int item = ltid(); item < 2 * D * 8; item += kThreads) {
     const int tl = item / (D * 8), d = (item / 8) % D, j = item % 8;   // 8 positions per item
     uint32_t w[4];
 #pragma unroll
@@ -396,7 +402,7 @@ __device__ __forceinline__ void store_vt_tiles(const uint32_t* xs, uint16_t* dst
 template <int D>
 __device__ __forceinline__ void store_qk_codes(const int8_t* codes, uint8_t* dst) {
   constexpr int kDw = D / 8;   // packed dwords per token
-  for (int i = threadIdx.x; i < kBlock * kDw; i += kThreads) {
+  for (int i = ltid(); i < kBlock * kDw; i += kThreads) {
     const int n = i / kDw, g = i % kDw;
     const uint32_t lo = *(const uint32_t*)(codes + n * kCodeStride + 8 * g);
     const uint32_t hi = *(const uint32_t*)(codes + n * kCodeStride + 8 * g + 4);
@@ -408,7 +414,7 @@ __device__ __forceinline__ void store_qk_codes(const int8_t* codes, uint8_t* dst
 template <int D>
 __device__ __forceinline__ void store_qk_codes_f8(const int8_t* codes, uint8_t* dst) {
   constexpr int kDw = D / 4;
-  for (int i = threadIdx.x; i < kBlock * kDw; i += kThreads) {
+  for (int i = ltid(); i < kBlock * kDw; i += kThreads) {
     const int n = i / kDw, g = i % kDw;
     *(uint32_t*)(dst + (size_t)n * D + 4 * g) = *(const uint32_t*)(codes + n * kCodeStride + 4 * g);
   }
@@ -420,7 +426,7 @@ __device__ __forceinline__ void store_qk_codes_f8(const int8_t* codes, uint8_t* 
 // whole: j%4 is the byte.
 template <int D>
 __device__ __forceinline__ void store_v_codes_f8(const int8_t* codesT, uint8_t* dst) {
-  for (int i = threadIdx.x; i < D * 32; i += kThreads) {
+  for (int i = ltid(); i < D * 32; i += kThreads) {
     const int d = i / 32, q = i % 32;                 // output dword q of row d
     const int c = q / 16, h = (q / 8) & 1, j = 4 * (q & 7);
     const int key = 64 * c + 32 * h + 8 * ((j % 16) / 4) + 4 * (j / 16);
@@ -465,7 +471,7 @@ __device__ __forceinline__ void pack_fields32(const uint32_t (&f)[8], uint32_t (
 template <int D>
 __device__ __forceinline__ void store_qk_codes_f6(const int8_t* codes, uint8_t* dst) {
   constexpr int kG = D / 32;   // groups per token
-  for (int i = threadIdx.x; i < kBlock * kG; i += kThreads) {
+  for (int i = ltid(); i < kBlock * kG; i += kThreads) {
     const int n = i / kG, g = i % kG;
     const uint32_t* src = (const uint32_t*)(codes + n * kCodeStride + 32 * g);
     uint32_t f[8], o[6];
@@ -486,7 +492,7 @@ __device__ __forceinline__ void store_qk_codes_f6(const int8_t* codes, uint8_t* 
 // The fields come four at a time: k%4 is the byte of a code dword.
 template <int D>
 __device__ __forceinline__ void store_v_codes_f6(const int8_t* codesT, uint8_t* dst) {
-  for (int i = threadIdx.x; i < D * 4; i += kThreads) {
+  for (int i = ltid(); i < D * 4; i += kThreads) {
     const int d = i / 4, g = i % 4, c = g / 2, h = g % 2;
     const int8_t* row = codesT + d * kCodeStride + 64 * c + 4 * h;
     uint32_t f[8], o[6];
@@ -502,7 +508,7 @@ __device__ __forceinline__ void store_v_codes_f6(const int8_t* codesT, uint8_t* 
 // V codes (LDS, [channel][token]) -> packed V^T block [D][64] in global memory.
 template <int D>
 __device__ __forceinline__ void store_v_codes(const int8_t* codesT, uint8_t* dst) {
-  for (int i = threadIdx.x; i < D * 16; i += kThreads) {
+  for (int i = ltid(); i < D * 16; i += kThreads) {
     const int d = i / 16, g = i % 16;
     const uint32_t lo = *(const uint32_t*)(codesT + d * kCodeStride + 8 * g);
     const uint32_t hi = *(const uint32_t*)(codesT + d * kCodeStride + 8 * g + 4);
@@ -524,7 +530,7 @@ __device__ __forceinline__ void quant_qk_tile(const PrologueArgs& a, uint32_t* x
   constexpr int TB = kBlock / 16 / (kThreads / 64);   // 16-token groups per wave
   // LDS codes: E4M3 bytes for the FP8 layout, int8 for the others
   constexpr bool F8 = LAY == ROTATTN_LAYOUT_FP8;
-  const int w = threadIdx.x >> 6;
+  const int w = ltid() >> 6;
   const int tok0 = 16 * TB * w;
   const int n0 = blk * kBlock;
   const int HW = a.grid_h * a.grid_w;
@@ -591,7 +597,7 @@ __device__ __forceinline__ void quant_qk_tile(const PrologueArgs& a, uint32_t* x
     store_qk_codes_f6<D>(codes, (s == 0 ? a.q4 : a.k4) + pad_row * D);
   else
     store_qk_codes<D>(codes, (s == 0 ? a.q4 : a.k4) + pad_row * (D / 2));
-  if (threadIdx.x == 0) {
+  if (ltid() == 0) {
     if (s == 0)
       a.q_scale_l2[(size_t)bh * a.NB + blk] = scale * a.kappa;
     else
@@ -614,7 +620,7 @@ __device__ __forceinline__ void quant_v_tile(const PrologueArgs& a, uint32_t* xs
     store_v_codes_f6<D>(codes, a.v4 + ((size_t)bh * a.NB + blk) * D * 128);
   else
     store_v_codes<D>(codes, a.v4 + ((size_t)bh * a.NB + blk) * D * 64);
-  if (threadIdx.x == 0) a.v_scale[(size_t)bh * a.NB + blk] = scale;
+  if (ltid() == 0) a.v_scale[(size_t)bh * a.NB + blk] = scale;
 }
 
 // A head that is not a fallback head: Q and K staged together, each tensor
@@ -650,8 +656,8 @@ template <int D, int D0, int D1>
 __device__ __forceinline__ void rope_fallback(const PrologueArgs& a, uint32_t* xs, int n0) {
   constexpr int kRS = D / 2 + 1;
   constexpr int NY = D0 > 2 * D1 ? D0 : 2 * D1;
-  const int n = threadIdx.x & (kBlock - 1);
-  const int half = __builtin_amdgcn_readfirstlane(threadIdx.x / kBlock);
+  const int n = ltid() & (kBlock - 1);
+  const int half = __builtin_amdgcn_readfirstlane(ltid() / kBlock);
   const int HW = a.grid_h * a.grid_w;
   uint32_t* xrow = xs + n * kRS;
   float y[NY];
@@ -844,14 +850,23 @@ void k_qkv_proj_prologue(QkvProjArgs a) {
   // tile of this work-group: dispatch is round-robin over the 8 XCDs, so
   // ids L, L+8, L+16, ... share an XCD (and its L2); each XCD works through
   // groups of 64 tiles = 8 token blocks x 8 (tensor, head) pairs
-  const int L = blockIdx.x;
-  const int S = (L / 512) * 8 + (L % 8);        // group
-  const int r = (L / 8) % 64;                   // tile within the group
-  if (S >= a.SBT * a.SHT) return;
-  const int tb = (S % a.SBT) * 8 + (r % 8);     // token block over all batches
-  const int ht = (S / a.SBT) * 8 + (r / 8);     // (tensor, head) pair
   const int H = a.p.H, NB = a.p.NB, N = a.p.N;
-  if (tb >= a.B * NB || ht >= 3 * H) return;
+  int tb, ht;                                   // token block over all batches, (tensor, head) pair
+  if (a.last_block_only) {
+    // the blocks the 256 x 256 kernel leaves over: the last of each batch entry
+    const int L = blockIdx.x;
+    if (L >= a.B * 3 * H) return;
+    tb = (L / (3 * H)) * NB + NB - 1;
+    ht = L % (3 * H);
+  } else {
+    const int L = blockIdx.x;
+    const int S = (L / 512) * 8 + (L % 8);      // group
+    const int r = (L / 8) % 64;                 // tile within the group
+    if (S >= a.SBT * a.SHT) return;
+    tb = (S % a.SBT) * 8 + (r % 8);
+    ht = (S / a.SBT) * 8 + (r / 8);
+    if (tb >= a.B * NB || ht >= 3 * H) return;
+  }
   const int b = tb / NB, blk = tb % NB, t = ht / H, h = ht % H;
   const int bh = b * H + h, n0 = blk * kBlock;
 
@@ -989,6 +1004,198 @@ void k_qkv_proj_prologue(QkvProjArgs a) {
   }
 }
 
+// The same projection on a 256-channel x 256-token work-group tile: two
+// (tensor, head) pairs 2j, 2j+1 (rows 256 j .. 256 j + 255 of W, contiguous) x
+// two token blocks 2i, 2i+1 of one batch entry, 8 waves of 64 channels x 128
+// tokens.  A 64-deep stage brings 64 KiB for 8.4 MFLOP, half the bytes per
+// flop of the 128 x 128 tile, whose feed is bounded by the L2.  One
+// work-group per CU (two buffers of staged + packed tile size, each holding
+// one stage of the double-buffered projection).  Epilogue in two rounds on the
+// two halves of the work-group (waves 0-3: token block 2i, waves 4-7: 2i+1),
+// each half running one prologue unit: round one the first (tensor, head),
+// whose fp16 tiles go straight to the staged layout, round two the second,
+// whose tiles wait packed (XOR-swizzled rows) beside them.  Both halves of a
+// round work on the same tensor of the same head, so they take the same code
+// path and meet the same barriers.
+template <int D, int D0, int D1, int LAY, bool ROT>
+__global__ __launch_bounds__(2 * kThreads, 1)
+void k_qkv_proj_prologue2(QkvProjArgs a) {
+  static_assert(D == 128, "one 128-channel head per prologue unit");
+  constexpr int kRS = D / 2 + 1;
+  constexpr int kStaged = kBlock * kRS * 4;            // staged fp16 tile (padded rows)
+  constexpr int kPacked = kBlock * D * 2;              // packed fp16 tile
+  constexpr int kBuf = kStaged + kPacked;
+  constexpr int kT2 = 256 * kGRow;                     // one 256-row tile of a stage
+  static_assert(kBuf >= 2 * kT2, "a stage fits in one buffer");
+  // buffer h: stage h of the projection, then the staged tile of token block
+  // 2i+h and the packed tile of the second (tensor, head); separate arrays,
+  // so that the compiler sees that the next stage's loads never alias the
+  // operand reads of the current one
+  __shared__ __align__(16) uint8_t buf0[kBuf];
+  __shared__ __align__(16) uint8_t buf1[kBuf];
+  __shared__ float red[32];
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+
+  // tile: each XCD works through groups of 32 tiles = 8 token-block pairs x
+  // 4 pairs of (tensor, head) pairs
+  const int H = a.p.H, NB = a.p.NB, N = a.p.N;
+  const int TPB = NB / 2;                              // token-block pairs per batch entry
+  const int L = blockIdx.x;
+  const int S = (L / 256) * 8 + (L % 8);
+  const int r = (L / 8) % 32;
+  if (S >= a.SBT * a.SHT) return;
+  const int tp = (S % a.SBT) * 8 + (r % 8);
+  const int hp = (S / a.SBT) * 4 + (r / 8);
+  if (tp >= a.B * TPB || hp >= 3 * H / 2) return;
+  const int b = tp / TPB, blk0 = 2 * (tp % TPB), ht0 = 2 * hp;
+  const int n00 = blk0 * kBlock;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;   // 8 waves
+  const int col = lane & 31, hh = lane >> 5;
+  const int wc = w & 3, wt = w >> 2;           // wave's 64 channels of 256, token block of the pair
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+
+  // stage loads: wave instruction i (0..3) fills the 1 KiB window 8i + w of a
+  // 256-row tile, rows 8 (8i + w) + lane/8; rows 64 apart share the swizzle key
+  const int lrow = 8 * w + lane / 8;
+  const int lchunk = (lane % 8) ^ gswz(lrow);
+  const size_t wrow_bytes = (size_t)a.C * 2;
+  const uint8_t* wbase = (const uint8_t*)(a.w + (size_t)ht0 * D * a.C);
+  const uint32_t woff = (uint32_t)(lrow * wrow_bytes) + 16 * lchunk;
+  const uint8_t* xbase = (const uint8_t*)(a.x + (int64_t)b * a.x_batch + (int64_t)n00 * a.x_token);
+  const int rmax = (N - n00 < 2 * kBlock ? N - n00 : 2 * kBlock) - 1;
+  uint32_t xoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = lrow + 64 * i;
+    xoff[i] = (uint32_t)((int64_t)(row < rmax ? row : rmax) * a.x_token * 2) + 16 * lchunk;
+  }
+  auto gload = [&](int it, uint8_t* slot) {
+    uint32_t wo = woff, xo0 = xoff[0], xo1 = xoff[1], xo2 = xoff[2], xo3 = xoff[3];
+    asm volatile("" : "+v"(wo), "+v"(xo0), "+v"(xo1), "+v"(xo2), "+v"(xo3));
+    const uint32_t xo[4] = {xo0, xo1, xo2, xo3};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint8_t* wb = wbase + (size_t)it * kGRow + (size_t)64 * i * wrow_bytes;
+      const uint8_t* xb = xbase + (size_t)it * kGRow;
+      asm volatile("" : "+s"(wb), "+s"(xb));
+      __builtin_amdgcn_global_load_lds((const void*)(wb + wo),
+                                       (lds_ptr)(slot + (8 * i + wu) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(xb + xo[i]),
+                                       (lds_ptr)(slot + kT2 + (8 * i + wu) * 1024), 16, 0, 0);
+    }
+  };
+
+  uint32_t xa = (64 * wc + col) * kGRow + 16 * (hh ^ gswz(64 * wc + col));
+  uint32_t xb = kT2 + (128 * wt + col) * kGRow + 16 * (hh ^ gswz(128 * wt + col));
+  asm volatile("" : "+v"(xa), "+v"(xb));
+  v16f acc[2][4];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v16f{0.0f};
+  const int kIters = a.C / kGK;
+
+  // stage it from `cur`: request stage it+1 into `next` (last read in
+  // iteration it-1, before the barrier), 32 MFMAs, wait, barrier
+  auto step = [&](int it, const uint8_t* cur, uint8_t* next) {
+    if (it + 1 < kIters) gload(it + 1, next);
+#pragma unroll
+    for (int ks = 0; ks < kGK / 16; ++ks) {
+      v8h fa[2], fb[4];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) fa[m] = *(const v8h*)(cur + ((xa + 32 * kGRow * m) ^ (32 * ks)));
+#pragma unroll
+      for (int m = 0; m < 4; ++m) fb[m] = *(const v8h*)(cur + ((xb + 32 * kGRow * m) ^ (32 * ks)));
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  gload(0, buf0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+#pragma unroll 1
+  for (int it = 0; it < kIters; it += 2) {
+    step(it, buf0, buf1);
+    if (it + 1 < kIters) step(it + 1, buf1, buf0);
+  }
+
+  // epilogue 1: + bias, fp16; the first (tensor, head)'s channels (waves with
+  // wc < 2) into the staged layout of buffer wt, the second's packed beside it
+  // (the last barrier above has every stage read done)
+  uint8_t* mybuf = wt == 0 ? buf0 : buf1;
+  uint32_t* xs = (uint32_t*)mybuf;
+  uint32_t* pk = (uint32_t*)(mybuf + kStaged);
+  const int second = wc >> 1;
+  const int htw = ht0 + second;
+  const int nvalid = N - (n00 + kBlock * wt);
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int tok = 32 * ni + col;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c0 = 64 * (wc & 1) + 32 * mi + 8 * g + 4 * hh;   // channel within the head
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = acc[mi][ni][4 * g + e];
+          if (a.bias) v[e] += h2f(a.bias[(size_t)htw * D + c0 + e]);
+        }
+        uint32_t p0 = (uint32_t)f2h(v[0]) | ((uint32_t)f2h(v[1]) << 16);
+        uint32_t p1 = (uint32_t)f2h(v[2]) | ((uint32_t)f2h(v[3]) << 16);
+        if (tok >= nvalid) p0 = p1 = 0u;
+        if (second == 0) {
+          xs[tok * kRS + c0 / 2] = p0;
+          xs[tok * kRS + c0 / 2 + 1] = p1;
+        } else {
+          // packed row of 64 dwords, dword d at d ^ (tok & 63): conflict-free
+          // writes down a column of tokens and reads along a row
+          pk[tok * 64 + ((c0 / 2) ^ (tok & 63))] = p0;
+          pk[tok * 64 + ((c0 / 2 + 1) ^ (tok & 63))] = p1;
+        }
+      }
+    }
+  __syncthreads();
+
+  // epilogue 2: two rounds of prologue units, half wt on token block blk0+wt
+  const size_t BH = (size_t)a.B * H, N_pad = (size_t)NB * kBlock;
+  const int blk = blk0 + wt, n0 = blk * kBlock;
+  float* myred = red + 16 * wt;
+  auto unit = [&](int ht) {
+    const int t = ht / H, bh = b * H + ht % H;
+    if (a.qkv_out) store_tile_all<D>(a.qkv_out + ((size_t)t * BH + bh) * N_pad * D, n0, xs);
+    if (a.p.fallback.test(bh)) {
+      if (t < 2) {
+        rope_fallback<D, D0, D1>(a.p, xs, n0);
+        __syncthreads();
+        store_tile_all<D>((t == 0 ? a.p.q_rope : a.p.k_rope) + (size_t)bh * N_pad * D, n0, xs);
+      } else {
+        store_vt_tiles<D>(xs, a.p.v_t + ((size_t)bh * N_pad + n0) * D);
+      }
+    } else if (t < 2) {
+      quant_qk_tile<D, D0, D1, LAY, ROT>(a.p, xs, myred, t, blk, bh, [] {});
+    } else {
+      quant_v_tile<D, LAY>(a.p, xs, myred, blk, bh);
+    }
+  };
+  unit(ht0);
+  __syncthreads();
+  // the second (tensor, head)'s tile of this half: packed -> staged layout
+  for (int i = ltid(); i < kBlock * 64; i += kThreads) {
+    const int tok = i >> 6, d = i & 63;
+    xs[tok * kRS + d] = pk[tok * 64 + (d ^ (tok & 63))];
+  }
+  __syncthreads();
+  unit(ht0 + 1);
+}
+
 template <int LAY>
 static void launch_qkv_proj_l(bool rot, dim3 grid, const QkvProjArgs& a, hipStream_t st) {
   if (rot)
@@ -997,17 +1204,49 @@ static void launch_qkv_proj_l(bool rot, dim3 grid, const QkvProjArgs& a, hipStre
     hipLaunchKernelGGL((k_qkv_proj_prologue<128, 44, 42, LAY, false>), grid, dim3(kThreads), 0, st, a);
 }
 
+template <int LAY>
+static void launch_qkv_proj2_l(bool rot, dim3 grid, const QkvProjArgs& a, hipStream_t st) {
+  if (rot)
+    hipLaunchKernelGGL((k_qkv_proj_prologue2<128, 44, 42, LAY, true>), grid, dim3(2 * kThreads), 0,
+                       st, a);
+  else
+    hipLaunchKernelGGL((k_qkv_proj_prologue2<128, 44, 42, LAY, false>), grid, dim3(2 * kThreads), 0,
+                       st, a);
+}
+
+template <int LAY>
+static void launch_qkv_proj_all(bool rot, const QkvProjArgs& a0, hipStream_t st) {
+  const int H = a0.p.H, NB = a0.p.NB;
+  if (H % 2 == 0 && NB >= 2) {
+    // 256 x 256 tiles over the token-block pairs, then the 128 x 128 kernel
+    // on the last block of each batch entry when NB is odd
+    QkvProjArgs a = a0;
+    a.SBT = (a.B * (NB / 2) + 7) / 8;
+    a.SHT = (3 * H / 2 + 3) / 4;
+    a.last_block_only = 0;
+    launch_qkv_proj2_l<LAY>(rot, dim3((unsigned)(((a.SBT * a.SHT + 7) / 8) * 256)), a, st);
+    if (NB % 2 == 1) {
+      a.last_block_only = 1;
+      launch_qkv_proj_l<LAY>(rot, dim3((unsigned)(a.B * 3 * H)), a, st);
+    }
+  } else {
+    QkvProjArgs a = a0;
+    a.SBT = (a.B * NB + 7) / 8;
+    a.SHT = (3 * H + 7) / 8;
+    a.last_block_only = 0;
+    launch_qkv_proj_l<LAY>(rot, dim3((unsigned)(((a.SBT * a.SHT + 7) / 8) * 512)), a, st);
+  }
+}
+
 hipError_t launch_qkv_proj(int D, int dt, int layout, bool rot, const QkvProjArgs& a,
                            hipStream_t st) {
   if (D != 128 || dt != 44) return hipErrorInvalidValue;
-  const int groups = a.SBT * a.SHT;
-  dim3 grid((unsigned)(((groups + 7) / 8) * 512));
   if (layout == ROTATTN_LAYOUT_FP8)
-    launch_qkv_proj_l<ROTATTN_LAYOUT_FP8>(rot, grid, a, st);
+    launch_qkv_proj_all<ROTATTN_LAYOUT_FP8>(rot, a, st);
   else if (layout == ROTATTN_LAYOUT_FP6)
-    launch_qkv_proj_l<ROTATTN_LAYOUT_FP6>(rot, grid, a, st);
+    launch_qkv_proj_all<ROTATTN_LAYOUT_FP6>(rot, a, st);
   else
-    launch_qkv_proj_l<ROTATTN_LAYOUT_PACKED>(rot, grid, a, st);
+    launch_qkv_proj_all<ROTATTN_LAYOUT_PACKED>(rot, a, st);
   return hipGetLastError();
 }
 

@@ -499,8 +499,7 @@ int rotattn_qkv_proj_prepare(const rotattn_shape* s, const uint16_t* x, int64_t 
   a.qkv_out = qkv_out;
   a.C = C;
   a.B = s->B;
-  a.SBT = (s->B * nblocks(s) + 7) / 8;
-  a.SHT = (3 * s->H + 7) / 8;
+  a.SBT = a.SHT = a.last_block_only = 0;   // set per launch
   return launch_qkv_proj(s->D, s->d_t, out->layout, rr->rot_t != nullptr, a, stream) == hipSuccess
              ? ROTATTN_OK
              : ROTATTN_E_HIP;

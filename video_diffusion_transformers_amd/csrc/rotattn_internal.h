@@ -148,7 +148,8 @@ struct QkvProjArgs {
   const uint16_t* bias;         // [3 H D] or null
   uint16_t* qkv_out;            // optional [3][B H][N_pad][D] copy of the projection, or null
   int C, B;
-  int SBT, SHT;                 // groups of 8 token blocks, of 8 (tensor, head) pairs
+  int SBT, SHT;                 // tile groups along tokens and along (tensor, head) pairs
+  int last_block_only;          // 128 x 128 kernel: only the last block of each batch entry
   PrologueArgs p;               // q, k, v and in unused
 };
 
