@@ -5,7 +5,10 @@
 // zeros) and V^T per 64-key tile in the operand order of the P.V product.
 // O = softmax(Q'K'^T/sqrt(D)) V.
 //
-// One work-group = 4 waves x 32 queries, two work-groups per CU.  Per 64-key
+// One work-group = 8 waves x 32 queries, one per CU (two waves per SIMD, so
+// that one wave's softmax overlaps the other's MFMAs); the 8 waves share every
+// K and V^T tile the work-group brings into LDS (4-wave work-groups, two per
+// CU, moved twice the tile bytes per flop and ran 1.5% slower).  Per 64-key
 // tile: S^T = K Q'^T on v_mfma_f32_32x32x16_f16 (each lane then holds one
 // query's scores in the layout of the P^T operand), fp32 online softmax in the
 // log2 domain (kappa = log2(e)/sqrt(D)), P rounded to fp16 in registers,
@@ -19,7 +22,7 @@
 
 namespace rotattn {
 
-constexpr int kFThreads = 256;
+constexpr int kFThreads = 512;   // 8 waves: 256 queries per work-group
 constexpr int kKT = 64;   // keys per tile
 
 typedef float v2f __attribute__((ext_vector_type(2)));
@@ -160,20 +163,23 @@ struct Fp16Kernel {
 
     v8h qf[KS];
     {
-      const uint16_t* qrow = a.q + (head_pad + (size_t)qb * kBlock + 32 * w + col) * D;
+      // queries past N (the last work-group's second half when N_pad / 128 is
+      // odd) read the last valid row and are not written
+      const int qrow_i = qb * (NW * 32) + 32 * w + col;
+      const uint16_t* qrow = a.q + (head_pad + (size_t)(qrow_i < N ? qrow_i : N - 1)) * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const v8h*)(qrow + 16 * ks + 8 * hh);
     }
 
     // tile loads straight into LDS: wave w, instruction i fills chunks
-    // (NW i + w) * 64 + lane of the tile.  Instruction i lands 16 K rows (32
+    // (NW i + w) * 64 + lane of the tile.  Instruction i lands 32 K rows (64
     // V^T rows) further down than instruction 0 and the swizzle keys repeat
-    // with that period, so its per-lane byte offset is instruction 0's plus
-    // 4096 i: the uniform part goes to the scalar base (saddr form) and one
+    // with periods dividing that, so its per-lane byte offset is instruction
+    // 0's plus 8 KiB i: the uniform part goes to the scalar base (saddr form) and one
     // 32-bit offset register per tensor remains.
     typedef __attribute__((address_space(3))) void* lds_ptr;
     const int wu = __builtin_amdgcn_readfirstlane(w);
-    static_assert(NW * 64 * 16 == 4096, "4 KiB per load instruction of the work-group");
+    constexpr uint32_t kInstr = NW * 64 * 16;   // bytes per load instruction of the work-group
     uint32_t koff0, voff0;
     {
       const int pc = w * 64 + lane;   // physical chunk of instruction 0
@@ -189,7 +195,7 @@ struct Fp16Kernel {
       asm volatile("" : "+v"(ko));
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const uint8_t* kbi = kb + 4096 * i;
+        const uint8_t* kbi = kb + kInstr * i;
         asm volatile("" : "+s"(kbi));
         __builtin_amdgcn_global_load_lds((const void*)(kbi + ko),
                                          (lds_ptr)(dst + (NW * i + wu) * 1024), 16, 0, 0);
@@ -201,7 +207,7 @@ struct Fp16Kernel {
       asm volatile("" : "+v"(vo));
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const uint8_t* vbi = vb + 4096 * i;
+        const uint8_t* vbi = vb + kInstr * i;
         asm volatile("" : "+s"(vbi));
         __builtin_amdgcn_global_load_lds((const void*)(vbi + vo),
                                          (lds_ptr)(dst + (NW * i + wu) * 1024), 16, 0, 0);
@@ -251,7 +257,7 @@ struct Fp16Kernel {
     }
 
     l += other_half(l);
-    const int query = qb * kBlock + 32 * w + col;
+    const int query = qb * (NW * 32) + 32 * w + col;
     if (query < N) {
       const float il = 1.0f / l;
       uint16_t* orow = a.o + a.os.head_offset(gbh, a.H) + (int64_t)query * a.os.token;
@@ -271,13 +277,13 @@ struct Fp16Kernel {
 };
 
 template <int D>
-__global__ __launch_bounds__(kFThreads, 2) void k_fp16_attn(Fp16Args a) {
+__global__ __launch_bounds__(kFThreads, 1) void k_fp16_attn(Fp16Args a) {
   Fp16Kernel<D>::run(a);
 }
 
 // BH: heads in the buffers (global heads a.bh0 .. a.bh0 + BH - 1)
 hipError_t launch_fp16(int D, int BH, const Fp16Args& a, hipStream_t st) {
-  dim3 grid(a.NB, BH);
+  dim3 grid((a.NB * kBlock + kFThreads / 2 - 1) / (kFThreads / 2), BH);   // 256 queries each
   if (D == 128)
     hipLaunchKernelGGL(k_fp16_attn<128>, grid, dim3(kFThreads), 0, st, a);
   else
