@@ -151,8 +151,9 @@ typedef enum rotattn_layout {
  *          FP6: [B*H][NB][D][128]: row d in four groups g = 2c+h (c, h in
  *          {0,1}); field k of group g is key 64c + 32(k/16) + 8(k%16/4) +
  *          4h + k%4.
- *  rot64:  library scratch, 3*64*64 doubles: the rotation in fp64, refilled
- *          by every rotattn_prepare_qkv call.
+ *  rot64:  library scratch (its size is part of rotattn_prepared_bytes): the
+ *          rotation and the RoPE tables rearranged for the prologue, refilled
+ *          by every rotattn_prepare_qkv call that has a head to quantize.
  *  q_scale_l2, k_scale, v_scale: [B*H][NB] fp32 block scales (amax/7).
  *          q_scale_l2 = fl(q_scale * kappa), kappa = fl32(log2(e)/sqrt(D)), so
  *          that 2^(I * q_scale_l2 * k_scale) = exp(QK^T / sqrt(D)).

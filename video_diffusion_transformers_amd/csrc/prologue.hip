@@ -75,11 +75,52 @@ __global__ void k_rot_to_f64(const float* rt, const float* rh, const float* rw, 
     const int k = j / w_, r = j % w_;              // stored [k][r] from R[r][k]
     out[i] = (double)src[r * w_ + k];
   }
+  // the prologue's B fragments of R_a^T, fp32, lane-major (see load_rot_frags)
+  float* frag = (float*)((uint8_t*)out + kRotFragOffset);
+  const int nfrag = 3 * 64 * kRotFragStride;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nfrag; i += gridDim.x * blockDim.x) {
+    const int part = i / (64 * kRotFragStride), rem = i % (64 * kRotFragStride);
+    const int l = rem / kRotFragStride, e = rem % kRotFragStride;
+    const int w_ = part == 0 ? dt : dh;
+    const float* src = part == 0 ? rt : (part == 1 ? rh : rw);
+    const int JB = (w_ + 15) / 16, KS = (w_ + 3) / 4;
+    const int ks = e / JB, jb = e % JB;
+    const int k = 4 * ks + l / 16, j = 16 * jb + l % 16;
+    frag[i] = (ks < KS && k < w_ && j < w_) ? src[j * w_ + k] : 0.0f;
+  }
 }
 
 hipError_t launch_rot_to_f64(const float* rt, const float* rh, const float* rw, int dt, int dh,
                              double* out, hipStream_t st) {
   hipLaunchKernelGGL(k_rot_to_f64, dim3(16), dim3(256), 0, st, rt, rh, rw, dt, dh, out);
+  return hipGetLastError();
+}
+
+// The three axes' RoPE tables as (cos, sin) pairs: one 8-byte load per
+// channel pair in the prologue instead of two.
+__global__ void k_rope_pairs(rotattn_rope_rot rr, int np_t, int np_h, int np_w, float* out) {
+  const int total = np_t + np_h + np_w;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+    const float *c = rr.cos_t, *s = rr.sin_t;
+    int j = i;
+    if (j >= np_t) {
+      j -= np_t;
+      c = rr.cos_h;
+      s = rr.sin_h;
+      if (j >= np_h) {
+        j -= np_h;
+        c = rr.cos_w;
+        s = rr.sin_w;
+      }
+    }
+    out[2 * i] = c[j];
+    out[2 * i + 1] = s[j];
+  }
+}
+
+hipError_t launch_rope_pairs(const rotattn_rope_rot* rr, int np_t, int np_h, int np_w, float* out,
+                             hipStream_t st) {
+  hipLaunchKernelGGL(k_rope_pairs, dim3(32), dim3(256), 0, st, *rr, np_t, np_h, np_w, out);
   return hipGetLastError();
 }
 
@@ -130,20 +171,32 @@ struct Part {
 
 // B fragments of R_a^T: lane l holds B[k][j] = R[j][k] for k = 4 ks + l/16,
 // j = 16 jb + l%16 (zero outside d_a), kept as fp32 (R is fp32-valued; the
-// conversion to fp64 at each use is exact).  rot is [k][r] in fp64.
+// conversion to fp64 at each use is exact).  k_rot_to_f64 lays them out lane
+// by lane (kRotFragStride floats per lane, element ks * JB + jb), so that a
+// lane reads its 33 (D = 128) values with 9 16-byte loads, all in flight at
+// once, instead of 33 scattered fp64 loads.
 template <int DA>
-__device__ __forceinline__ void load_rot_frags(const double* rot,
+__device__ __forceinline__ void load_rot_frags(const float* frag,
                                                float (&b)[Part<DA>::KS][Part<DA>::JB]) {
+  constexpr int KS = Part<DA>::KS, JB = Part<DA>::JB, NV = (KS * JB + 3) / 4;
+  static_assert(NV * 4 <= kRotFragStride, "fragment row fits its stride");
   const int l = ltid() & 63;
+  const float4* p = (const float4*)(frag + l * kRotFragStride);
+  float v[NV * 4];
 #pragma unroll
-  for (int ks = 0; ks < Part<DA>::KS; ++ks)
+  for (int i = 0; i < NV; ++i) {
+    const float4 q = p[i];
+    v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+  }
 #pragma unroll
-    for (int jb = 0; jb < Part<DA>::JB; ++jb) {
-      const int k = 4 * ks + (l >> 4), j = 16 * jb + (l & 15);
-      // unconditional (clamped) loads: all of them in flight at once
-      const float r = (float)rot[min(k, DA - 1) * DA + min(j, DA - 1)];
-      b[ks][jb] = (k < DA && j < DA) ? r : 0.0f;
-    }
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) b[ks][jb] = v[ks * JB + jb];
+}
+
+// the fragments of partition `part` (0: t, 1: h, 2: w) in the rotation scratch
+__device__ __forceinline__ const float* rot_frags(const double* rot64, int part) {
+  return (const float*)((const uint8_t*)rot64 + kRotFragOffset) + part * 64 * kRotFragStride;
 }
 
 // Position of token n (< N) on RoPE axis `axis`: t = n / (Hg Wg),
@@ -155,18 +208,20 @@ __device__ __forceinline__ int axis_pos(int n, int N, int axis, int HW, int gh, 
 
 // The RoPE'd value of channel c (< DA) of one partition for one token: the
 // token's staged fp16 row xrow (one dword per channel pair, partition start),
-// its table rows start at element trow of cos_a and sin_a.  Even channel:
+// its table row starts at pair trow of cs_a, the (cos, sin) pairs of the
+// partition's axis (built in the library scratch by k_rope_pairs).  Even channel:
 // fl(x0 c) - fl(x1 s); odd channel: fl(x0 s) + fl(x1 c).  Operands are
 // selected instead of branching (negation is exact).  Channels >= DA (MFMA
 // zero padding) read a clamped pair.
 template <int DA>
-__device__ __forceinline__ float rope_channel(const uint32_t* xrow, const float* cos_a,
-                                              const float* sin_a, int trow, int c) {
+__device__ __forceinline__ float rope_channel(const uint32_t* xrow, const float* cs_a, int trow,
+                                              int c) {
   const int jp = (c >> 1) < DA / 2 ? (c >> 1) : DA / 2 - 1;
   const uint32_t pr = xrow[jp];
   const float x0 = h2f((uint16_t)(pr & 0xffffu));
   const float x1 = h2f((uint16_t)(pr >> 16));
-  const float cs = cos_a[trow + jp], sn = sin_a[trow + jp];
+  const float2 t = *(const float2*)(cs_a + 2 * (trow + jp));   // (cos, sin)
+  const float cs = t.x, sn = t.y;
   const bool odd = (c & 1) != 0;
   const float p0 = x0 * (odd ? sn : cs);
   const float p1 = x1 * (odd ? cs : sn);
@@ -179,8 +234,7 @@ __device__ __forceinline__ float rope_channel(const uint32_t* xrow, const float*
 // partition); returns the lane's max |z|.  xs: staged fp16 rows (kRS dwords
 // per row); b: R_a^T as B fragments.
 template <int DA, int TB, int kRS>
-__device__ __forceinline__ float rotate_part(const uint32_t* xs, const float* cos_a,
-                                             const float* sin_a,
+__device__ __forceinline__ float rotate_part(const uint32_t* xs, const float* cs_a,
                                              float (&b)[Part<DA>::KS][Part<DA>::JB], int off,
                                              int tok0, int n0, int N, int axis, int HW, int gh,
                                              int gw, float (&z)[TB][Part<DA>::JB][4]) {
@@ -205,7 +259,7 @@ __device__ __forceinline__ float rotate_part(const uint32_t* xs, const float* co
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int c = 4 * ks + (l >> 4);                      // channel in the partition
-      const float y = rope_channel<DA>(xrow, cos_a, sin_a, trow, c);
+      const float y = rope_channel<DA>(xrow, cs_a, trow, c);
       av[ks] = c < DA ? (double)y : 0.0;
     }
     v4d acc[JB];
@@ -233,8 +287,8 @@ __device__ __forceinline__ float rotate_part(const uint32_t* xs, const float* co
 // in that layout (token tok0 + 16 tb + l%16, channel 4 ks + l/16).  Returns
 // the lane's max |z|.
 template <int DA, int TB, int kRS>
-__device__ __forceinline__ float rope_part_a(const uint32_t* xs, const float* cos_a,
-                                             const float* sin_a, int off, int tok0, int n0, int N,
+__device__ __forceinline__ float rope_part_a(const uint32_t* xs, const float* cs_a, int off,
+                                             int tok0, int n0, int N,
                                              int axis, int HW, int gh, int gw,
                                              float (&z)[TB][Part<DA>::KS]) {
   constexpr int KS = Part<DA>::KS;
@@ -249,7 +303,7 @@ __device__ __forceinline__ float rope_part_a(const uint32_t* xs, const float* co
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int c = 4 * ks + (l >> 4);
-      const float y = rope_channel<DA>(xrow, cos_a, sin_a, trow, c);
+      const float y = rope_channel<DA>(xrow, cs_a, trow, c);
       z[tb][ks] = c < DA ? y : 0.0f;
       amax = fmaxf(amax, fabsf(z[tb][ks]));
     }
@@ -542,8 +596,7 @@ __device__ __forceinline__ void quant_qk_tile(const PrologueArgs& a, uint32_t* x
   // registers across both tensors
   int zero = 0;
   asm volatile("" : "+s"(zero));
-  const float *cos_t = a.cos_t + zero, *sin_t = a.sin_t + zero, *cos_h = a.cos_h + zero;
-  const float *sin_h = a.sin_h + zero, *cos_w = a.cos_w + zero, *sin_w = a.sin_w + zero;
+  const float *cs_t = a.cs_t + zero, *cs_h = a.cs_h + zero, *cs_w = a.cs_w + zero;
   if (ROT) {
     // R_a^T of each partition as B fragments, loaded (from cache) just before
     // its use; rotation matrices in fp64 [k][r]: t at 0, h at D0^2, w at
@@ -552,23 +605,20 @@ __device__ __forceinline__ void quant_qk_tile(const PrologueArgs& a, uint32_t* x
     float amax;
     {
       float b[Part<D0>::KS][Part<D0>::JB];
-      const double* rp = a.rot64 + zero;   // read again per tensor, not held
-      load_rot_frags<D0>(rp, b);
-      amax = rotate_part<D0, TB, kRS>(xs, cos_t, sin_t, b, 0, tok0, n0, a.N, 0, HW, a.grid_h,
+      load_rot_frags<D0>(rot_frags(a.rot64, 0) + zero, b);   // read again per tensor, not held
+      amax = rotate_part<D0, TB, kRS>(xs, cs_t, b, 0, tok0, n0, a.N, 0, HW, a.grid_h,
                                       a.grid_w, z0);
     }
     {
       float b[Part<D1>::KS][Part<D1>::JB];
-      const double* rp = a.rot64 + D0 * D0 + zero;
-      load_rot_frags<D1>(rp, b);
-      amax = fmaxf(amax, rotate_part<D1, TB, kRS>(xs, cos_h, sin_h, b, D0, tok0, n0, a.N, 1,
+      load_rot_frags<D1>(rot_frags(a.rot64, 1) + zero, b);
+      amax = fmaxf(amax, rotate_part<D1, TB, kRS>(xs, cs_h, b, D0, tok0, n0, a.N, 1,
                                                   HW, a.grid_h, a.grid_w, z1));
     }
     {
       float b[Part<D1>::KS][Part<D1>::JB];
-      const double* rp = a.rot64 + D0 * D0 + D1 * D1 + zero;
-      load_rot_frags<D1>(rp, b);
-      amax = fmaxf(amax, rotate_part<D1, TB, kRS>(xs, cos_w, sin_w, b, D0 + D1, tok0, n0,
+      load_rot_frags<D1>(rot_frags(a.rot64, 2) + zero, b);
+      amax = fmaxf(amax, rotate_part<D1, TB, kRS>(xs, cs_w, b, D0 + D1, tok0, n0,
                                                   a.N, 2, HW, a.grid_h, a.grid_w, z2));
     }
     block_scale(amax, red, inv, scale);
@@ -578,11 +628,11 @@ __device__ __forceinline__ void quant_qk_tile(const PrologueArgs& a, uint32_t* x
     quant_part<D1, TB, F8>(z2, inv, D0 + D1, tok0, codes);
   } else {
     float z0[TB][Part<D0>::KS], z1[TB][Part<D1>::KS], z2[TB][Part<D1>::KS];
-    float amax = rope_part_a<D0, TB, kRS>(xs, cos_t, sin_t, 0, tok0, n0, a.N, 0, HW,
+    float amax = rope_part_a<D0, TB, kRS>(xs, cs_t, 0, tok0, n0, a.N, 0, HW,
                                           a.grid_h, a.grid_w, z0);
-    amax = fmaxf(amax, rope_part_a<D1, TB, kRS>(xs, cos_h, sin_h, D0, tok0, n0, a.N, 1, HW,
+    amax = fmaxf(amax, rope_part_a<D1, TB, kRS>(xs, cs_h, D0, tok0, n0, a.N, 1, HW,
                                                 a.grid_h, a.grid_w, z1));
-    amax = fmaxf(amax, rope_part_a<D1, TB, kRS>(xs, cos_w, sin_w, D0 + D1, tok0, n0, a.N,
+    amax = fmaxf(amax, rope_part_a<D1, TB, kRS>(xs, cs_w, D0 + D1, tok0, n0, a.N,
                                                 2, HW, a.grid_h, a.grid_w, z2));
     block_scale(amax, red, inv, scale);
     mid();

@@ -20,9 +20,18 @@ static __device__ __align__(256) uint8_t scratch[ROTATTN_NOALLOC_SCRATCH_BYTES];
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr size_t kRotBytes = 3 * 64 * 64 * sizeof(double);   // fp64 rotation scratch
+constexpr size_t kRotBytes = kRotTabOffset;   // rotation scratch before the tables
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+// The library scratch of a rotattn_prepared: the rotation (fp64 and the
+// prologue's fp32 fragments), then the RoPE tables as (cos, sin) pairs, one
+// 8-byte pair per (position, channel pair) of each axis.
+size_t scratch_bytes(const rotattn_shape* s) {
+  const size_t pairs = (size_t)s->grid_t * (s->d_t / 2) + (size_t)s->grid_h * (s->d_h / 2) +
+                       (size_t)s->grid_w * (s->d_w / 2);
+  return kRotBytes + align_up(pairs * 8);
+}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -152,7 +161,7 @@ size_t rotattn_prepared_bytes_layout(const rotattn_shape* s, int with_rope, int 
   const size_t scales = align_up(BH * NB * sizeof(float));
   // fallback buffers: q_rope, k_rope, v_t, each [B*H][N_pad][D] fp16
   const size_t rope = with_rope ? align_up(BH * NB * kBlock * D * 2) : 0;
-  return 3 * packed + 3 * scales + kRotBytes + 3 * rope;
+  return 3 * packed + 3 * scales + scratch_bytes(s) + 3 * rope;
 }
 
 int rotattn_prepared_carve(const rotattn_shape* s, void* base, size_t bytes, int with_rope,
@@ -176,7 +185,7 @@ int rotattn_prepared_carve(const rotattn_shape* s, void* base, size_t bytes, int
   out->q_scale_l2 = (float*)p; p += scales;
   out->k_scale = (float*)p; p += scales;
   out->v_scale = (float*)p; p += scales;
-  out->rot64 = (double*)p; p += kRotBytes;
+  out->rot64 = (double*)p; p += scratch_bytes(s);
   if (with_rope) {
     out->q_rope = (uint16_t*)p; p += rope;
     out->k_rope = (uint16_t*)p; p += rope;
@@ -233,14 +242,13 @@ int check_prepare_out(const rotattn_shape* s, const rotattn_rope_rot* rr,
   // all three rotation matrices, or none (rotation merged into the tables)
   const int n_rot = (rr->rot_t != nullptr) + (rr->rot_h != nullptr) + (rr->rot_w != nullptr);
   if (n_rot != 0 && n_rot != 3) return ROTATTN_E_NULL;
-  const bool rot = n_rot == 3;
   const int BH = s->B * s->H;
   if (!valid_layout(out->layout)) return ROTATTN_E_ARG;
   int n_fb = 0;
   make_bits(fallback_mask_host, BH, true, false, &n_fb);
   if (n_fb < BH) {
     if (!out->q4 || !out->k4 || !out->v4 || !out->q_scale_l2 || !out->k_scale || !out->v_scale ||
-        (rot && !out->rot64))
+        !out->rot64)
       return ROTATTN_E_NULL;
     if (!aligned16(out->q4) || !aligned16(out->k4) || !aligned16(out->v4)) return ROTATTN_E_ALIGN;
   }
@@ -276,7 +284,15 @@ int prologue_args(const rotattn_shape* s, const rotattn_rope_rot* rr,
       launch_rot_to_f64(rr->rot_t, rr->rot_h, rr->rot_w, s->d_t, s->d_h, out->rot64, stream) !=
           hipSuccess)
     return ROTATTN_E_HIP;
+  float* tabs = (float*)((uint8_t*)out->rot64 + kRotTabOffset);
+  const int np_t = s->grid_t * (s->d_t / 2), np_h = s->grid_h * (s->d_h / 2);
+  const int np_w = s->grid_w * (s->d_w / 2);
+  if (n_fb < BH && launch_rope_pairs(rr, np_t, np_h, np_w, tabs, stream) != hipSuccess)
+    return ROTATTN_E_HIP;
   PrologueArgs& a = *pa;
+  a.cs_t = tabs;
+  a.cs_h = tabs + 2 * np_t;
+  a.cs_w = tabs + 2 * (np_t + np_h);
   a.q = a.k = a.v = nullptr;
   a.in = Strides{};
   a.H = s->H;

@@ -82,6 +82,7 @@ struct PrologueArgs {
   Strides in;                   // of q, k and v
   int H;
   const float *cos_t, *sin_t, *cos_h, *sin_h, *cos_w, *sin_w;
+  const float *cs_t, *cs_h, *cs_w;   // the same tables as (cos, sin) pairs (library scratch)
   const double* rot64;          // rotation in fp64, [k][r] per partition (t at 0, h at d_t^2, w next);
                                 // unused by the kernels without a dense rotation
   uint8_t *q4, *k4, *v4;
@@ -136,6 +137,17 @@ struct StageArgs {
   int bh0;
 };
 
+// The library scratch of a rotattn_prepared (rot64): the rotation in fp64
+// [k][r] per partition from byte 0; from byte kRotFragOffset the prologue's
+// MFMA B fragments of it in fp32, 64 lanes x kRotFragStride floats per
+// partition; from byte kRotTabOffset the RoPE tables as (cos, sin) pairs, axis
+// t, then h, then w, each [position][channel pair].
+constexpr int kRotFragOffset = 48 * 1024;
+constexpr int kRotFragStride = 36;
+constexpr int kRotTabOffset = 96 * 1024;
+static_assert(kRotFragOffset >= (44 * 44 + 2 * 42 * 42) * 8, "fp64 rotation before the fragments");
+static_assert(kRotFragOffset + 3 * 64 * kRotFragStride * 4 <= kRotTabOffset, "fragments fit");
+
 // The QKV projection with the prologue as its epilogue: x [B][N][C] (channel
 // stride 1) times the fused weight w [3 H D][C] (row r = output channel r: Q
 // heads, then K, then V), + bias, rounded to fp16, then the prologue's work on
@@ -156,6 +168,8 @@ struct QkvProjArgs {
 // Launchers (each defined next to its kernel).  Return a hipError_t.
 hipError_t launch_rot_to_f64(const float* rt, const float* rh, const float* rw, int dt, int dh,
                              double* out, hipStream_t st);
+hipError_t launch_rope_pairs(const rotattn_rope_rot* rr, int np_t, int np_h, int np_w, float* out,
+                             hipStream_t st);
 hipError_t launch_prologue(int D, int dt, int BH, int layout, bool rot, const PrologueArgs& a,
                            hipStream_t st);
 hipError_t launch_int4(int D, int BH, const Int4Args& a, const Int4Debug* dbg, hipStream_t st);
