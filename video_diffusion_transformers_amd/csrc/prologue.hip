@@ -241,43 +241,45 @@ __device__ __forceinline__ float rotate_part(const uint32_t* xs, const float* cs
   constexpr int KS = Part<DA>::KS, JB = Part<DA>::JB;
   const int l = ltid() & 63;
   float amax = 0.0f;
+  // RoPE'd A fragments of every token group, then one MFMA chain over k in
+  // which each fp64 B fragment serves all TB groups
+  double av[TB][KS];
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) {
-    // the fp32 fragments are marked as changing here so that their fp64
-    // conversions stay next to the MFMAs instead of being hoisted into
-    // 2 x KS x JB live registers
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int jb = 0; jb < JB; ++jb) asm volatile("" : "+v"(b[ks][jb]));
     const int i = tok0 + 16 * tb + (l & 15);   // this lane's A row (token in the block)
     const int pos = axis_pos(n0 + i, N, axis, HW, gh, gw);
     const uint32_t* xrow = xs + i * kRS + off / 2;
     const int trow = pos * (DA / 2);
-    // RoPE'd A fragments of this token group, then the MFMA chain over k
-    double av[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int c = 4 * ks + (l >> 4);                      // channel in the partition
       const float y = rope_channel<DA>(xrow, cs_a, trow, c);
-      av[ks] = c < DA ? (double)y : 0.0;
+      av[tb][ks] = c < DA ? (double)y : 0.0;
     }
-    v4d acc[JB];
+  }
+  v4d acc[TB][JB];
 #pragma unroll
-    for (int jb = 0; jb < JB; ++jb) acc[jb] = v4d{0.0, 0.0, 0.0, 0.0};
+  for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int jb = 0; jb < JB; ++jb) acc[tb][jb] = v4d{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int jb = 0; jb < JB; ++jb)
-        acc[jb] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ks], (double)b[ks][jb], acc[jb], 0, 0, 0);
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+      const double bd = (double)b[ks][jb];
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+        acc[tb][jb] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[tb][ks], bd, acc[tb][jb], 0, 0, 0);
+    }
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        z[tb][jb][r] = (float)acc[jb][r];
+        z[tb][jb][r] = (float)acc[tb][jb][r];
         amax = fmaxf(amax, fabsf(z[tb][jb][r]));
       }
-  }
   return amax;
 }
 
